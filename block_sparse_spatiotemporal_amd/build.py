@@ -1,0 +1,50 @@
+"""Build libfva.so in-tree with hipcc for gfx950.
+
+Usage: python -m block_sparse_spatiotemporal_amd.build   (or call build()).
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libfva.so")
+SOURCES = ["plan.cpp", "permute.hip", "select.hip", "attention.hip"]
+
+
+def hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source for gfx950 and link libfva.so next to this file."""
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    common = ["-O3", "-std=c++17", "-fPIC", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+              "-Wall", "-Wno-unused-function"]
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(objdir, src + ".o")
+        cmd = [hipcc()] + common + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd[1:1] = ["-x", "hip", "--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang",
+                    "-packed-fp32-ops", "-ffp-contract=fast"]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        objs.append(obj)
+    tmp = LIB + ".tmp"
+    subprocess.run([hipcc(), "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp] + objs, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose="-v" in sys.argv)
+    print(LIB)

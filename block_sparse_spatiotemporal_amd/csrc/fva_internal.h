@@ -1,0 +1,57 @@
+// Internal declarations shared by the libfva translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+
+#include "fva.h"
+
+#define FVA_BLK 64        // tokens per block (tile volume)
+#define FVA_MAX_PHEAD 512 // per-head p values passed by value to the kernels
+#define FVA_MAX_NBLK 4096 // blocks per head the selection kernels support
+
+struct fva_plan_s {
+  fva_plan_desc desc;
+  fva_plan_info info;
+  int esize;          // bytes per element: 2 (bf16) or 4 (fp32)
+  int nw;             // 64-bit mask words per selection row = ceil(n_blk / 64)
+  int device;
+  int num_cu;
+  hipStream_t stream; // stream the tables were uploaded on
+
+  // device tables (uploaded once at creation)
+  int32_t* perm;      // [n_pad] raster token or -1
+  uint64_t* blk_mask; // [n_blk] valid-position bitmask
+  int32_t* blk_cnt;   // [n_blk] valid tokens
+  uint8_t* sub_pos;   // [n_blk][8][8] local positions of each sub-block
+  int32_t* sub_cnt;   // [n_blk][8] valid tokens per sub-block
+
+  // workspace
+  float* qbar;        // [B*H*n_blk*D]
+  float* kbar;        // [B*H*n_blk*(n_sub or 1)*D]
+  float* zbuf;        // [B*H*n_blk*n_blk] block logits, then scores in place
+  float2* rowstat;    // [n_rows] (max logit, sum of exp)
+  int32_t* rowcnt;    // [n_rows] kept blocks per row
+  uint64_t* rowmask;  // [n_rows*nw] kept-block bitmask per row
+  int32_t* headcnt;   // [B*H]
+  int32_t* deficit;   // [B*H] slack blocks to add per head
+  uint64_t* slack_thr;// [B*H]
+  int32_t* worklist;  // [n_rows] attention rows in schedule order
+  int32_t* counters;  // [64] work-queue cursor and misc counters
+
+  void* dev_base;     // single device allocation holding everything above
+  size_t dev_bytes;
+};
+
+// Thread-local error text; returns `code` for convenient `return fva_fail(...)`.
+int fva_fail(int code, const char* fmt, ...);
+// Checks a HIP status; on failure records it and returns FVA_EHIP.
+int fva_hip_check(hipError_t e, const char* what);
+// After the launches of one call: with FVA_DEBUG=1, synchronise and check.
+int fva_after_launch(hipStream_t s, const char* what);
+
+struct SelectArgs {
+  float p[FVA_MAX_PHEAD];
+};

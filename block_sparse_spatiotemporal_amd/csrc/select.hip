@@ -1,0 +1,710 @@
+// Coarse stage and routing:
+//   pool   - "Video Sparse Attention" explainer, dialogue and section 3
+//            (pooled (4,4,4) tiles), "DFSAttn" explainer trick 2 (sub-blocks)
+//   score  - pooled q_bar . k_bar / sqrt(D), softmax over key blocks
+//   select - "FVAttn" review, sections 00 and 02: adaptive Top-p with a
+//            Top-k safety floor, emitted as CSR block lists
+//   slack  - "FVAttn" section 02 slack-aware augmentation, one-GPU reading:
+//            light heads are filled up to the median head's block count
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "fva_internal.h"
+
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// ------------------------------------------------------------------ helpers
+__device__ __forceinline__ float ld_elem(const uint16_t* p) {
+  return __uint_as_float((uint32_t)(*p) << 16);
+}
+__device__ __forceinline__ float ld_elem(const float* p) { return *p; }
+
+// Selection view of a score: NaN and s <= 0 -> +0, s > 1 -> 1; returns bits.
+__device__ __forceinline__ uint32_t clamp_bits(float s) {
+  if (!(s > 0.0f)) return 0u;
+  if (s >= 1.0f) return 0x3F800000u;
+  return __float_as_uint(s);
+}
+
+// floor(s * 2^47) for the fp32 value with bits b in [0, 1], exactly.
+__device__ __forceinline__ uint64_t fix_mass(uint32_t b) {
+  if (b == 0) return 0;
+  const uint32_t e = b >> 23;
+  const uint64_t mant = (b & 0x7FFFFFu) | (e ? 0x800000u : 0u);
+  const int sh = (int)(e ? e : 1) - 103;
+  if (sh >= 0) return mant << sh;
+  return sh > -64 ? (mant >> (-sh)) : 0;
+}
+
+__device__ __forceinline__ uint64_t p_threshold(float p) {
+  // ceil(p * 2^47): exact, p is an fp32 value in (0, 1).
+  return (uint64_t)ceil((double)p * 140737488355328.0);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_incl_scan(T v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    T u = __shfl_up(v, o);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ------------------------------------------------------------------ pool
+// Mean of the 64 rows of one block (pads are zero rows, so the sum over all
+// rows is the sum over valid rows), divided by the valid count.  One wave per
+// (block, b*h, tensor); lanes own 16-byte column chunks of interleaved rows.
+template <typename T, int D>
+__global__ __launch_bounds__(64) void k_pool(const T* __restrict__ q, const T* __restrict__ k,
+                                             float* __restrict__ qbar, float* __restrict__ kbar,
+                                             const int32_t* __restrict__ blk_cnt, int n_blk, int64_t n_pad) {
+  constexpr int EPC = 16 / sizeof(T);   // elements per 16-byte chunk
+  constexpr int CPR = D / EPC;          // chunks per row
+  constexpr int RG = 64 / CPR;          // row groups
+  __shared__ float part[RG][D];
+  const int blk = blockIdx.x, bh = blockIdx.y;
+  const T* src = (blockIdx.z == 0 ? q : k) + ((int64_t)bh * n_pad + (int64_t)blk * 64) * D;
+  float* dst = (blockIdx.z == 0 ? qbar : kbar) + ((int64_t)bh * n_blk + blk) * D;
+  const int lane = threadIdx.x;
+  const int ch = lane % CPR, g = lane / CPR;
+  float acc[EPC];
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) acc[e] = 0.0f;
+  for (int r = g; r < 64; r += RG) {
+    const T* row = src + (int64_t)r * D + ch * EPC;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[e] += ld_elem(row + e);
+  }
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) part[g][ch * EPC + e] = acc[e];
+  __syncthreads();
+  const float inv_n = 1.0f / (float)blk_cnt[blk];
+  for (int d = lane; d < D; d += 64) {
+    float s = 0.0f;
+#pragma unroll
+    for (int gg = 0; gg < RG; ++gg) s += part[gg][d];
+    dst[d] = s * inv_n;
+  }
+}
+
+// Sub-block means of K ("DFSAttn" trick 2): kbar[(bh, blk, s), :] = mean of the
+// valid rows of sub-block s; an empty sub-block gets zeros (its logit is
+// masked by the score kernel through sub_cnt).
+template <typename T, int D>
+__global__ __launch_bounds__(64) void k_pool_sub(const T* __restrict__ k, float* __restrict__ kbar,
+                                                 const uint8_t* __restrict__ sub_pos,
+                                                 const int32_t* __restrict__ sub_cnt, int n_blk,
+                                                 int64_t n_pad) {
+  const int blk = blockIdx.x, bh = blockIdx.y;
+  const T* src = k + ((int64_t)bh * n_pad + (int64_t)blk * 64) * D;
+  float* dst = kbar + ((int64_t)bh * n_blk + blk) * 8 * D;
+  for (int e = threadIdx.x; e < 8 * D; e += 64) {
+    const int s = e / D, d = e - s * D;
+    const uint8_t* pos = sub_pos + ((int64_t)blk * 8 + s) * 8;
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc += ld_elem(src + (int64_t)pos[i] * D + d);
+    const int c = sub_cnt[blk * 8 + s];
+    dst[e] = c ? acc / (float)c : 0.0f;
+  }
+}
+
+// ------------------------------------------------------------------ score
+// Block logits Y[bh, i, j] = q_bar_i . k_bar_j * scale (with sub-blocks: the
+// log-sum-exp over the non-empty sub-blocks of j), on fp32 matrix cores
+// (v_mfma_f32_32x32x2_f32), plus per-row (max, sum exp(y - max)).
+// Workgroup: 4 waves, 32 query rows of one (b, h); waves stride over 32-row
+// key tiles.  Z^T = Kbar * Qbar^T so that each lane owns one query row and
+// its key values sit in the lane's accumulators.
+template <bool SUB, int D>
+__global__ __launch_bounds__(256) void k_score(const float* __restrict__ qbar, const float* __restrict__ kbar,
+                                               const int32_t* __restrict__ sub_cnt, float* __restrict__ z,
+                                               float2* __restrict__ rowstat, int n_blk, float scale) {
+  constexpr int HD = D / 2;
+  __shared__ float2 stat[4][64];
+  const int bh = blockIdx.y;
+  const int i0 = blockIdx.x * 32;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int nkeys = SUB ? n_blk * 8 : n_blk;
+  const int ntiles = SUB ? (n_blk + 3) / 4 : (n_blk + 31) / 32;
+  const float* qb = qbar + (int64_t)bh * n_blk * D;
+  const float* kb = kbar + (int64_t)bh * nkeys * D;
+  const int qi = i0 + l32;
+  const bool qvalid = qi < n_blk;
+  float qv[HD];
+  {
+    const float4* src = (const float4*)(qb + (int64_t)min(qi, n_blk - 1) * D + h * HD);
+#pragma unroll
+    for (int c = 0; c < HD / 4; ++c) {
+      const float4 t = src[c];
+      qv[4 * c] = t.x, qv[4 * c + 1] = t.y, qv[4 * c + 2] = t.z, qv[4 * c + 3] = t.w;
+    }
+  }
+  float m_run = -INFINITY, s_run = 0.0f;
+  float* zrow = z + ((int64_t)bh * n_blk + min(qi, n_blk - 1)) * n_blk;
+  for (int kt = w; kt < ntiles; kt += 4) {
+    int krow;
+    bool kvalid;
+    if (!SUB) {
+      krow = kt * 32 + l32;
+      kvalid = krow < n_blk;
+    } else {
+      const int qq = l32 >> 3, hm = (l32 >> 2) & 1, ii = l32 & 3;
+      const int blk = kt * 4 + 2 * hm + (qq >> 1);
+      krow = blk * 8 + 4 * (qq & 1) + ii;
+      kvalid = blk < n_blk;
+    }
+    const float4* ks = (const float4*)(kb + (int64_t)(kvalid ? krow : 0) * D + h * HD);
+    f32x16 acc = {};
+#pragma unroll
+    for (int c = 0; c < HD / 4; ++c) {
+      const float4 a = ks[c];
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, qv[4 * c + 0], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, qv[4 * c + 1], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, qv[4 * c + 2], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, qv[4 * c + 3], acc, 0, 0, 0);
+    }
+    // accumulator r of this lane: key row m = 8*(r/4) + 4*h + r%4, query l32
+    if (!SUB) {
+      float tmax = -INFINITY;
+      float y[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = kt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        y[r] = j < n_blk ? acc[r] * scale : -INFINITY;
+        tmax = fmaxf(tmax, y[r]);
+      }
+      const float m_new = fmaxf(m_run, tmax);
+      if (m_new > -INFINITY) {
+        float add = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) add += __expf(y[r] - m_new);
+        s_run = s_run * __expf(m_run - m_new) + add;
+        m_run = m_new;
+      }
+      if (qvalid) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int j0 = kt * 32 + 8 * g4 + 4 * h;
+          if (j0 + 3 < n_blk) {
+            *(float4*)(zrow + j0) = make_float4(y[4 * g4], y[4 * g4 + 1], y[4 * g4 + 2], y[4 * g4 + 3]);
+          } else {
+            for (int e = 0; e < 4; ++e)
+              if (j0 + e < n_blk) zrow[j0 + e] = y[4 * g4 + e];
+          }
+        }
+      }
+    } else {
+      float yb[2];
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2) {
+        const int blk = kt * 4 + 2 * h + b2;
+        float v[8];
+        float c = -INFINITY;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const bool ok = blk < n_blk && sub_cnt[(blk < n_blk ? blk : 0) * 8 + s] > 0;
+          v[s] = ok ? acc[8 * b2 + s] * scale : -INFINITY;
+          c = fmaxf(c, v[s]);
+        }
+        float e = 0.0f;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) e += __expf(v[s] - c);
+        yb[b2] = (blk < n_blk) ? c + __logf(e) : -INFINITY;
+      }
+      const float tmax = fmaxf(yb[0], yb[1]);
+      const float m_new = fmaxf(m_run, tmax);
+      if (m_new > -INFINITY) {
+        s_run = s_run * __expf(m_run - m_new) + __expf(yb[0] - m_new) + __expf(yb[1] - m_new);
+        m_run = m_new;
+      }
+      if (qvalid) {
+        const int j0 = kt * 4 + 2 * h;
+        if (j0 + 1 < n_blk) *(float2*)(zrow + j0) = make_float2(yb[0], yb[1]);
+        else if (j0 < n_blk) zrow[j0] = yb[0];
+      }
+    }
+  }
+  // merge (max, sum) over the two lane halves, then over the four waves
+  {
+    const float mo = __shfl_xor(m_run, 32), so = __shfl_xor(s_run, 32);
+    const float mm = fmaxf(m_run, mo);
+    const float ss = (m_run > -INFINITY ? s_run * __expf(m_run - mm) : 0.0f) +
+                     (mo > -INFINITY ? so * __expf(mo - mm) : 0.0f);
+    stat[w][lane] = make_float2(mm, ss);
+  }
+  __syncthreads();
+  if (w == 0 && lane < 32 && qvalid) {
+    float mm = -INFINITY;
+    for (int ww = 0; ww < 4; ++ww) mm = fmaxf(mm, stat[ww][lane].x);
+    float ss = 0.0f;
+    for (int ww = 0; ww < 4; ++ww) {
+      const float2 t = stat[ww][lane];
+      if (t.x > -INFINITY) ss += t.y * __expf(t.x - mm);
+    }
+    rowstat[(int64_t)bh * n_blk + qi] = make_float2(mm, ss);
+  }
+}
+
+// ------------------------------------------------------------------ select
+// One wave per row (b, h, I).  Scores are either recomputed from the block
+// logits (S = exp(y - max) / sum, fp32) or read from scores_in.  The kept set
+// is the shortest prefix in (score desc, id asc) order whose fixed-point
+// mass reaches p, extended to the floor min(k_min, n).  It is found by an
+// MSD radix select over the 48-bit key (score bits << 16 | (0xFFFF - J)):
+// each level builds a 256-bin histogram of mass and count in LDS, keeps the
+// bin where the mass target or the count target is crossed, and as soon as
+// that bin holds <= 64 keys they are sorted across the wave (bitonic) and the
+// exact cut is read off a prefix sum.  Output: a bitmask of kept ids per row
+// and the kept count.
+template <int NI>
+__global__ __launch_bounds__(256) void k_select(const float* __restrict__ z, const float2* __restrict__ rowstat,
+                                                const float* __restrict__ scores_in, float* __restrict__ s_out,
+                                                SelectArgs pa, int p_count, int k_min, int n_blk,
+                                                int64_t n_rows, int32_t* __restrict__ rowcnt,
+                                                uint64_t* __restrict__ rowmask, int nw) {
+  __shared__ unsigned long long hmass[4][256];
+  __shared__ unsigned int hcnt[4][256];
+  __shared__ unsigned long long lkey[4][64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t r = (int64_t)blockIdx.x * 4 + wv;
+  if (r >= n_rows) return;
+  const int n = n_blk;
+  const int bh = (int)(r / n);
+  const float p = pa.p[p_count == 1 ? 0 : bh];
+
+  uint32_t bits[NI];
+  {
+    float m = 0.0f, sum = 1.0f;
+    if (!scores_in) {
+      const float2 st = rowstat[r];
+      m = st.x, sum = st.y;
+    }
+    const float* zr = z + r * n;
+    const float* sr = scores_in ? scores_in + r * n : nullptr;
+    float* so = s_out ? s_out + r * n : nullptr;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int j = lane + 64 * i;
+      bits[i] = 0;
+      if (j < n) {
+        const float s = sr ? sr[j] : expf(zr[j] - m) / sum;
+        if (so) so[j] = s;
+        bits[i] = clamp_bits(s);
+      }
+    }
+  }
+  auto key_of = [&](int i) -> uint64_t {
+    return ((uint64_t)bits[i] << 16) | (uint64_t)(0xFFFF - (lane + 64 * i));
+  };
+
+  uint64_t thr = 0;   // keep ids whose key >= thr
+  int kept = n;
+  const int kf = min(k_min, n);
+  if (p < 1.0f) {
+    uint64_t needP = p_threshold(p);
+    int needF = kf;
+    bool useP = true, useF = kf > 0;
+    int kAbove = 0;
+    uint64_t active = 0;   // bit i: element i of this lane still a candidate
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      if (lane + 64 * i < n) active |= 1ull << i;
+    bool all = false;
+    for (int level = 0; level < 6; ++level) {
+      const int shift = 40 - 8 * level;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        hmass[wv][lane * 4 + t] = 0;
+        hcnt[wv][lane * 4 + t] = 0;
+      }
+      wave_sync_lds();
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        if (active >> i & 1) {
+          const int dg = 255 - (int)((key_of(i) >> shift) & 0xFF);
+          atomicAdd(&hmass[wv][dg], (unsigned long long)fix_mass(bits[i]));
+          atomicAdd(&hcnt[wv][dg], 1u);
+        }
+      }
+      wave_sync_lds();
+      uint64_t bm[4];
+      uint32_t bc[4];
+      uint64_t lm = 0;
+      uint32_t lc = 0;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        bm[t] = hmass[wv][lane * 4 + t];
+        bc[t] = hcnt[wv][lane * 4 + t];
+        lm += bm[t];
+        lc += bc[t];
+      }
+      const uint64_t mi = wave_incl_scan<uint64_t>(lm, lane);
+      const uint32_t ci = wave_incl_scan<uint32_t>(lc, lane);
+      const uint64_t mtot = __shfl(mi, 63);
+      if (level == 0 && useP && mtot < needP) {   // total mass never reaches p: keep all
+        all = true;
+        break;
+      }
+      // crossing bins for each live criterion (bin index, -1 when unused)
+      int bP = -1, bF = -1;
+      {
+        uint64_t me = mi - lm;
+        uint32_t ce = ci - lc;
+        int myP = -1, myF = -1;
+        if (useP && me < needP && mi >= needP) {
+          uint64_t a = me;
+          for (int t = 0; t < 4; ++t) {
+            a += bm[t];
+            if (a >= needP) { myP = lane * 4 + t; break; }
+          }
+        }
+        if (useF && (int)ce < needF && (int)ci >= needF) {
+          uint32_t a = ce;
+          for (int t = 0; t < 4; ++t) {
+            a += bc[t];
+            if ((int)a >= needF) { myF = lane * 4 + t; break; }
+          }
+        }
+        const uint64_t vp = __ballot(myP >= 0), vf = __ballot(myF >= 0);
+        if (vp) bP = __shfl(myP, __ffsll((unsigned long long)vp) - 1);
+        if (vf) bF = __shfl(myF, __ffsll((unsigned long long)vf) - 1);
+      }
+      const int bs = max(bP, bF);
+      if (bP < bs) useP = false;
+      if (bF < bs) useF = false;
+      // mass / count strictly above bin bs
+      uint64_t ma = 0;
+      uint32_t ca = 0;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if (lane * 4 + t < bs) {
+          ma += bm[t];
+          ca += bc[t];
+        }
+      }
+      ma = wave_incl_scan<uint64_t>(ma, lane);
+      ca = wave_incl_scan<uint32_t>(ca, lane);
+      ma = __shfl(ma, 63);
+      ca = __shfl(ca, 63);
+      if (useP) needP -= ma;
+      if (useF) needF -= (int)ca;
+      kAbove += (int)ca;
+      const uint32_t cstar = hcnt[wv][bs];
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        if ((active >> i & 1) && 255 - (int)((key_of(i) >> shift) & 0xFF) != bs) active &= ~(1ull << i);
+      if (cstar <= 64) break;
+    }
+    if (!all) {
+      // gather the <= 64 candidates, sort descending across the wave
+      int base = 0;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const bool a = active >> i & 1;
+        const uint64_t b = __ballot(a);
+        if (a) lkey[wv][base + __popcll(b & ((1ull << lane) - 1))] = key_of(i);
+        base += __popcll(b);
+      }
+      wave_sync_lds();
+      uint64_t kk = lane < base ? lkey[wv][lane] : 0ull;
+      for (int kb = 2; kb <= 64; kb <<= 1) {
+        for (int jb = kb >> 1; jb > 0; jb >>= 1) {
+          const uint64_t o = __shfl_xor(kk, jb);
+          const bool up = (lane & kb) == 0, lower = (lane & jb) == 0;
+          kk = (up == lower) ? (kk > o ? kk : o) : (kk < o ? kk : o);
+        }
+      }
+      const uint64_t qm = lane < base ? fix_mass((uint32_t)(kk >> 16)) : 0;
+      const uint64_t qi = wave_incl_scan<uint64_t>(qm, lane);
+      int tP = 0;
+      if (useP) {
+        const uint64_t hit = __ballot(lane < base && qi >= needP);
+        tP = hit ? __ffsll((unsigned long long)hit) : base;   // 1-based position
+      }
+      const int tF = useF ? needF : 0;
+      const int t = max(max(tP, tF), 1);
+      thr = __shfl(kk, t - 1);
+      kept = kAbove + t;
+    }
+  }
+  // emit the bitmask of kept ids
+  uint64_t* mrow = rowmask + r * nw;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    if (i < nw) {
+      const bool sel = (lane + 64 * i < n) && key_of(i) >= thr;
+      const uint64_t b = __ballot(sel);
+      if (lane == 0) mrow[i] = b;
+    }
+  }
+  if (lane == 0) rowcnt[r] = kept;
+}
+
+// ------------------------------------------------------------------ slack
+// Lower median of the per-(b,h) kept counts and the deficit of every head.
+__global__ __launch_bounds__(1024) void k_slack_target(const int32_t* __restrict__ rowcnt, int n_blk, int n_bh,
+                                                       int32_t* __restrict__ headcnt,
+                                                       int32_t* __restrict__ deficit) {
+  __shared__ int hn[FVA_MAX_PHEAD];
+  __shared__ int target;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  for (int bh = wv; bh < n_bh; bh += 16) {
+    int s = 0;
+    for (int i = lane; i < n_blk; i += 64) s += rowcnt[(int64_t)bh * n_blk + i];
+    for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+    if (lane == 0) hn[bh] = s;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < n_bh; i += 1024) {
+    int rank = 0;
+    for (int j = 0; j < n_bh; ++j) rank += (hn[j] < hn[i]) || (hn[j] == hn[i] && j < i);
+    if (rank == (n_bh - 1) / 2) target = hn[i];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < n_bh; i += 1024) {
+    headcnt[i] = hn[i];
+    deficit[i] = max(0, target - hn[i]);
+  }
+}
+
+// Per deficient head: the key (score bits << 32 | ~(I*n + J)) of the d-th best
+// unselected pair, by an 8-level MSD radix select over all n^2 pairs.
+__global__ __launch_bounds__(1024) void k_slack_thresh(const float* __restrict__ S,
+                                                       const uint64_t* __restrict__ rowmask, int nw,
+                                                       int n_blk, const int32_t* __restrict__ deficit,
+                                                       uint64_t* __restrict__ slack_thr) {
+  __shared__ unsigned int hist[256];
+  __shared__ uint64_t prefix;
+  __shared__ int need;
+  const int bh = blockIdx.x;
+  const int d = deficit[bh];
+  if (d <= 0) return;
+  const int64_t n = n_blk, nn = n * n;
+  const float* Sh = S + (int64_t)bh * nn;
+  const uint64_t* mh = rowmask + (int64_t)bh * n * nw;
+  if (threadIdx.x == 0) {
+    prefix = 0;
+    need = d;
+  }
+  for (int level = 0; level < 8; ++level) {
+    const int shift = 56 - 8 * level;
+    for (int t = threadIdx.x; t < 256; t += 1024) hist[t] = 0;
+    __syncthreads();
+    const uint64_t pre = prefix;
+    for (int64_t e = threadIdx.x; e < nn; e += 1024) {
+      const int64_t I = e / n, J = e - I * n;
+      if (mh[I * nw + (J >> 6)] >> (J & 63) & 1) continue;
+      const uint64_t key = ((uint64_t)clamp_bits(Sh[e]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+      if (level > 0 && (key >> (shift + 8)) != (pre >> (shift + 8))) continue;
+      atomicAdd(&hist[(key >> shift) & 0xFF], 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int acc = 0;
+      for (int b = 255; b >= 0; --b) {
+        if (acc + (int)hist[b] >= need) {
+          prefix = pre | ((uint64_t)b << shift);
+          need -= acc;
+          break;
+        }
+        acc += hist[b];
+      }
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) slack_thr[bh] = prefix;
+}
+
+// Add the pairs at or above a deficient head's threshold to its rows.
+__global__ __launch_bounds__(256) void k_slack_apply(const float* __restrict__ S, uint64_t* __restrict__ rowmask,
+                                                     int32_t* __restrict__ rowcnt, int nw, int n_blk,
+                                                     int64_t n_rows, const int32_t* __restrict__ deficit,
+                                                     const uint64_t* __restrict__ slack_thr) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t r = (int64_t)blockIdx.x * 4 + wv;
+  if (r >= n_rows) return;
+  const int bh = (int)(r / n_blk);
+  if (deficit[bh] <= 0) return;
+  const uint64_t thr = slack_thr[bh];
+  const int I = (int)(r - (int64_t)bh * n_blk);
+  const float* Sr = S + r * n_blk;
+  int added = 0;
+  for (int i = 0; i < nw; ++i) {
+    const int J = lane + 64 * i;
+    const uint64_t old = rowmask[r * nw + i];
+    bool add = false;
+    if (J < n_blk && !(old >> lane & 1)) {
+      const uint32_t e = (uint32_t)I * (uint32_t)n_blk + (uint32_t)J;
+      const uint64_t key = ((uint64_t)clamp_bits(Sr[J]) << 32) | (uint64_t)(0xFFFFFFFFu - e);
+      add = key >= thr;
+    }
+    const uint64_t b = __ballot(add);
+    if (lane == 0 && b) rowmask[r * nw + i] = old | b;
+    added += __popcll(b);
+  }
+  if (lane == 0) rowcnt[r] += added;
+}
+
+// ------------------------------------------------------------------ CSR
+// Exclusive scan of kept counts into row_ptr (one workgroup) and per-head
+// totals.
+__global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ cnt, int64_t n_rows,
+                                               int32_t* __restrict__ row_ptr, int32_t* __restrict__ head_nnz,
+                                               int n_blk, int n_bh) {
+  __shared__ int part[1024];
+  const int tid = threadIdx.x;
+  const int64_t per = (n_rows + 1023) / 1024;
+  const int64_t b0 = min<int64_t>(tid * per, n_rows), b1 = min<int64_t>(b0 + per, n_rows);
+  int s = 0;
+  for (int64_t i = b0; i < b1; ++i) s += cnt[i];
+  part[tid] = s;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int v = tid >= o ? part[tid - o] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int run = part[tid] - s;
+  for (int64_t i = b0; i < b1; ++i) {
+    row_ptr[i] = run;
+    run += cnt[i];
+  }
+  if (tid == 1023) row_ptr[n_rows] = part[1023];
+  if (head_nnz) {
+    for (int bh = tid; bh < n_bh; bh += 1024) {
+      int hs = 0;
+      for (int i = 0; i < n_blk; ++i) hs += cnt[(int64_t)bh * n_blk + i];
+      head_nnz[bh] = hs;
+    }
+  }
+}
+
+// Kept-id bitmask -> ascending column indices at row_ptr[r].
+__global__ __launch_bounds__(256) void k_emit(const uint64_t* __restrict__ rowmask, const int32_t* __restrict__ row_ptr,
+                                              int32_t* __restrict__ col_idx, int nw, int64_t n_rows) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t r = (int64_t)blockIdx.x * 4 + wv;
+  if (r >= n_rows) return;
+  int base = row_ptr[r];
+  const uint64_t below = (1ull << lane) - 1;
+  for (int i = 0; i < nw; ++i) {
+    const uint64_t m = rowmask[r * nw + i];
+    if (m >> lane & 1) col_idx[base + __popcll(m & below)] = 64 * i + lane;
+    base += __popcll(m);
+  }
+}
+
+template <typename T, int D>
+void launch_pool(fva_plan_t plan, const void* q, const void* k, hipStream_t s) {
+  const fva_plan_info& in = plan->info;
+  const int bh = plan->desc.batch * plan->desc.heads;
+  const bool sub = in.n_sub != 0;
+  dim3 grid(in.n_blk, bh, sub ? 1 : 2);
+  hipLaunchKernelGGL((k_pool<T, D>), grid, dim3(64), 0, s, (const T*)q, (const T*)k, plan->qbar, plan->kbar,
+                     plan->blk_cnt, in.n_blk, in.n_pad);
+  if (sub)
+    hipLaunchKernelGGL((k_pool_sub<T, D>), dim3(in.n_blk, bh), dim3(64), 0, s, (const T*)k, plan->kbar,
+                       plan->sub_pos, plan->sub_cnt, in.n_blk, in.n_pad);
+}
+
+template <int D>
+void launch_score(fva_plan_t plan, hipStream_t s) {
+  const fva_plan_info& in = plan->info;
+  const int bh = plan->desc.batch * plan->desc.heads;
+  dim3 grid((in.n_blk + 31) / 32, bh);
+  const float scale = 1.0f / sqrtf((float)D);
+  if (in.n_sub)
+    hipLaunchKernelGGL((k_score<true, D>), grid, dim3(256), 0, s, plan->qbar, plan->kbar, plan->sub_cnt,
+                       plan->zbuf, plan->rowstat, in.n_blk, scale);
+  else
+    hipLaunchKernelGGL((k_score<false, D>), grid, dim3(256), 0, s, plan->qbar, plan->kbar, plan->sub_cnt,
+                       plan->zbuf, plan->rowstat, in.n_blk, scale);
+}
+
+}  // namespace
+
+extern "C" int fva_select(fva_plan_t plan, const void* q_perm, const void* k_perm, const float* p,
+                          int32_t p_count, int32_t k_min, int32_t slack_mode, const float* scores_in,
+                          float* scores_out, int32_t* row_ptr, int32_t* col_idx, int32_t* head_nnz,
+                          hipStream_t stream) {
+  if (!plan) return fva_fail(FVA_EINVAL, "plan is NULL");
+  const fva_plan_desc& d = plan->desc;
+  const fva_plan_info& in = plan->info;
+  const int n_bh = d.batch * d.heads;
+  if (!p) return fva_fail(FVA_EINVAL, "p is NULL");
+  if (p_count != 1 && p_count != n_bh)
+    return fva_fail(FVA_EINVAL, "p_count %d must be 1 or B*H = %d", p_count, n_bh);
+  if (p_count > FVA_MAX_PHEAD)
+    return fva_fail(FVA_EUNSUPPORTED, "per-head p supports at most %d heads", FVA_MAX_PHEAD);
+  SelectArgs pa;
+  for (int i = 0; i < p_count; ++i) {
+    if (!(p[i] > 0.0f)) return fva_fail(FVA_EINVAL, "p[%d] = %g must be > 0", i, (double)p[i]);
+    pa.p[i] = p[i];
+  }
+  if (k_min < 0) return fva_fail(FVA_EINVAL, "k_min %d must be >= 0", k_min);
+  if (slack_mode != FVA_SLACK_NONE && slack_mode != FVA_SLACK_MEDIAN)
+    return fva_fail(FVA_EINVAL, "unknown slack mode %d", slack_mode);
+  if (slack_mode == FVA_SLACK_MEDIAN && n_bh > FVA_MAX_PHEAD)
+    return fva_fail(FVA_EUNSUPPORTED, "slack fill supports at most %d heads", FVA_MAX_PHEAD);
+  if (!row_ptr || !col_idx) return fva_fail(FVA_EINVAL, "row_ptr / col_idx is NULL");
+  if (!scores_in && (!q_perm || !k_perm)) return fva_fail(FVA_EINVAL, "q_perm / k_perm is NULL");
+
+  if (!scores_in) {
+    if (d.dtype == FVA_DTYPE_BF16) {
+      if (d.head_dim == 128) launch_pool<uint16_t, 128>(plan, q_perm, k_perm, stream);
+      else launch_pool<uint16_t, 64>(plan, q_perm, k_perm, stream);
+    } else {
+      if (d.head_dim == 128) launch_pool<float, 128>(plan, q_perm, k_perm, stream);
+      else launch_pool<float, 64>(plan, q_perm, k_perm, stream);
+    }
+    if (d.head_dim == 128) launch_score<128>(plan, stream);
+    else launch_score<64>(plan, stream);
+  }
+  float* s_out = scores_out ? scores_out : (scores_in ? nullptr : plan->zbuf);
+  const float* s_read = scores_in ? scores_in : s_out;
+  const unsigned sel_grid = (unsigned)((in.n_rows + 3) / 4);
+  const int ni = (in.n_blk + 63) / 64;
+#define FVA_SELECT(NI)                                                                                  \
+  hipLaunchKernelGGL((k_select<NI>), dim3(sel_grid), dim3(256), 0, stream, plan->zbuf, plan->rowstat,  \
+                     scores_in, s_out, pa, p_count, k_min, in.n_blk, in.n_rows, plan->rowcnt,           \
+                     plan->rowmask, plan->nw)
+  if (ni <= 4) FVA_SELECT(4);
+  else if (ni <= 8) FVA_SELECT(8);
+  else if (ni <= 16) FVA_SELECT(16);
+  else if (ni <= 24) FVA_SELECT(24);
+  else if (ni <= 32) FVA_SELECT(32);
+  else FVA_SELECT(64);
+#undef FVA_SELECT
+  if (slack_mode == FVA_SLACK_MEDIAN) {
+    hipLaunchKernelGGL(k_slack_target, dim3(1), dim3(1024), 0, stream, plan->rowcnt, in.n_blk, n_bh,
+                       plan->headcnt, plan->deficit);
+    hipLaunchKernelGGL(k_slack_thresh, dim3(n_bh), dim3(1024), 0, stream, s_read, plan->rowmask, plan->nw,
+                       in.n_blk, plan->deficit, plan->slack_thr);
+    hipLaunchKernelGGL(k_slack_apply, dim3(sel_grid), dim3(256), 0, stream, s_read, plan->rowmask,
+                       plan->rowcnt, plan->nw, in.n_blk, in.n_rows, plan->deficit, plan->slack_thr);
+  }
+  hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, stream, plan->rowcnt, in.n_rows, row_ptr, head_nnz,
+                     in.n_blk, n_bh);
+  hipLaunchKernelGGL(k_emit, dim3(sel_grid), dim3(256), 0, stream, plan->rowmask, row_ptr, col_idx, plan->nw,
+                     in.n_rows);
+  return fva_after_launch(stream, "fva_select");
+}

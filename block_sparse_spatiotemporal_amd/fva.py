@@ -1,0 +1,264 @@
+"""ctypes binding of libfva.so (C ABI in include/fva.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  Functions keep the C names; tensors are torch tensors on the GPU
+(torch provides device memory and streams).  If the library is missing this
+module raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfva.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "fva.h")
+
+FVA_OK, FVA_EINVAL, FVA_EUNSUPPORTED, FVA_EHIP, FVA_ENOMEM = range(5)
+ORDER = {"tile": 0, "hilbert": 1}
+DTYPE = {"bf16": 0, "f32": 1}
+LAYOUT_ROWS, LAYOUT_VT = 0, 1
+SLACK = {"none": 0, "median": 1}
+SCHED = {"persistent": 0, "plain": 1}
+
+c_i32, c_i64, c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+
+
+class fva_plan_desc(ctypes.Structure):
+    _fields_ = [("batch", c_i32), ("heads", c_i32), ("head_dim", c_i32), ("grid", c_i32 * 3),
+                ("tile", c_i32 * 3), ("order", c_i32), ("sub", c_i32 * 3), ("dtype", c_i32)]
+
+
+class fva_plan_info(ctypes.Structure):
+    _fields_ = [("n_tokens", c_i64), ("n_pad", c_i64), ("n_blk", c_i32), ("n_sub", c_i32),
+                ("padded", c_i32 * 3), ("n_rows", c_i64), ("max_nnz", c_i64),
+                ("workspace_bytes", c_i64), ("max_wg", c_i32)]
+
+
+class FvaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"fva error {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Open libfva.so (built by block_sparse_spatiotemporal_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: run __graft_entry__.build() first")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER
+        sig = {
+            "fva_plan_dims": (c_i32, [P(fva_plan_desc), P(fva_plan_info)]),
+            "fva_plan_tables": (c_i32, [P(fva_plan_desc), c_vp, c_vp, c_vp, c_vp]),
+            "fva_plan_create": (c_i32, [P(c_vp), P(fva_plan_desc), c_vp]),
+            "fva_plan_query": (c_i32, [c_vp, P(fva_plan_info)]),
+            "fva_plan_destroy": (None, [c_vp]),
+            "fva_permute": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_vp]),
+            "fva_select": (c_i32, [c_vp, c_vp, c_vp, P(ctypes.c_float), c_i32, c_i32, c_i32, c_vp, c_vp,
+                                   c_vp, c_vp, c_vp, c_vp]),
+            "fva_attention": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp]),
+            "fva_unpermute": (c_i32, [c_vp, c_vp, c_vp, c_vp]),
+            "fva_last_error": (ctypes.c_char_p, []),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype, f.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def header_symbols() -> list[str]:
+    """Entry points declared in include/fva.h."""
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(fva_\w+)\s*\(", txt, re.M)))
+
+
+def _check(rc: int):
+    if rc != FVA_OK:
+        raise FvaError(rc, lib().fva_last_error().decode())
+
+
+def make_desc(batch, heads, head_dim, grid, tile=(4, 4, 4), order="tile", sub=(0, 0, 0), dtype="bf16"):
+    d = fva_plan_desc()
+    d.batch, d.heads, d.head_dim = batch, heads, head_dim
+    d.grid[:] = list(grid)
+    d.tile[:] = list(tile)
+    d.order = ORDER[order] if isinstance(order, str) else int(order)
+    d.sub[:] = list(sub)
+    d.dtype = DTYPE[dtype] if isinstance(dtype, str) else int(dtype)
+    return d
+
+
+def fva_plan_dims(desc: fva_plan_desc) -> fva_plan_info:
+    info = fva_plan_info()
+    _check(lib().fva_plan_dims(ctypes.byref(desc), ctypes.byref(info)))
+    return info
+
+
+def fva_plan_tables(desc: fva_plan_desc):
+    """Host tables as numpy arrays: (perm, blk_cnt, blk_mask, sub_id)."""
+    import numpy as np
+    info = fva_plan_dims(desc)
+    perm = np.empty(info.n_pad, np.int32)
+    cnt = np.empty(info.n_blk, np.int32)
+    mask = np.empty(info.n_blk, np.uint64)
+    sid = np.empty(info.n_pad, np.int32)
+    _check(lib().fva_plan_tables(ctypes.byref(desc), perm.ctypes.data, cnt.ctypes.data, mask.ctypes.data,
+                                 sid.ctypes.data))
+    return perm, cnt, mask, sid
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return c_vp(s.cuda_stream)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("tensors must be contiguous CUDA/HIP tensors")
+    return c_vp(t.data_ptr())
+
+
+class Plan:
+    """Owns an fva_plan_t; see include/fva.h for the meaning of every field."""
+
+    def __init__(self, batch, heads, head_dim, grid, tile=(4, 4, 4), order="tile", sub=(0, 0, 0),
+                 dtype="bf16", stream=None):
+        self.desc = make_desc(batch, heads, head_dim, grid, tile, order, sub, dtype)
+        self.dtype = dtype
+        self.torch_dtype = torch.bfloat16 if dtype == "bf16" else torch.float32
+        h = c_vp()
+        _check(lib().fva_plan_create(ctypes.byref(h), ctypes.byref(self.desc), _stream(stream)))
+        self.handle = h
+        self.info = fva_plan_info()
+        _check(lib().fva_plan_query(h, ctypes.byref(self.info)))
+
+    @property
+    def n_blk(self):
+        return self.info.n_blk
+
+    @property
+    def n_pad(self):
+        return self.info.n_pad
+
+    @property
+    def n_rows(self):
+        return self.info.n_rows
+
+    def raster_shape(self):
+        d = self.desc
+        return (d.batch, self.info.n_tokens, d.heads, d.head_dim)
+
+    def perm_shape(self):
+        d = self.desc
+        return (d.batch, d.heads, self.info.n_pad, d.head_dim)
+
+    def destroy(self):
+        if getattr(self, "handle", None) is not None and _lib is not None:
+            lib().fva_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def _expect(t, shape, dtype, name):
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name}: expected {tuple(shape)} {dtype}, got {tuple(t.shape)} {t.dtype}")
+
+
+def fva_permute(plan: Plan, x_raster, x_perm, layout=LAYOUT_ROWS, stream=None):
+    _expect(x_raster, plan.raster_shape(), plan.torch_dtype, "x_raster")
+    if x_perm.numel() != plan.desc.batch * plan.desc.heads * plan.n_pad * plan.desc.head_dim \
+            or x_perm.dtype != plan.torch_dtype:
+        raise ValueError("x_perm has the wrong size or dtype")
+    _check(lib().fva_permute(plan.handle, _ptr(x_raster), _ptr(x_perm), int(layout), _stream(stream)))
+
+
+def fva_unpermute(plan: Plan, x_perm, x_raster, stream=None):
+    _expect(x_raster, plan.raster_shape(), plan.torch_dtype, "x_raster")
+    _expect(x_perm, plan.perm_shape(), plan.torch_dtype, "x_perm")
+    _check(lib().fva_unpermute(plan.handle, _ptr(x_perm), _ptr(x_raster), _stream(stream)))
+
+
+def fva_select(plan: Plan, q_perm, k_perm, p, k_min, row_ptr, col_idx, slack="none", scores_in=None,
+               scores_out=None, head_nnz=None, stream=None):
+    d = plan.desc
+    sq = (d.batch, d.heads, plan.n_blk, plan.n_blk)
+    if scores_in is None:
+        _expect(q_perm, plan.perm_shape(), plan.torch_dtype, "q_perm")
+        _expect(k_perm, plan.perm_shape(), plan.torch_dtype, "k_perm")
+    else:
+        _expect(scores_in, sq, torch.float32, "scores_in")
+    if scores_out is not None:
+        _expect(scores_out, sq, torch.float32, "scores_out")
+    _expect(row_ptr, (plan.n_rows + 1,), torch.int32, "row_ptr")
+    if col_idx.dtype != torch.int32 or col_idx.numel() < plan.info.max_nnz:
+        raise ValueError("col_idx must be int32 with capacity max_nnz")
+    if head_nnz is not None:
+        _expect(head_nnz, (d.batch * d.heads,), torch.int32, "head_nnz")
+    pl = [float(x) for x in (p if hasattr(p, "__len__") else [p])]
+    parr = (ctypes.c_float * len(pl))(*pl)
+    _check(lib().fva_select(plan.handle, _ptr(q_perm) if q_perm is not None else None,
+                            _ptr(k_perm) if k_perm is not None else None, parr, len(pl), int(k_min),
+                            SLACK[slack] if isinstance(slack, str) else int(slack), _ptr(scores_in),
+                            _ptr(scores_out), _ptr(row_ptr), _ptr(col_idx), _ptr(head_nnz), _stream(stream)))
+
+
+def fva_attention(plan: Plan, q_perm, k_perm, vt_perm, row_ptr, col_idx, o_perm, sched="persistent",
+                  wg_times=None, stream=None):
+    for t, n in ((q_perm, "q_perm"), (k_perm, "k_perm"), (o_perm, "o_perm")):
+        _expect(t, plan.perm_shape(), plan.torch_dtype, n)
+    if vt_perm.numel() != o_perm.numel() or vt_perm.dtype != plan.torch_dtype:
+        raise ValueError("vt_perm has the wrong size or dtype")
+    _expect(row_ptr, (plan.n_rows + 1,), torch.int32, "row_ptr")
+    if col_idx.dtype != torch.int32:
+        raise ValueError("col_idx must be int32")
+    if wg_times is not None and (wg_times.dtype != torch.int64 or wg_times.numel() < 2 * plan.info.max_wg):
+        raise ValueError("wg_times must be int64 with 2*max_wg entries")
+    _check(lib().fva_attention(plan.handle, _ptr(q_perm), _ptr(k_perm), _ptr(vt_perm), _ptr(row_ptr),
+                               _ptr(col_idx), _ptr(o_perm), SCHED[sched] if isinstance(sched, str) else int(sched),
+                               _ptr(wg_times), _stream(stream)))
+
+
+class Buffers:
+    """Device buffers for one full call on a plan (block-order Q/K/V^T/O,
+    CSR lists, per-head counts), allocated once and reused."""
+
+    def __init__(self, plan: Plan):
+        dev = torch.device("cuda")
+        shp = plan.perm_shape()
+        self.q = torch.empty(shp, dtype=plan.torch_dtype, device=dev)
+        self.k = torch.empty(shp, dtype=plan.torch_dtype, device=dev)
+        self.vt = torch.empty(shp, dtype=plan.torch_dtype, device=dev)
+        self.o = torch.empty(shp, dtype=plan.torch_dtype, device=dev)
+        self.row_ptr = torch.empty(plan.n_rows + 1, dtype=torch.int32, device=dev)
+        self.col_idx = torch.empty(plan.info.max_nnz, dtype=torch.int32, device=dev)
+        self.head_nnz = torch.empty(plan.desc.batch * plan.desc.heads, dtype=torch.int32, device=dev)
+
+
+def attention_call(plan: Plan, q, k, v, out, p, k_min, bufs: Buffers, slack="none", sched="persistent",
+                   scores_out=None, wg_times=None, stream=None):
+    """One full attention call, raster in and raster out:
+    permute(Q, K, V) -> select -> attention -> unpermute."""
+    fva_permute(plan, q, bufs.q, LAYOUT_ROWS, stream)
+    fva_permute(plan, k, bufs.k, LAYOUT_ROWS, stream)
+    fva_permute(plan, v, bufs.vt, LAYOUT_VT, stream)
+    fva_select(plan, bufs.q, bufs.k, p, k_min, bufs.row_ptr, bufs.col_idx, slack=slack, scores_out=scores_out,
+               head_nnz=bufs.head_nnz, stream=stream)
+    fva_attention(plan, bufs.q, bufs.k, bufs.vt, bufs.row_ptr, bufs.col_idx, bufs.o, sched=sched,
+                  wg_times=wg_times, stream=stream)
+    fva_unpermute(plan, bufs.o, out, stream)

@@ -1,0 +1,221 @@
+/*
+ * fva.h - training-free block-sparse spatiotemporal attention on AMD Instinct
+ * MI355X (gfx950).  C ABI of libfva.so.
+ *
+ * The method (sources are the explainer/review pages, cited by title and
+ * section):
+ *   - "Video Sparse Attention" explainer, dialogue and section 3: tokens of
+ *     the (t, h, w) latent grid are grouped into small (4,4,4) cubes; a light
+ *     coarse stage pools each cube and predicts cube importance from the
+ *     pooled tiles; a fine stage runs token-level attention only inside the
+ *     chosen cubes, on a block layout that suits the hardware.
+ *   - "FVAttn: Adaptive Sparse Attention with Runtime Load Balancing for Video
+ *     Generation", sections 00-02: cubes are kept per query block by adaptive
+ *     Top-p routing with a Top-k safety floor; per-head load is uneven and is
+ *     balanced at run time; spare capacity buys extra high-value blocks.
+ *   - "DFSAttn: Dynamic Fine-grained Sparse Attention for Efficient Video
+ *     Generation", tricks 1-2: an optional 3D Hilbert-curve token order and
+ *     block scores formed by summing finer sub-block scores.
+ *
+ * Call sequence for one attention call on one HIP stream:
+ *   fva_permute(Q, rows) ; fva_permute(K, rows) ; fva_permute(V, vt)
+ *   fva_select(...)      -> CSR block lists (row_ptr, col_idx)
+ *   fva_attention(...)   -> O in block order
+ *   fva_unpermute(O)     -> O in raster order
+ *
+ * Conventions shared by every call:
+ *   - Raster tensors are [B, N, H, D] contiguous, token n = (t*GH + h)*GW + w
+ *     (w fastest) on the unpadded grid (GT, GH, GW).
+ *   - Block-order tensors are [B, H, N_pad, D] contiguous.  Position
+ *     pos = blk*64 + local; pad positions hold zeros.
+ *   - Element type is bfloat16 or float32 as fixed by the plan's dtype.
+ *   - Every tensor pointer is a device pointer owned by the caller; it must
+ *     stay valid until the stream has passed the call.
+ *   - All calls are asynchronous on `stream` and never synchronise the host.
+ *     Arguments are validated before anything is enqueued: on a non-zero
+ *     status nothing was written.  A kernel fault surfaces at the caller's
+ *     next synchronisation; with FVA_DEBUG=1 in the environment every call
+ *     synchronises and checks after its launches.
+ *   - A plan is not safe for concurrent calls on different streams: its
+ *     workspace is shared.  No C++ exception crosses this interface.
+ */
+#ifndef FVA_H
+#define FVA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+  FVA_OK = 0,
+  FVA_EINVAL = 1,        /* bad argument (null pointer, out-of-range value)  */
+  FVA_EUNSUPPORTED = 2,  /* valid but not built: tile volume != 64, head_dim
+                            not 64/128, unknown dtype, too many blocks ...   */
+  FVA_EHIP = 3,          /* a HIP runtime call failed                        */
+  FVA_ENOMEM = 4         /* device or host allocation failed                 */
+};
+
+enum { FVA_ORDER_TILE = 0, FVA_ORDER_HILBERT = 1 };
+enum { FVA_DTYPE_BF16 = 0, FVA_DTYPE_F32 = 1 };
+/* Block-order layouts written by fva_permute. */
+enum {
+  FVA_LAYOUT_ROWS = 0,   /* [B, H, N_pad, D]: used for Q and K               */
+  FVA_LAYOUT_VT = 1      /* per 64-token block, two 32-key halves, each a
+                            [D][32] matrix whose 32 key slots are ordered for
+                            the matrix-core operand (see fva_permute): used
+                            for V                                            */
+};
+enum { FVA_SLACK_NONE = 0, FVA_SLACK_MEDIAN = 1 };
+enum { FVA_SCHED_PERSISTENT = 0, FVA_SCHED_PLAIN = 1 };
+
+typedef struct fva_plan_s* fva_plan_t;
+
+/* Problem statement: token grid, tile, heads, head_dim ("Video Sparse
+ * Attention" section 3 for the (4,4,4) cubes; "DFSAttn" tricks 1-2 for the
+ * Hilbert order and sub-blocks). */
+typedef struct {
+  int32_t batch;       /* B >= 1                                             */
+  int32_t heads;       /* H >= 1                                             */
+  int32_t head_dim;    /* D in {64, 128}                                     */
+  int32_t grid[3];     /* (GT, GH, GW) token grid, each >= 1                 */
+  int32_t tile[3];     /* cube shape; product must be 64                     */
+  int32_t order;       /* FVA_ORDER_TILE or FVA_ORDER_HILBERT (needs
+                          tile (4,4,4))                                      */
+  int32_t sub[3];      /* sub-block shape for key-side sub-block scoring:
+                          {0,0,0} = off, else divides tile with volume 8     */
+  int32_t dtype;       /* FVA_DTYPE_BF16 or FVA_DTYPE_F32                    */
+} fva_plan_desc;
+
+typedef struct {
+  int64_t n_tokens;        /* GT*GH*GW                                       */
+  int64_t n_pad;           /* padded tokens = n_blk * 64                     */
+  int32_t n_blk;           /* blocks per head                                */
+  int32_t n_sub;           /* sub-blocks per block (0 or 8)                  */
+  int32_t padded[3];       /* grid rounded up to tile multiples              */
+  int64_t n_rows;          /* B*H*n_blk: rows of the block lists             */
+  int64_t max_nnz;         /* n_rows*n_blk: capacity col_idx must have       */
+  int64_t workspace_bytes; /* device bytes the plan owns                     */
+  int32_t max_wg;          /* entries/2 that fva_attention's wg_times needs  */
+} fva_plan_info;
+
+/* Validate a descriptor and report sizes.  Host only: touches no device.
+ * Returns FVA_EINVAL / FVA_EUNSUPPORTED on a bad descriptor. */
+int fva_plan_dims(const fva_plan_desc* desc, fva_plan_info* info);
+
+/* Build the plan's host tables into caller-owned host arrays (any may be
+ * NULL).  Host only; for inspection and tests.
+ *   perm[n_pad]      raster token index of each block-order position, or -1
+ *                    for a pad position ("Video Sparse Attention" section 3;
+ *                    with FVA_ORDER_HILBERT, positions are ranked by the 3D
+ *                    Hilbert index of their padded-grid coordinate on the
+ *                    enclosing 2^m cube, "DFSAttn" trick 1)
+ *   blk_cnt[n_blk]   valid tokens per block
+ *   blk_mask[n_blk]  bit i set when local position i of the block is valid
+ *   sub_id[n_pad]    sub-block index within the block (raster order of the
+ *                    sub-cube inside the tile), or -1 when sub-blocks are off
+ */
+int fva_plan_tables(const fva_plan_desc* desc, int32_t* perm, int32_t* blk_cnt,
+                    uint64_t* blk_mask, int32_t* sub_id);
+
+/* Create a plan: validate, build the tables, allocate the device tables and
+ * the workspace (pooled Q/K, block logits and scores, selection scratch,
+ * work list), and enqueue the table upload on `stream`.  *out receives the
+ * handle.  The plan owns its device memory until fva_plan_destroy. */
+int fva_plan_create(fva_plan_t* out, const fva_plan_desc* desc, hipStream_t stream);
+
+/* Sizes of an existing plan. */
+int fva_plan_query(fva_plan_t plan, fva_plan_info* info);
+
+/* Synchronise the plan's creation stream and free everything it owns.
+ * NULL is accepted. */
+void fva_plan_destroy(fva_plan_t plan);
+
+/* Gather a raster tensor [B, N, H, D] into block order ("Video Sparse
+ * Attention" section 3: the tokens of a cube become contiguous so that the
+ * fine stage works block by block).  Pad positions are written as zero.
+ *   layout = FVA_LAYOUT_ROWS : x_perm is [B, H, N_pad, D].
+ *   layout = FVA_LAYOUT_VT   : for block (b, h, j) at element offset
+ *        ((b*H + h)*n_blk + j)*64*D, half u = key/32 occupies D*32 elements
+ *        starting at u*D*32; inside it element [d*32 + s] holds x[key][d]
+ *        with, for k = key%32, c = k/16, r = k%16:
+ *        s = 16*c + 8*((r/4)%2) + (r%4) + 4*(r/8).
+ * x_raster and x_perm must not overlap. */
+int fva_permute(fva_plan_t plan, const void* x_raster, void* x_perm, int32_t layout,
+                hipStream_t stream);
+
+/* Coarse stage and routing ("Video Sparse Attention" dialogue and section 3;
+ * "FVAttn" sections 00 and 02; "DFSAttn" trick 2):
+ *   pool   q_bar_I = mean of the valid rows of Q block I (k_bar likewise; with
+ *          sub-blocks on, one k_bar per non-empty (J, s) pair), fp32;
+ *   score  S_I. = softmax_J(q_bar_I . k_bar_J / sqrt(D)) in fp32; with
+ *          sub-blocks, the softmax runs over all non-empty (J, s) and S_IJ is
+ *          the sum over s (computed as a log-sum-exp block logit);
+ *   select per row, order J by (S desc, J asc) and keep the shortest prefix
+ *          whose mass reaches p, then at least min(k_min, n_blk) blocks;
+ *          p >= 1 keeps all blocks.  The mass is the exact integer sum of
+ *          floor(clamp(S, 0, 1) * 2^47) against ceil(p * 2^47); NaN scores
+ *          count as 0.  Kept ids are emitted ascending;
+ *   slack  FVA_SLACK_MEDIAN: every (b, h) whose block count is below the
+ *          lower median over the call's B*H heads gets the unselected (I, J)
+ *          pairs of highest score (ties: lower I, then lower J) until its
+ *          count equals that median ("FVAttn" section 02, one-GPU reading).
+ * Arguments:
+ *   q_perm, k_perm  block-order Q and K (FVA_LAYOUT_ROWS); ignored when
+ *                   scores_in is given.
+ *   p, p_count      host array: p_count == 1 (one p for all heads) or
+ *                   p_count == B*H (per (b, h), b major); 0 < p; B*H <= 512
+ *                   when per-head.
+ *   k_min           >= 0.
+ *   scores_in       optional device [B, H, n_blk, n_blk] fp32: skip pool and
+ *                   score and select on these values instead.
+ *   scores_out      optional device [B, H, n_blk, n_blk] fp32: receives the
+ *                   scores selection used.
+ *   row_ptr         device int32 [n_rows + 1], rows r = (b*H + h)*n_blk + I.
+ *   col_idx         device int32, capacity max_nnz; only row_ptr[n_rows]
+ *                   entries are written.
+ *   head_nnz        optional device int32 [B*H]: kept blocks per (b, h). */
+int fva_select(fva_plan_t plan, const void* q_perm, const void* k_perm, const float* p,
+               int32_t p_count, int32_t k_min, int32_t slack_mode, const float* scores_in,
+               float* scores_out, int32_t* row_ptr, int32_t* col_idx, int32_t* head_nnz,
+               hipStream_t stream);
+
+/* Fine stage ("Video Sparse Attention" section 3; load balancing of uneven
+ * per-head work from "FVAttn" section 02, here across the compute units of
+ * one GPU).  For every valid query token i of block I:
+ *   o_i = sum_j softmax_j(q_i . k_j / sqrt(D)) v_j
+ * over the valid key tokens j of the blocks listed in row (b, h, I).  Pad
+ * query rows of o_perm are written as zero; a row with no blocks gives zero.
+ *   q_perm, k_perm  FVA_LAYOUT_ROWS;  vt_perm  FVA_LAYOUT_VT.
+ *   row_ptr, col_idx  any valid CSR over the plan's rows (ids in
+ *                   [0, n_blk), ascending or not), e.g. from fva_select.
+ *   o_perm          [B, H, N_pad, D], plan dtype.
+ *   sched_mode      FVA_SCHED_PERSISTENT: a persistent grid pops rows from a
+ *                   device work list sorted by decreasing cost;
+ *                   FVA_SCHED_PLAIN: one workgroup per row in list order.
+ *   wg_times        optional device uint64 [2*max_wg]: per workgroup the
+ *                   start and end of its busy time (100 MHz wall clock).
+ * bf16: QK^T and PV run on bf16 matrix cores with fp32 accumulation, the
+ * softmax in fp32, P rounded to bf16 before PV, O rounded to bf16 at the end.
+ * fp32: fp32 throughout. */
+int fva_attention(fva_plan_t plan, const void* q_perm, const void* k_perm, const void* vt_perm,
+                  const int32_t* row_ptr, const int32_t* col_idx, void* o_perm,
+                  int32_t sched_mode, uint64_t* wg_times, hipStream_t stream);
+
+/* Scatter block-order [B, H, N_pad, D] (FVA_LAYOUT_ROWS) back to raster
+ * [B, N, H, D], dropping pad positions.  Inverse of fva_permute. */
+int fva_unpermute(fva_plan_t plan, const void* x_perm, void* x_raster, hipStream_t stream);
+
+/* Message for the last non-zero status returned on this thread. */
+const char* fva_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FVA_H */

@@ -1,0 +1,101 @@
+"""The C ABI library loads, exports every declared entry point, validates
+arguments on the host, and builds plan tables identical to the oracle's.
+CPU only: no call here launches device work."""
+import ctypes
+
+import numpy as np
+import pytest
+
+from block_sparse_spatiotemporal_amd import fva
+from oracle import fva_oracle as O
+
+
+def test_library_exports_every_declared_symbol():
+    L = fva.lib()
+    syms = fva.header_symbols()
+    assert len(syms) >= 10
+    for s in syms:
+        assert hasattr(L, s), s
+
+
+@pytest.mark.parametrize("grid,order,sub,dtype,hd", [
+    ((8, 16, 16), "tile", (0, 0, 0), "f32", 64),
+    ((21, 30, 52), "tile", (0, 0, 0), "bf16", 128),
+    ((21, 45, 80), "hilbert", (2, 2, 2), "bf16", 128),
+])
+def test_plan_dims(grid, order, sub, dtype, hd):
+    d = fva.make_desc(2, 40, hd, grid, order=order, sub=sub, dtype=dtype)
+    info = fva.fva_plan_dims(d)
+    pl = O.plan(grid, order=order, sub=sub)
+    assert info.n_blk == pl.n_blk and info.n_pad == pl.n_pad
+    assert info.n_rows == 2 * 40 * pl.n_blk and info.max_nnz == info.n_rows * pl.n_blk
+    assert info.n_sub == (8 if any(sub) else 0)
+    assert tuple(info.padded) == pl.padded
+    assert info.workspace_bytes > 4 * 2 * 40 * pl.n_blk ** 2
+
+
+@pytest.mark.parametrize("grid,tile,order,sub", [
+    ((5, 6, 7), (4, 4, 4), "tile", (0, 0, 0)),
+    ((21, 30, 52), (4, 4, 4), "tile", (2, 2, 2)),
+    ((3, 17, 9), (2, 4, 8), "tile", (1, 2, 4)),
+    ((6, 9, 12), (4, 4, 4), "hilbert", (2, 2, 2)),
+    ((21, 45, 80), (4, 4, 4), "hilbert", (2, 2, 2)),
+])
+def test_plan_tables_match_oracle(grid, tile, order, sub):
+    d = fva.make_desc(1, 1, 64, grid, tile=tile, order=order, sub=sub)
+    perm, cnt, mask, sid = fva.fva_plan_tables(d)
+    pl = O.plan(grid, tile=tile, order=order, sub=sub)
+    assert np.array_equal(perm, pl.perm)
+    assert np.array_equal(cnt, pl.cnt)
+    valid = (pl.perm >= 0).reshape(pl.n_blk, 64)
+    ref_mask = (valid.astype(np.uint64) << np.arange(64, dtype=np.uint64)).sum(axis=1, dtype=np.uint64)
+    assert np.array_equal(mask, ref_mask)
+    if any(sub):
+        assert np.array_equal(sid, pl.sub_id)
+    else:
+        assert np.all(sid == -1)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("head_dim", 96, fva.FVA_EUNSUPPORTED),
+    ("batch", 0, fva.FVA_EINVAL),
+    ("heads", -1, fva.FVA_EINVAL),
+    ("order", 7, fva.FVA_EINVAL),
+    ("dtype", 9, fva.FVA_EUNSUPPORTED),
+])
+def test_plan_validation_codes(field, value, code):
+    d = fva.make_desc(1, 2, 128, (21, 30, 52))
+    setattr(d, field, value)
+    with pytest.raises(fva.FvaError) as e:
+        fva.fva_plan_dims(d)
+    assert e.value.code == code
+    assert fva.lib().fva_last_error().decode()
+
+
+def test_plan_validation_shapes():
+    bad = [
+        (dict(tile=(4, 4, 2)), fva.FVA_EUNSUPPORTED),           # volume 32
+        (dict(tile=(2, 4, 8), order="hilbert"), fva.FVA_EUNSUPPORTED),
+        (dict(sub=(2, 2, 1)), fva.FVA_EUNSUPPORTED),            # volume 4
+        (dict(sub=(3, 2, 2)), fva.FVA_EUNSUPPORTED),            # does not divide
+        (dict(grid=(0, 30, 52)), fva.FVA_EINVAL),
+        (dict(grid=(64, 64, 80)), fva.FVA_EUNSUPPORTED),        # too many blocks
+    ]
+    for kw, code in bad:
+        args = dict(batch=1, heads=2, head_dim=128, grid=(21, 30, 52))
+        args.update(kw)
+        with pytest.raises(fva.FvaError) as e:
+            fva.fva_plan_dims(fva.make_desc(**args))
+        assert e.value.code == code, kw
+
+
+def test_null_arguments_rejected_before_any_device_work():
+    L = fva.lib()
+    assert L.fva_plan_dims(None, None) == fva.FVA_EINVAL
+    assert L.fva_plan_create(None, None, None) == fva.FVA_EINVAL
+    assert L.fva_permute(None, None, None, 0, None) == fva.FVA_EINVAL
+    assert L.fva_unpermute(None, None, None, None) == fva.FVA_EINVAL
+    assert L.fva_attention(None, None, None, None, None, None, None, 0, None, None) == fva.FVA_EINVAL
+    p = (ctypes.c_float * 1)(0.9)
+    assert L.fva_select(None, None, None, p, 1, 0, 0, None, None, None, None, None, None) == fva.FVA_EINVAL
+    L.fva_plan_destroy(None)   # accepted

@@ -1,0 +1,232 @@
+"""GPU path against the CPU oracle, element by element, through the C ABI.
+
+Tolerances: block lists bit-exact when selection reads the oracle's scores;
+end-to-end lists epsilon-valid (1e-6) against the oracle's fp64 scores;
+attention max-abs 2e-2 (bf16) / 1e-4 (fp32) against the oracle run on the
+same block lists; permutation bitwise.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_spatiotemporal_amd import fva, synth
+from oracle import fva_oracle as O
+from tests._helpers import eps_valid, inputs, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _plan_and_inputs(w, **kw):
+    (q, k, v), (q64, k64, v64), meta = inputs(w)
+    plan = fva.Plan(w.B, w.H, w.D, w.grid, tile=w.tile, order=w.order, sub=w.sub, dtype=w.dtype, **kw)
+    opl = O.plan(w.grid, tile=w.tile, order=w.order, sub=w.sub)
+    return plan, opl, (to_dev(q, w.dtype), to_dev(k, w.dtype), to_dev(v, w.dtype)), (q64, k64, v64), meta
+
+
+def _vt_expected(v_perm64, D):
+    """VT layout from block-order rows, written from the header's formula."""
+    B, H, n_pad, _ = v_perm64.shape
+    out = np.empty((B, H, n_pad // 64, 2, D, 32))
+    slot_of = []
+    for k in range(32):
+        c, r = k // 16, k % 16
+        slot_of.append(16 * c + 8 * ((r // 4) % 2) + (r % 4) + 4 * (r // 8))
+    blocks = v_perm64.reshape(B, H, n_pad // 64, 2, 32, D)
+    for k in range(32):
+        out[:, :, :, :, :, slot_of[k]] = blocks[:, :, :, :, k, :]
+    return out.reshape(B, H, n_pad, D)
+
+
+SMALL = [
+    synth.scaled(synth.WORKLOADS["tiny_f32"]),
+    synth.scaled(synth.WORKLOADS["wan1.3b_480p"], H=2, grid=(9, 10, 13)),
+    synth.scaled(synth.WORKLOADS["wan_720p_hilbert_sub"], H=2, grid=(7, 9, 14)),
+    synth.scaled(synth.WORKLOADS["wan1.3b_480p"], H=2, D=64, grid=(5, 12, 11)),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: f"{w.name}-{w.grid}-D{w.D}")
+def test_permute_unpermute_bitwise(w):
+    plan, opl, (q, k, v), (q64, k64, v64), _ = _plan_and_inputs(w)
+    b = fva.Buffers(plan)
+    fva.fva_permute(plan, q, b.q, fva.LAYOUT_ROWS)
+    fva.fva_permute(plan, v, b.vt, fva.LAYOUT_VT)
+    out = torch.empty_like(q)
+    fva.fva_unpermute(plan, b.q, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_f64(b.q), O.permute(q64, opl))
+    assert np.array_equal(to_f64(b.vt), _vt_expected(O.permute(v64, opl), w.D))
+    assert torch.equal(out, q)
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: f"{w.name}-{w.grid}-D{w.D}")
+def test_scores_match_oracle(w):
+    plan, opl, (q, k, v), (q64, k64, v64), _ = _plan_and_inputs(w)
+    b = fva.Buffers(plan)
+    fva.fva_permute(plan, q, b.q)
+    fva.fva_permute(plan, k, b.k)
+    S = torch.empty(w.B, w.H, plan.n_blk, plan.n_blk, dtype=torch.float32, device="cuda")
+    fva.fva_select(plan, b.q, b.k, 0.9, 4, b.row_ptr, b.col_idx, scores_out=S)
+    torch.cuda.synchronize()
+    qp, kp = O.permute(q64, opl), O.permute(k64, opl)
+    qb = O.pool(qp, opl)
+    if opl.n_sub:
+        kbs, empty = O.pool_sub(kp, opl)
+        ref = O.score_sub(qb, kbs, empty)
+    else:
+        ref = O.score(qb, O.pool(kp, opl))
+    got = S.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(got - ref)) < 1e-6
+    assert np.allclose(got.sum(-1), 1.0, atol=1e-5)
+
+
+def _random_scores(B, H, n, rng, ties=True):
+    S = rng.dirichlet(np.full(n, 0.3), size=(B, H, n))
+    if ties:
+        S[..., 1::7] = S[..., 0:1]        # many exact ties per row
+    return S.astype(np.float32)
+
+
+@pytest.mark.parametrize("n_grid,B,H,k_min,p", [
+    ((4, 8, 16), 1, 3, 0, 0.9),           # 32 blocks
+    ((4, 8, 16), 2, 2, 5, [0.5, 0.99, 0.7, 1.0]),
+    ((21, 30, 52), 1, 2, 16, 0.9),        # 624 blocks
+    ((21, 45, 80), 1, 1, 32, 0.95),       # 1440 blocks
+    ((9, 10, 13), 1, 4, 200, 0.3),        # floor above n
+])
+def test_select_bit_exact_on_oracle_scores(n_grid, B, H, k_min, p):
+    rng = np.random.default_rng(hash((n_grid, B, H)) % 2 ** 32)
+    plan = fva.Plan(B, H, 128, n_grid)
+    n = plan.n_blk
+    S = _random_scores(B, H, n, rng)
+    S[0, 0, 0, :] = 0.0
+    S[0, 0, 0, 3] = np.nan
+    S[0, 0, 0, 5] = 0.7
+    S[0, -1, -1, :] = np.float32(1.0 / n)  # all equal
+    b = fva.Buffers(plan)
+    sin = torch.from_numpy(S).cuda()
+    fva.fva_select(plan, None, None, p, k_min, b.row_ptr, b.col_idx, scores_in=sin, head_nnz=b.head_nnz)
+    torch.cuda.synchronize()
+    ps = p if isinstance(p, list) else [p] * (B * H)
+    rows = [O.select_row(S[bb, h, i], ps[bb * H + h], k_min)
+            for bb in range(B) for h in range(H) for i in range(n)]
+    rp_ref, ci_ref = O.to_csr(rows)
+    rp = b.row_ptr.cpu().numpy()
+    assert np.array_equal(rp, rp_ref)
+    assert np.array_equal(b.col_idx[: rp[-1]].cpu().numpy(), ci_ref)
+    assert np.array_equal(b.head_nnz.cpu().numpy(), O.head_nnz(rp_ref, B, H, n))
+
+
+def test_slack_fill_bit_exact_on_oracle_scores():
+    rng = np.random.default_rng(5)
+    B, H = 1, 9
+    plan = fva.Plan(B, H, 128, (9, 10, 13))
+    n = plan.n_blk
+    S = _random_scores(B, H, n, rng)
+    p = rng.uniform(0.3, 0.99, size=H).astype(np.float32)
+    b = fva.Buffers(plan)
+    fva.fva_select(plan, None, None, p.tolist(), 2, b.row_ptr, b.col_idx, slack="median",
+                   scores_in=torch.from_numpy(S).cuda(), head_nnz=b.head_nnz)
+    torch.cuda.synchronize()
+    rows = [O.select_row(S[0, h, i], p[h], 2) for h in range(H) for i in range(n)]
+    rp0, ci0 = O.to_csr(rows)
+    rp_ref, ci_ref = O.slack_fill(S, rp0, ci0)
+    rp = b.row_ptr.cpu().numpy()
+    assert np.array_equal(rp, rp_ref)
+    assert np.array_equal(b.col_idx[: rp[-1]].cpu().numpy(), ci_ref)
+
+
+def _oracle_scores(w, opl, q64, k64):
+    qp, kp = O.permute(q64, opl), O.permute(k64, opl)
+    qb = O.pool(qp, opl)
+    if opl.n_sub:
+        kbs, empty = O.pool_sub(kp, opl)
+        return O.score_sub(qb, kbs, empty)
+    return O.score(qb, O.pool(kp, opl))
+
+
+@pytest.mark.parametrize("w", SMALL + [synth.scaled(synth.WORKLOADS["tiny_f32_indep"])],
+                         ids=lambda w: f"{w.name}-{w.grid}-D{w.D}")
+@pytest.mark.parametrize("sched", ["persistent", "plain"])
+def test_end_to_end_vs_oracle(w, sched):
+    plan, opl, (q, k, v), (q64, k64, v64), meta = _plan_and_inputs(w)
+    b = fva.Buffers(plan)
+    out = torch.empty_like(q)
+    p = meta["p_head"][0] if not isinstance(w.p, tuple) else meta["p_head"].tolist()
+    fva.attention_call(plan, q, k, v, out, p, w.k_min, b, sched=sched)
+    torch.cuda.synchronize()
+    # selection: epsilon-valid against the oracle's fp64 scores
+    S64 = _oracle_scores(w, opl, q64, k64)
+    rp = b.row_ptr.cpu().numpy().astype(np.int64)
+    ci = b.col_idx[: rp[-1]].cpu().numpy().astype(np.int64)
+    rows = O.from_csr(rp, ci)
+    n = plan.n_blk
+    for r, G in enumerate(rows):
+        bh, i = divmod(r, n)
+        ok, why = eps_valid(G, S64.reshape(-1, n, n)[bh, i], float(np.float32(meta["p_head"][bh % w.H])), w.k_min)
+        assert ok, (r, why)
+        assert np.all(np.diff(G) > 0)
+    # attention on the GPU's own lists
+    ref = O.unpermute(O.attention(O.permute(q64, opl), O.permute(k64, opl), O.permute(v64, opl), rp, ci, opl), opl)
+    tol = 2e-2 if w.dtype == "bf16" else 1e-4
+    err = np.max(np.abs(to_f64(out) - ref))
+    assert err < tol, err
+
+
+def test_persistent_and_plain_bitwise_equal():
+    w = synth.scaled(synth.WORKLOADS["wan1.3b_480p"], H=3, grid=(9, 10, 13))
+    plan, opl, (q, k, v), _, meta = _plan_and_inputs(w)
+    outs = []
+    for sched in ("persistent", "plain", "persistent"):
+        b = fva.Buffers(plan)
+        out = torch.empty_like(q)
+        fva.attention_call(plan, q, k, v, out, 0.9, 16, b, sched=sched)
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+@pytest.mark.parametrize("dtype,tol", [("bf16", 2e-2), ("f32", 1e-4)])
+def test_p1_equals_dense_attention(dtype, tol):
+    w = synth.scaled(synth.WORKLOADS["wan1.3b_480p"], H=2, D=64, grid=(5, 6, 13), dtype=dtype)
+    plan, opl, (q, k, v), (q64, k64, v64), _ = _plan_and_inputs(w)
+    b = fva.Buffers(plan)
+    out = torch.empty_like(q)
+    fva.attention_call(plan, q, k, v, out, 1.0, 0, b)
+    torch.cuda.synchronize()
+    assert b.row_ptr[-1].item() == plan.n_rows * plan.n_blk
+    t = lambda a: torch.from_numpy(a).permute(0, 2, 1, 3)
+    ref = torch.nn.functional.scaled_dot_product_attention(t(q64), t(k64), t(v64)).permute(0, 2, 1, 3).numpy()
+    assert np.max(np.abs(to_f64(out) - ref)) < tol
+
+
+def test_attention_rows_sum_to_one_and_pad_rows_zero():
+    w = synth.scaled(synth.WORKLOADS["wan1.3b_480p"], H=2, grid=(9, 10, 13))
+    plan, opl, (q, k, v), _, _ = _plan_and_inputs(w)
+    b = fva.Buffers(plan)
+    fva.fva_permute(plan, q, b.q)
+    fva.fva_permute(plan, k, b.k)
+    ones = torch.ones_like(v)
+    fva.fva_permute(plan, ones, b.vt, fva.LAYOUT_VT)
+    fva.fva_select(plan, b.q, b.k, 0.8, 3, b.row_ptr, b.col_idx)
+    fva.fva_attention(plan, b.q, b.k, b.vt, b.row_ptr, b.col_idx, b.o)
+    torch.cuda.synchronize()
+    o = to_f64(b.o)
+    valid = opl.perm >= 0
+    assert np.all(o[:, :, ~valid] == 0)
+    assert np.max(np.abs(o[:, :, valid] - 1.0)) < 1e-2
+
+
+def test_wg_times_recorded():
+    w = synth.scaled(synth.WORKLOADS["wan1.3b_480p"], H=2, grid=(9, 10, 13))
+    plan, _, (q, k, v), _, _ = _plan_and_inputs(w)
+    b = fva.Buffers(plan)
+    out = torch.empty_like(q)
+    wt = torch.zeros(2 * plan.info.max_wg, dtype=torch.int64, device="cuda")
+    fva.attention_call(plan, q, k, v, out, 0.9, 16, b, wg_times=wt)
+    torch.cuda.synchronize()
+    t = wt.cpu().numpy().reshape(-1, 2)
+    used = t[t[:, 0] > 0]
+    assert len(used) > 0 and np.all(used[:, 1] >= used[:, 0])
