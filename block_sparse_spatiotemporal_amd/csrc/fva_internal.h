@@ -29,10 +29,11 @@ struct fva_plan_s {
   int32_t* sub_cnt;   // [n_blk][8] valid tokens per sub-block
 
   // workspace
-  float* qbar;        // [B*H*n_blk*D]
-  float* kbar;        // [B*H*n_blk*(n_sub or 1)*D]
-  float* zbuf;        // [B*H*n_blk*n_blk] block logits, then scores in place
-  float2* rowstat;    // [n_rows] (max logit, sum of exp)
+  double* qbar;       // [B*H*n_blk*D] pooled Q, fp64
+  double* kbar;       // [B*H*n_blk*(n_sub or 1)*D] pooled K (per sub-block), fp64
+  double* ybuf;       // [B*H*n_blk*n_blk] block logits, fp64
+  float* sbuf;        // [B*H*n_blk*n_blk] fp32 scores the selection read
+  double2* rowstat;   // [n_rows] (max logit, sum of exp), fp64
   int32_t* rowcnt;    // [n_rows] kept blocks per row
   uint64_t* rowmask;  // [n_rows*nw] kept-block bitmask per row
   int32_t* headcnt;   // [B*H]

@@ -155,10 +155,10 @@ static void layout_workspace(const fva_plan_desc* d, const fva_plan_info& in, si
   offs[2] = c.take(sizeof(int32_t) * in.n_blk);                           // blk_cnt
   offs[3] = c.take(in.n_sub ? 64 * (size_t)in.n_blk : 0);                 // sub_pos
   offs[4] = c.take(in.n_sub ? sizeof(int32_t) * 8 * in.n_blk : 0);        // sub_cnt
-  offs[5] = c.take(sizeof(float) * bh * in.n_blk * d->head_dim);         // qbar
-  offs[6] = c.take(sizeof(float) * bh * in.n_blk * (in.n_sub ? 8 : 1) * d->head_dim);  // kbar
-  offs[7] = c.take(sizeof(float) * bh * in.n_blk * in.n_blk);            // zbuf
-  offs[8] = c.take(sizeof(float2) * in.n_rows);                          // rowstat
+  offs[5] = c.take(sizeof(double) * bh * in.n_blk * d->head_dim);        // qbar
+  offs[6] = c.take(sizeof(double) * bh * in.n_blk * (in.n_sub ? 8 : 1) * d->head_dim);  // kbar
+  offs[7] = c.take(sizeof(double) * bh * in.n_blk * in.n_blk);           // ybuf
+  offs[8] = c.take(sizeof(double2) * in.n_rows);                         // rowstat
   offs[9] = c.take(sizeof(int32_t) * in.n_rows);                         // rowcnt
   offs[10] = c.take(sizeof(uint64_t) * in.n_rows * nw);                  // rowmask
   offs[11] = c.take(sizeof(int32_t) * bh);                               // headcnt
@@ -166,6 +166,7 @@ static void layout_workspace(const fva_plan_desc* d, const fva_plan_info& in, si
   offs[13] = c.take(sizeof(uint64_t) * bh);                              // slack_thr
   offs[14] = c.take(sizeof(int32_t) * in.n_rows);                        // worklist
   offs[15] = c.take(sizeof(int32_t) * 64);                               // counters
+  offs[16] = c.take(sizeof(float) * bh * in.n_blk * in.n_blk);           // sbuf
   *total = c.off;
 }
 
@@ -244,7 +245,7 @@ extern "C" int fva_plan_dims(const fva_plan_desc* desc, fva_plan_info* info) {
   if (!info) return fva_fail(FVA_EINVAL, "info is NULL");
   int rc = validate(desc, info);
   if (rc) return rc;
-  size_t offs[16], total;
+  size_t offs[17], total;
   layout_workspace(desc, *info, offs, &total);
   info->workspace_bytes = (int64_t)total;
   return FVA_OK;
@@ -269,7 +270,7 @@ extern "C" int fva_plan_create(fva_plan_t* out, const fva_plan_desc* desc, hipSt
   fva_plan_info in;
   int rc = validate(desc, &in);
   if (rc) return rc;
-  size_t offs[16], total;
+  size_t offs[17], total;
   layout_workspace(desc, in, offs, &total);
   in.workspace_bytes = (int64_t)total;
 
@@ -302,10 +303,10 @@ extern "C" int fva_plan_create(fva_plan_t* out, const fva_plan_desc* desc, hipSt
   p->blk_cnt = (int32_t*)(b + offs[2]);
   p->sub_pos = in.n_sub ? (uint8_t*)(b + offs[3]) : nullptr;
   p->sub_cnt = in.n_sub ? (int32_t*)(b + offs[4]) : nullptr;
-  p->qbar = (float*)(b + offs[5]);
-  p->kbar = (float*)(b + offs[6]);
-  p->zbuf = (float*)(b + offs[7]);
-  p->rowstat = (float2*)(b + offs[8]);
+  p->qbar = (double*)(b + offs[5]);
+  p->kbar = (double*)(b + offs[6]);
+  p->ybuf = (double*)(b + offs[7]);
+  p->rowstat = (double2*)(b + offs[8]);
   p->rowcnt = (int32_t*)(b + offs[9]);
   p->rowmask = (uint64_t*)(b + offs[10]);
   p->headcnt = (int32_t*)(b + offs[11]);
@@ -313,6 +314,7 @@ extern "C" int fva_plan_create(fva_plan_t* out, const fva_plan_desc* desc, hipSt
   p->slack_thr = (uint64_t*)(b + offs[13]);
   p->worklist = (int32_t*)(b + offs[14]);
   p->counters = (int32_t*)(b + offs[15]);
+  p->sbuf = (float*)(b + offs[16]);
 
   // Synchronous upload from pageable memory: the tables are small and this
   // happens once per plan, outside any timed path.

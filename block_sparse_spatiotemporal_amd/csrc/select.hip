@@ -1,7 +1,7 @@
 // Coarse stage and routing:
 //   pool   - "Video Sparse Attention" explainer, dialogue and section 3
 //            (pooled (4,4,4) tiles), "DFSAttn" explainer trick 2 (sub-blocks)
-//   score  - pooled q_bar . k_bar / sqrt(D), softmax over key blocks
+//   score  - pooled q_bar . k_bar / sqrt(D) in fp64, softmax over key blocks
 //   select - "FVAttn" review, sections 00 and 02: adaptive Top-p with a
 //            Top-k safety floor, emitted as CSR block lists
 //   slack  - "FVAttn" section 02 slack-aware augmentation, one-GPU reading:
@@ -14,7 +14,7 @@
 
 namespace {
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------------ helpers
 __device__ __forceinline__ float ld_elem(const uint16_t* p) {
@@ -68,204 +68,183 @@ __device__ __forceinline__ void wave_sync_lds() {
 
 // ------------------------------------------------------------------ pool
 // Mean of the 64 rows of one block (pads are zero rows, so the sum over all
-// rows is the sum over valid rows), divided by the valid count.  One wave per
-// (block, b*h, tensor); lanes own 16-byte column chunks of interleaved rows.
+// rows is the sum over valid rows), divided by the valid count, in fp64.
+// One wave per (block, b*h, tensor); lanes own 16-byte column chunks of
+// interleaved rows.
 template <typename T, int D>
 __global__ __launch_bounds__(64) void k_pool(const T* __restrict__ q, const T* __restrict__ k,
-                                             float* __restrict__ qbar, float* __restrict__ kbar,
+                                             double* __restrict__ qbar, double* __restrict__ kbar,
                                              const int32_t* __restrict__ blk_cnt, int n_blk, int64_t n_pad) {
   constexpr int EPC = 16 / sizeof(T);   // elements per 16-byte chunk
   constexpr int CPR = D / EPC;          // chunks per row
   constexpr int RG = 64 / CPR;          // row groups
-  __shared__ float part[RG][D];
+  __shared__ double part[RG][D];
   const int blk = blockIdx.x, bh = blockIdx.y;
   const T* src = (blockIdx.z == 0 ? q : k) + ((int64_t)bh * n_pad + (int64_t)blk * 64) * D;
-  float* dst = (blockIdx.z == 0 ? qbar : kbar) + ((int64_t)bh * n_blk + blk) * D;
+  double* dst = (blockIdx.z == 0 ? qbar : kbar) + ((int64_t)bh * n_blk + blk) * D;
   const int lane = threadIdx.x;
   const int ch = lane % CPR, g = lane / CPR;
-  float acc[EPC];
+  double acc[EPC];
 #pragma unroll
-  for (int e = 0; e < EPC; ++e) acc[e] = 0.0f;
+  for (int e = 0; e < EPC; ++e) acc[e] = 0.0;
   for (int r = g; r < 64; r += RG) {
     const T* row = src + (int64_t)r * D + ch * EPC;
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) acc[e] += ld_elem(row + e);
+    for (int e = 0; e < EPC; ++e) acc[e] += (double)ld_elem(row + e);
   }
 #pragma unroll
   for (int e = 0; e < EPC; ++e) part[g][ch * EPC + e] = acc[e];
   __syncthreads();
-  const float inv_n = 1.0f / (float)blk_cnt[blk];
+  const double cnt = (double)blk_cnt[blk];
   for (int d = lane; d < D; d += 64) {
-    float s = 0.0f;
+    double s = 0.0;
 #pragma unroll
     for (int gg = 0; gg < RG; ++gg) s += part[gg][d];
-    dst[d] = s * inv_n;
+    dst[d] = s / cnt;
   }
 }
 
-// Sub-block means of K ("DFSAttn" trick 2): kbar[(bh, blk, s), :] = mean of the
-// valid rows of sub-block s; an empty sub-block gets zeros (its logit is
-// masked by the score kernel through sub_cnt).
+// Sub-block means of K ("DFSAttn" trick 2), fp64: kbar[(bh, blk, s), :] =
+// mean of the valid rows of sub-block s; an empty sub-block gets zeros (its
+// logit is masked by the score kernel through sub_cnt).
 template <typename T, int D>
-__global__ __launch_bounds__(64) void k_pool_sub(const T* __restrict__ k, float* __restrict__ kbar,
+__global__ __launch_bounds__(64) void k_pool_sub(const T* __restrict__ k, double* __restrict__ kbar,
                                                  const uint8_t* __restrict__ sub_pos,
                                                  const int32_t* __restrict__ sub_cnt, int n_blk,
                                                  int64_t n_pad) {
   const int blk = blockIdx.x, bh = blockIdx.y;
   const T* src = k + ((int64_t)bh * n_pad + (int64_t)blk * 64) * D;
-  float* dst = kbar + ((int64_t)bh * n_blk + blk) * 8 * D;
+  double* dst = kbar + ((int64_t)bh * n_blk + blk) * 8 * D;
   for (int e = threadIdx.x; e < 8 * D; e += 64) {
     const int s = e / D, d = e - s * D;
     const uint8_t* pos = sub_pos + ((int64_t)blk * 8 + s) * 8;
-    float acc = 0.0f;
+    double acc = 0.0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc += ld_elem(src + (int64_t)pos[i] * D + d);
+    for (int i = 0; i < 8; ++i) acc += (double)ld_elem(src + (int64_t)pos[i] * D + d);
     const int c = sub_cnt[blk * 8 + s];
-    dst[e] = c ? acc / (float)c : 0.0f;
+    dst[e] = c ? acc / (double)c : 0.0;
   }
 }
 
 // ------------------------------------------------------------------ score
-// Block logits Y[bh, i, j] = q_bar_i . k_bar_j * scale (with sub-blocks: the
-// log-sum-exp over the non-empty sub-blocks of j), on fp32 matrix cores
-// (v_mfma_f32_32x32x2_f32), plus per-row (max, sum exp(y - max)).
-// Workgroup: 4 waves, 32 query rows of one (b, h); waves stride over 32-row
-// key tiles.  Z^T = Kbar * Qbar^T so that each lane owns one query row and
-// its key values sit in the lane's accumulators.
+// Block logits Y[bh, i, j] = q_bar_i . k_bar_j / sqrt(D) in fp64 (with
+// sub-blocks: the log-sum-exp over the non-empty sub-blocks of j, which makes
+// exp(Y) the sum of the sub-block terms), plus per-row (max, sum exp(y - max)).
+// fp64 matrix cores (v_mfma_f64_16x16x4_f64).  Workgroup = 4 waves, each
+// wave one 16-query tile; every wave sweeps all 16-key tiles, computing
+// Z^T = Kbar . Qbar^T so that lane l owns query l%16 and keys l/16 + 4*i.
+// fp64 keeps the logits exact to ~1e-15, so the fp32 scores the selection
+// reads carry only their final rounding.
 template <bool SUB, int D>
-__global__ __launch_bounds__(256) void k_score(const float* __restrict__ qbar, const float* __restrict__ kbar,
-                                               const int32_t* __restrict__ sub_cnt, float* __restrict__ z,
-                                               float2* __restrict__ rowstat, int n_blk, float scale) {
-  constexpr int HD = D / 2;
-  __shared__ float2 stat[4][64];
+__global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, const double* __restrict__ kbar,
+                                               const int32_t* __restrict__ sub_cnt, double* __restrict__ y,
+                                               double2* __restrict__ rowstat, int n_blk, double scale) {
+  constexpr int QD = D / 4;   // d values per lane group (k-steps of 4)
   const int bh = blockIdx.y;
-  const int i0 = blockIdx.x * 32;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int h = lane >> 5, l32 = lane & 31;
-  const int nkeys = SUB ? n_blk * 8 : n_blk;
-  const int ntiles = SUB ? (n_blk + 3) / 4 : (n_blk + 31) / 32;
-  const float* qb = qbar + (int64_t)bh * n_blk * D;
-  const float* kb = kbar + (int64_t)bh * nkeys * D;
-  const int qi = i0 + l32;
+  const int g = lane >> 4, l16 = lane & 15;
+  const int q0 = blockIdx.x * 64 + w * 16;
+  if (q0 >= n_blk) return;    // whole wave idle; no workgroup barrier below
+  const int qi = q0 + l16;
   const bool qvalid = qi < n_blk;
-  float qv[HD];
+  const int nkeys = SUB ? n_blk * 8 : n_blk;
+  const int ntiles = (nkeys + 15) / 16;
+  double qv[QD];
   {
-    const float4* src = (const float4*)(qb + (int64_t)min(qi, n_blk - 1) * D + h * HD);
+    const double2* src = (const double2*)(qbar + ((int64_t)bh * n_blk + min(qi, n_blk - 1)) * D + QD * g);
 #pragma unroll
-    for (int c = 0; c < HD / 4; ++c) {
-      const float4 t = src[c];
-      qv[4 * c] = t.x, qv[4 * c + 1] = t.y, qv[4 * c + 2] = t.z, qv[4 * c + 3] = t.w;
+    for (int c = 0; c < QD / 2; ++c) {
+      const double2 t = src[c];
+      qv[2 * c] = t.x, qv[2 * c + 1] = t.y;
     }
   }
-  float m_run = -INFINITY, s_run = 0.0f;
-  float* zrow = z + ((int64_t)bh * n_blk + min(qi, n_blk - 1)) * n_blk;
-  for (int kt = w; kt < ntiles; kt += 4) {
-    int krow;
-    bool kvalid;
-    if (!SUB) {
-      krow = kt * 32 + l32;
-      kvalid = krow < n_blk;
-    } else {
-      const int qq = l32 >> 3, hm = (l32 >> 2) & 1, ii = l32 & 3;
-      const int blk = kt * 4 + 2 * hm + (qq >> 1);
-      krow = blk * 8 + 4 * (qq & 1) + ii;
-      kvalid = blk < n_blk;
-    }
-    const float4* ks = (const float4*)(kb + (int64_t)(kvalid ? krow : 0) * D + h * HD);
-    f32x16 acc = {};
+  const double* kb = kbar + (int64_t)bh * nkeys * D + QD * g;
+  double* yrow = y + ((int64_t)bh * n_blk + min(qi, n_blk - 1)) * n_blk;
+  double m_run = -INFINITY, s_run = 0.0;
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int kidx = kt * 16 + l16;
+    const double2* ks = (const double2*)(kb + (int64_t)min(kidx, nkeys - 1) * D);
+    f64x4 acc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int c = 0; c < HD / 4; ++c) {
-      const float4 a = ks[c];
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, qv[4 * c + 0], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, qv[4 * c + 1], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, qv[4 * c + 2], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, qv[4 * c + 3], acc, 0, 0, 0);
+    for (int c = 0; c < QD / 2; ++c) {
+      const double2 a = ks[c];
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a.x, qv[2 * c], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a.y, qv[2 * c + 1], acc, 0, 0, 0);
     }
-    // accumulator r of this lane: key row m = 8*(r/4) + 4*h + r%4, query l32
+    // acc[i]: key kt*16 + g + 4*i, query l16 (fp64 16x16x4 accumulator layout)
     if (!SUB) {
-      float tmax = -INFINITY;
-      float y[16];
+      double yv[4];
+      double tmax = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = kt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        y[r] = j < n_blk ? acc[r] * scale : -INFINITY;
-        tmax = fmaxf(tmax, y[r]);
+      for (int i = 0; i < 4; ++i) {
+        const int j = kt * 16 + g + 4 * i;
+        yv[i] = j < n_blk ? acc[i] * scale : -INFINITY;
+        tmax = fmax(tmax, yv[i]);
       }
-      const float m_new = fmaxf(m_run, tmax);
+      const double m_new = fmax(m_run, tmax);
       if (m_new > -INFINITY) {
-        float add = 0.0f;
+        double add = 0.0;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) add += __expf(y[r] - m_new);
-        s_run = s_run * __expf(m_run - m_new) + add;
+        for (int i = 0; i < 4; ++i) add += exp(yv[i] - m_new);
+        s_run = s_run * exp(m_run - m_new) + add;
         m_run = m_new;
       }
       if (qvalid) {
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int j0 = kt * 32 + 8 * g4 + 4 * h;
-          if (j0 + 3 < n_blk) {
-            *(float4*)(zrow + j0) = make_float4(y[4 * g4], y[4 * g4 + 1], y[4 * g4 + 2], y[4 * g4 + 3]);
-          } else {
-            for (int e = 0; e < 4; ++e)
-              if (j0 + e < n_blk) zrow[j0 + e] = y[4 * g4 + e];
-          }
+        for (int i = 0; i < 4; ++i) {
+          const int j = kt * 16 + g + 4 * i;
+          if (j < n_blk) yrow[j] = yv[i];
         }
       }
     } else {
-      float yb[2];
+      // sub-key m = g + 4*i of the tile is sub-block m%8 of block kt*2 + m/8:
+      // acc[2*b2] and acc[2*b2+1] are sub-blocks g and g+4 of block kt*2+b2.
+      double yb[2];
 #pragma unroll
       for (int b2 = 0; b2 < 2; ++b2) {
-        const int blk = kt * 4 + 2 * h + b2;
-        float v[8];
-        float c = -INFINITY;
+        const int blk = kt * 2 + b2;
+        const int bc = min(blk, n_blk - 1) * 8;
+        const double v0 = (blk < n_blk && sub_cnt[bc + g] > 0) ? acc[2 * b2] * scale : -INFINITY;
+        const double v1 = (blk < n_blk && sub_cnt[bc + g + 4] > 0) ? acc[2 * b2 + 1] * scale : -INFINITY;
+        double c = fmax(v0, v1);
+        double e = c > -INFINITY ? exp(v0 - c) + exp(v1 - c) : 0.0;
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const bool ok = blk < n_blk && sub_cnt[(blk < n_blk ? blk : 0) * 8 + s] > 0;
-          v[s] = ok ? acc[8 * b2 + s] * scale : -INFINITY;
-          c = fmaxf(c, v[s]);
+        for (int o = 16; o <= 32; o <<= 1) {
+          const double c2 = __shfl_xor(c, o), e2 = __shfl_xor(e, o);
+          const double cc = fmax(c, c2);
+          e = (c > -INFINITY ? e * exp(c - cc) : 0.0) + (c2 > -INFINITY ? e2 * exp(c2 - cc) : 0.0);
+          c = cc;
         }
-        float e = 0.0f;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) e += __expf(v[s] - c);
-        yb[b2] = (blk < n_blk) ? c + __logf(e) : -INFINITY;
+        yb[b2] = c > -INFINITY ? c + log(e) : -INFINITY;
       }
-      const float tmax = fmaxf(yb[0], yb[1]);
-      const float m_new = fmaxf(m_run, tmax);
+      // every lane group now holds both block logits; group 0 counts and writes them
+      const double y0 = g == 0 ? yb[0] : -INFINITY, y1 = g == 0 ? yb[1] : -INFINITY;
+      const double m_new = fmax(m_run, fmax(y0, y1));
       if (m_new > -INFINITY) {
-        s_run = s_run * __expf(m_run - m_new) + __expf(yb[0] - m_new) + __expf(yb[1] - m_new);
+        s_run = s_run * exp(m_run - m_new) + exp(y0 - m_new) + exp(y1 - m_new);
         m_run = m_new;
       }
-      if (qvalid) {
-        const int j0 = kt * 4 + 2 * h;
-        if (j0 + 1 < n_blk) *(float2*)(zrow + j0) = make_float2(yb[0], yb[1]);
-        else if (j0 < n_blk) zrow[j0] = yb[0];
+      if (qvalid && g == 0) {
+        if (kt * 2 < n_blk) yrow[kt * 2] = yb[0];
+        if (kt * 2 + 1 < n_blk) yrow[kt * 2 + 1] = yb[1];
       }
     }
   }
-  // merge (max, sum) over the two lane halves, then over the four waves
-  {
-    const float mo = __shfl_xor(m_run, 32), so = __shfl_xor(s_run, 32);
-    const float mm = fmaxf(m_run, mo);
-    const float ss = (m_run > -INFINITY ? s_run * __expf(m_run - mm) : 0.0f) +
-                     (mo > -INFINITY ? so * __expf(mo - mm) : 0.0f);
-    stat[w][lane] = make_float2(mm, ss);
+  // merge (max, sum) over the four lane groups that share query l16
+#pragma unroll
+  for (int o = 16; o <= 32; o <<= 1) {
+    const double mo = __shfl_xor(m_run, o), so = __shfl_xor(s_run, o);
+    const double mm = fmax(m_run, mo);
+    s_run = (m_run > -INFINITY ? s_run * exp(m_run - mm) : 0.0) + (mo > -INFINITY ? so * exp(mo - mm) : 0.0);
+    m_run = mm;
   }
-  __syncthreads();
-  if (w == 0 && lane < 32 && qvalid) {
-    float mm = -INFINITY;
-    for (int ww = 0; ww < 4; ++ww) mm = fmaxf(mm, stat[ww][lane].x);
-    float ss = 0.0f;
-    for (int ww = 0; ww < 4; ++ww) {
-      const float2 t = stat[ww][lane];
-      if (t.x > -INFINITY) ss += t.y * __expf(t.x - mm);
-    }
-    rowstat[(int64_t)bh * n_blk + qi] = make_float2(mm, ss);
-  }
+  if (g == 0 && qvalid) rowstat[(int64_t)bh * n_blk + qi] = make_double2(m_run, s_run);
 }
 
 // ------------------------------------------------------------------ select
-// One wave per row (b, h, I).  Scores are either recomputed from the block
-// logits (S = exp(y - max) / sum, fp32) or read from scores_in.  The kept set
+// One wave per row (b, h, I).  Scores are either computed from the fp64
+// block logits (S = exp(y - max) / sum in fp64, rounded once to fp32) or
+// read from scores_in.  The kept set
 // is the shortest prefix in (score desc, id asc) order whose fixed-point
 // mass reaches p, extended to the floor min(k_min, n).  It is found by an
 // MSD radix select over the 48-bit key (score bits << 16 | (0xFFFF - J)):
@@ -275,7 +254,7 @@ __global__ __launch_bounds__(256) void k_score(const float* __restrict__ qbar, c
 // exact cut is read off a prefix sum.  Output: a bitmask of kept ids per row
 // and the kept count.
 template <int NI>
-__global__ __launch_bounds__(256) void k_select(const float* __restrict__ z, const float2* __restrict__ rowstat,
+__global__ __launch_bounds__(256) void k_select(const double* __restrict__ z, const double2* __restrict__ rowstat,
                                                 const float* __restrict__ scores_in, float* __restrict__ s_out,
                                                 SelectArgs pa, int p_count, int k_min, int n_blk,
                                                 int64_t n_rows, int32_t* __restrict__ rowcnt,
@@ -292,12 +271,12 @@ __global__ __launch_bounds__(256) void k_select(const float* __restrict__ z, con
 
   uint32_t bits[NI];
   {
-    float m = 0.0f, sum = 1.0f;
+    double m = 0.0, sum = 1.0;
     if (!scores_in) {
-      const float2 st = rowstat[r];
+      const double2 st = rowstat[r];
       m = st.x, sum = st.y;
     }
-    const float* zr = z + r * n;
+    const double* zr = z + r * n;
     const float* sr = scores_in ? scores_in + r * n : nullptr;
     float* so = s_out ? s_out + r * n : nullptr;
 #pragma unroll
@@ -305,7 +284,7 @@ __global__ __launch_bounds__(256) void k_select(const float* __restrict__ z, con
       const int j = lane + 64 * i;
       bits[i] = 0;
       if (j < n) {
-        const float s = sr ? sr[j] : expf(zr[j] - m) / sum;
+        const float s = sr ? sr[j] : (float)(exp(zr[j] - m) / sum);
         if (so) so[j] = s;
         bits[i] = clamp_bits(s);
       }
@@ -630,14 +609,14 @@ template <int D>
 void launch_score(fva_plan_t plan, hipStream_t s) {
   const fva_plan_info& in = plan->info;
   const int bh = plan->desc.batch * plan->desc.heads;
-  dim3 grid((in.n_blk + 31) / 32, bh);
-  const float scale = 1.0f / sqrtf((float)D);
+  dim3 grid((in.n_blk + 63) / 64, bh);
+  const double scale = 1.0 / sqrt((double)D);
   if (in.n_sub)
     hipLaunchKernelGGL((k_score<true, D>), grid, dim3(256), 0, s, plan->qbar, plan->kbar, plan->sub_cnt,
-                       plan->zbuf, plan->rowstat, in.n_blk, scale);
+                       plan->ybuf, plan->rowstat, in.n_blk, scale);
   else
     hipLaunchKernelGGL((k_score<false, D>), grid, dim3(256), 0, s, plan->qbar, plan->kbar, plan->sub_cnt,
-                       plan->zbuf, plan->rowstat, in.n_blk, scale);
+                       plan->ybuf, plan->rowstat, in.n_blk, scale);
 }
 
 }  // namespace
@@ -679,12 +658,12 @@ extern "C" int fva_select(fva_plan_t plan, const void* q_perm, const void* k_per
     if (d.head_dim == 128) launch_score<128>(plan, stream);
     else launch_score<64>(plan, stream);
   }
-  float* s_out = scores_out ? scores_out : (scores_in ? nullptr : plan->zbuf);
+  float* s_out = scores_out ? scores_out : (scores_in ? nullptr : plan->sbuf);
   const float* s_read = scores_in ? scores_in : s_out;
   const unsigned sel_grid = (unsigned)((in.n_rows + 3) / 4);
   const int ni = (in.n_blk + 63) / 64;
 #define FVA_SELECT(NI)                                                                                  \
-  hipLaunchKernelGGL((k_select<NI>), dim3(sel_grid), dim3(256), 0, stream, plan->zbuf, plan->rowstat,  \
+  hipLaunchKernelGGL((k_select<NI>), dim3(sel_grid), dim3(256), 0, stream, plan->ybuf, plan->rowstat,  \
                      scores_in, s_out, pa, p_count, k_min, in.n_blk, in.n_rows, plan->rowcnt,           \
                      plan->rowmask, plan->nw)
   if (ni <= 4) FVA_SELECT(4);

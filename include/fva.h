@@ -152,10 +152,11 @@ int fva_permute(fva_plan_t plan, const void* x_raster, void* x_perm, int32_t lay
 /* Coarse stage and routing ("Video Sparse Attention" dialogue and section 3;
  * "FVAttn" sections 00 and 02; "DFSAttn" trick 2):
  *   pool   q_bar_I = mean of the valid rows of Q block I (k_bar likewise; with
- *          sub-blocks on, one k_bar per non-empty (J, s) pair), fp32;
- *   score  S_I. = softmax_J(q_bar_I . k_bar_J / sqrt(D)) in fp32; with
- *          sub-blocks, the softmax runs over all non-empty (J, s) and S_IJ is
- *          the sum over s (computed as a log-sum-exp block logit);
+ *          sub-blocks on, one k_bar per non-empty (J, s) pair), fp64;
+ *   score  S_I. = softmax_J(q_bar_I . k_bar_J / sqrt(D)) computed in fp64
+ *          and rounded once to fp32; with sub-blocks, the softmax runs over
+ *          all non-empty (J, s) and S_IJ is the sum over s (computed as a
+ *          log-sum-exp block logit);
  *   select per row, order J by (S desc, J asc) and keep the shortest prefix
  *          whose mass reaches p, then at least min(k_min, n_blk) blocks;
  *          p >= 1 keeps all blocks.  The mass is the exact integer sum of

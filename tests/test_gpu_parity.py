@@ -78,7 +78,8 @@ def test_scores_match_oracle(w):
     else:
         ref = O.score(qb, O.pool(kp, opl))
     got = S.cpu().numpy().astype(np.float64)
-    assert np.max(np.abs(got - ref)) < 1e-6
+    # fp64 logits, one fp32 rounding at the end: |dS| <= 2^-24 S
+    assert np.all(np.abs(got - ref) <= 1e-7 * ref + 1e-38), np.max(np.abs(got - ref) / (ref + 1e-38))
     assert np.allclose(got.sum(-1), 1.0, atol=1e-5)
 
 
