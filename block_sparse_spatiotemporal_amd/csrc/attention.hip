@@ -8,6 +8,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 
 #include "fva_internal.h"
 
@@ -35,48 +36,154 @@ struct AttnArgs {
   int n_items;
   int n_blk;
   int persistent;
+  int chunk;                // work-list chunk dealt to one XCD at a time
   float scale;              // 1/sqrt(D)
 };
 
+constexpr int kXcds = 8;    // MI355X: 8 XCDs, workgroups dealt round-robin
+
+// Work-list position of the k-th row an XCD takes: the list is cut into
+// chunks of `chunk` rows dealt round-robin to the XCDs, so the workgroups of
+// one XCD (one L2) walk contiguous query blocks of the same head.
+__device__ __forceinline__ int64_t xcd_item(int x, int64_t k, int chunk) {
+  return ((k / chunk) * kXcds + x) * chunk + k % chunk;
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// Next row for this workgroup: from the atomic cursor (persistent) or the
-// workgroup index (plain).  Returns -1 when the work list is exhausted.
+// Next row for this workgroup, or -1 when the work list is exhausted.
+// Plain: workgroup b is on XCD b % 8 and takes its XCD's (b / 8)-th row.
+// Persistent: one cursor per XCD; an XCD whose share is done steals from
+// the others, so every workgroup leaves only when all rows are taken.
 __device__ __forceinline__ int next_item(const AttnArgs& a, int* s_item, bool first) {
-  if (!a.persistent) return first ? (int)blockIdx.x : -1;
+  if (!a.persistent) {
+    if (!first) return -1;
+    const int64_t it = xcd_item(blockIdx.x % kXcds, blockIdx.x / kXcds, a.chunk);
+    return it < a.n_items ? (int)it : -1;
+  }
   __syncthreads();
-  if (threadIdx.x == 0) *s_item = atomicAdd(a.cursor, 1);
+  if (threadIdx.x == 0) {
+    const int x0 = blockIdx.x % kXcds;
+    int found = -1;
+    for (int t = 0; t < kXcds && found < 0; ++t) {
+      const int x = (x0 + t) % kXcds;
+      if (__hip_atomic_load(&a.cursor[kXcds + x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) continue;
+      const int64_t it = xcd_item(x, atomicAdd(&a.cursor[x], 1), a.chunk);
+      if (it < a.n_items) found = (int)it;
+      else __hip_atomic_store(&a.cursor[kXcds + x], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    *s_item = found;
+  }
   __syncthreads();
-  const int it = *s_item;
-  return it < a.n_items ? it : -1;
+  return *s_item;
 }
 
 // ------------------------------------------------------------------ bf16
 // Workgroup = 2 waves = one 64-query block; wave w owns queries 32w..32w+31.
-// Per 32-key half of a selected block:
+// A step is one 32-key half of a selected block:
 //   S^T (32 keys x 32 queries) = K_half . Q^T     (D/16 MFMA 32x32x16 bf16)
 //   online softmax in fp32 on the accumulators (each lane owns one query)
 //   O^T (D x 32 queries) += V^T_half . P^T        (D/32 x 2 MFMA)
 // P^T feeds the second product straight from the accumulators (the VT key
-// slot order makes that consistent).  K and V^T halves are staged through
-// LDS with an XOR swizzle so the 16-byte operand reads are conflict free.
-template <int D>
+// slot order makes that consistent).  K and V^T halves stream from HBM into
+// an NST-stage LDS ring with direct global->LDS loads (no register staging);
+// each wave issues half of a stage's 1 KB loads, waits on its own vector
+// memory counter, and one barrier per step publishes the stage to both waves
+// and retires the stage the next load overwrites.  The LDS image of each
+// stage is XOR-swizzled so the 16-byte operand reads are conflict free: the
+// swizzle is applied by choosing each lane's source address, since a direct
+// load writes lane i's 16 bytes at offset 16*i of its 1 KB destination.
+// The running max is raised lazily: P may grow to 2^kLazy before O and l are
+// rescaled, which skips most rescales once the row maximum is found.
+
+__device__ __forceinline__ void dma16(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+
+// s_waitcnt with only the vector-memory count limited to n (other counters
+// left free).  gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] |
+// vmcnt_hi[15:14].
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier without the memory fence __syncthreads() implies: the
+// fence would drain every outstanding vector load, including the direct
+// loads of the steps still in flight.  The empty asm statements keep the
+// compiler from moving LDS accesses across the barrier.
+__device__ __forceinline__ void barrier_no_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Wave-uniform reads of read-only metadata through the scalar cache.
+template <typename T>
+__device__ __forceinline__ T sload(const T* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) T*)p)[i];
+}
+
+template <int D, int NST>
 __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnArgs a) {
-  constexpr int KS = D / 16;   // k-steps of S^T
-  constexpr int DT = D / 32;   // d tiles of O^T
-  constexpr int KCH = D / 8;   // 16-byte chunks per K row
-  __shared__ uint4 k_lds[32 * KCH];
-  __shared__ uint4 v_lds[D * 4];
+  constexpr int KS = D / 16;            // k-steps of S^T
+  constexpr int DT = D / 32;            // d tiles of O^T
+  constexpr int KCH = D / 8;            // 16-byte chunks per K row
+  constexpr int HALF = 32 * D * 2;      // bytes of one K half (and of one V^T half)
+  constexpr int STAGE = 2 * HALF;
+  constexpr int NI = HALF / 1024;       // 1 KB direct loads per half per workgroup
+  constexpr int PW = NI;                // loads per wave per step (NI for K + NI for V, split over 2 waves)
+  constexpr float kLazy = 8.0f;
+  static_assert(NI % 2 == 0, "loads split evenly over the two waves");
+  __shared__ __attribute__((aligned(1024))) uint4 ring[NST * STAGE / 16];
   __shared__ int s_item;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
   const uint64_t t0 = wall_clock64();
   const float sl2 = a.scale * 1.44269504088896340736f;   // scores in log2 units
+  // Source offset (bytes, within a K half / V^T half) of this lane's 16 bytes
+  // for each of the wave's direct loads.  Load i writes LDS bytes
+  // [1024 i, 1024 i + 1024) of the half; lane L lands at 1024 i + 16 L.
+  // K rows are D*2 bytes: physical chunk pc of row r holds logical chunk
+  // pc ^ (r & 7).  V^T rows are 64 bytes: physical chunk pc of row d holds
+  // logical chunk pc ^ ((d >> 1) & 3).
+  uint32_t koff[NI / 2], voff[NI / 2];
+#pragma unroll
+  for (int j = 0; j < NI / 2; ++j) {
+    const int off = (2 * j + w) * 1024 + lane * 16;
+    const int row = off / (KCH * 16), pc = (off / 16) % KCH;
+    koff[j] = row * (D * 2) + ((pc ^ (row & 7)) * 16);
+    const int d = off / 64, pv = (off / 16) & 3;
+    voff[j] = d * 64 + ((pv ^ ((d >> 1) & 3)) * 16);
+  }
   for (int item = next_item(a, &s_item, true); item >= 0; item = next_item(a, &s_item, false)) {
-    const int r = a.worklist[item];
+    const int r = sload(a.worklist, __builtin_amdgcn_readfirstlane(item));
     const int bh = r / a.n_blk;
     const int I = r - bh * a.n_blk;
     const int64_t head = (int64_t)bh * a.n_pad;
+    const int e0 = sload(a.row_ptr, r);
+    const int e1 = sload(a.row_ptr, r + 1);
+    const int nsteps = 2 * (e1 - e0);
+    const char* kbase = (const char*)(a.k + head * D);
+    const char* vbase = (const char*)(a.vt + head * D);
+
+    // Issue the direct loads of step `st` (block e0 + st/2, half st%2) into its stage.
+    auto issue = [&](int st) {
+      int J = sload(a.col_idx, e0 + (st >> 1));
+      if ((unsigned)J >= (unsigned)a.n_blk) J = 0;   // ids outside the plan: load block 0, masked below
+      const int u = st & 1;
+      const char* ksrc = kbase + ((int64_t)J * 64 + 32 * u) * D * 2;
+      const char* vsrc = vbase + (int64_t)J * 64 * D * 2 + u * HALF;
+      char* dst = (char*)ring + (st % NST) * STAGE;
+#pragma unroll
+      for (int j = 0; j < NI / 2; ++j) {
+        const int i = 2 * j + w;                     // this wave's share of the 1 KB loads
+        dma16(ksrc + koff[j], dst + i * 1024);
+        dma16(vsrc + voff[j], dst + HALF + i * 1024);
+      }
+    };
+
     bf16x8 qreg[KS];
     {
       const uint4* qrow = (const uint4*)(a.q + (head + (int64_t)I * 64 + 32 * w + l32) * D);
@@ -87,80 +194,88 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnArgs a) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
     float m_run = -INFINITY, l_run = 0.0f;
-    const int e0 = a.row_ptr[r], e1 = a.row_ptr[r + 1];
-    for (int e = e0; e < e1; ++e) {
-      const int J = a.col_idx[e];
-      if ((unsigned)J >= (unsigned)a.n_blk) continue;   // ids outside the plan are skipped
-      const uint64_t mJ = a.blk_mask[J];
-      const uint16_t* kblk = a.k + (head + (int64_t)J * 64) * D;
-      const uint16_t* vblk = a.vt + (head + (int64_t)J * 64) * D;
+
+    // prologue: NST-1 steps in flight
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const uint32_t mh = (uint32_t)(mJ >> (32 * u));
-        if (mh == 0) continue;   // half holds only pad keys (uniform over the workgroup)
-        __syncthreads();
-        for (int c = tid; c < 32 * KCH; c += 128) {
-          const int row = c / KCH, ch = c % KCH;
-          k_lds[row * KCH + (ch ^ (row & 7))] = *(const uint4*)(kblk + (32 * u + row) * D + ch * 8);
-        }
-        for (int c = tid; c < D * 4; c += 128) {
-          const int d = c >> 2, ch = c & 3;
-          v_lds[d * 4 + (ch ^ ((d >> 1) & 3))] = *(const uint4*)(vblk + u * 32 * D + d * 32 + ch * 8);
-        }
-        __syncthreads();
-        f32x16 s = {};
+    for (int st = 0; st < NST - 1; ++st)
+      if (st < nsteps) issue(st);
+
+    for (int st = 0; st < nsteps; ++st) {
+      // wait for this wave's loads of step st; later steps may stay in flight
+      const int ahead = min(nsteps - 1 - st, NST - 2);
+      if (ahead >= 2) wait_vm<2 * PW>();
+      else if (ahead == 1) wait_vm<PW>();
+      else wait_vm<0>();
+      barrier_no_fence();
+      if (st + NST - 1 < nsteps) issue(st + NST - 1);   // into the stage retired by the barrier
+
+      const int J = sload(a.col_idx, e0 + (st >> 1));
+      const int u = st & 1;
+      uint32_t mh = 0;
+      if ((unsigned)J < (unsigned)a.n_blk) mh = (uint32_t)(sload(a.blk_mask, J) >> (32 * u));
+      if (mh == 0) continue;   // half of pad keys only (uniform over the workgroup)
+      const uint4* kst = ring + (st % NST) * (STAGE / 16);
+      const uint4* vst = kst + HALF / 16;
+
+      f32x16 s = {};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k_lds[l32 * KCH + ((2 * ks + h) ^ (l32 & 7))]),
-                                                      qreg[ks], s, 0, 0, 0);
-        // s[i]: key 8*(i/4) + 4*h + i%4 of this half, query l32
-        float t[16];
-        float mx = -INFINITY;
+      for (int ks = 0; ks < KS; ++ks)
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kst[l32 * KCH + ((2 * ks + h) ^ (l32 & 7))]),
+                                                    qreg[ks], s, 0, 0, 0);
+      // s[i]: key 8*(i/4) + 4*h + i%4 of this half, query l32.  Pad keys get
+      // -inf; the scale (1/sqrt(D) in log2 units, > 0) is applied after the max.
+      if (mh != 0xFFFFFFFFu) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = 8 * (i >> 2) + 4 * h + (i & 3);
-          t[i] = (mh >> key & 1) ? s[i] * sl2 : -INFINITY;
-          mx = fmaxf(mx, t[i]);
+          if (!(mh >> key & 1)) s[i] = -INFINITY;
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+      }
+      float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
+#pragma unroll
+      for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s[i]), s[i + 1]);
+      mx = fmaxf(mx, s[15]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+      if (__ballot(mx > m_run + kLazy)) {   // raise the running max (first step always)
         const float m_new = fmaxf(m_run, mx);
-        const float alpha = exp2f(m_run - m_new);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
         m_run = m_new;
-        f32x8 p0, p1;
+      }
+      const float nm = -m_run;
+      f32x8 p0, p1;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          p0[i] = exp2f(t[i] - m_new);
-          p1[i] = exp2f(t[8 + i] - m_new);
-          l_run += p0[i] + p1[i];
-        }
-        const bf16x8 pb0 = __builtin_convertvector(p0, bf16x8);
-        const bf16x8 pb1 = __builtin_convertvector(p1, bf16x8);
+      for (int i = 0; i < 8; ++i) {
+        p0[i] = __builtin_amdgcn_exp2f(fmaf(s[i], sl2, nm));
+        p1[i] = __builtin_amdgcn_exp2f(fmaf(s[8 + i], sl2, nm));
+      }
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const int d = 32 * dt + l32;
-          const int sw = (d >> 1) & 3;
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(v_lds[d * 4 + ((0 + h) ^ sw)]), pb0, o[dt], 0, 0, 0);
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(v_lds[d * 4 + ((2 + h) ^ sw)]), pb1, o[dt], 0, 0, 0);
-        }
+      for (int i = 0; i < 8; ++i) l_run += p0[i] + p1[i];
+      const bf16x8 pb0 = __builtin_convertvector(p0, bf16x8);
+      const bf16x8 pb1 = __builtin_convertvector(p1, bf16x8);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int d = 32 * dt + l32;
+        const int sw = (d >> 1) & 3;
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vst[d * 4 + ((0 + h) ^ sw)]), pb0, o[dt], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vst[d * 4 + ((2 + h) ^ sw)]), pb1, o[dt], 0, 0, 0);
       }
     }
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    const bool qvalid = a.blk_mask[I] >> (32 * w + l32) & 1;
+    const bool qvalid = sload(a.blk_mask, I) >> (32 * w + l32) & 1;
     uint16_t* orow = (uint16_t*)a.o + (head + (int64_t)I * 64 + 32 * w + l32) * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        float4 v = make_float4(o[dt][4 * g4] * inv, o[dt][4 * g4 + 1] * inv, o[dt][4 * g4 + 2] * inv,
-                               o[dt][4 * g4 + 3] * inv);
-        if (!qvalid) v = make_float4(0.f, 0.f, 0.f, 0.f);
         typedef float f32x4 __attribute__((ext_vector_type(4)));
         typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-        const bf16x4 b = __builtin_convertvector((f32x4{v.x, v.y, v.z, v.w}), bf16x4);
+        f32x4 v = {o[dt][4 * g4] * inv, o[dt][4 * g4 + 1] * inv, o[dt][4 * g4 + 2] * inv, o[dt][4 * g4 + 3] * inv};
+        if (!qvalid) v = f32x4{0.f, 0.f, 0.f, 0.f};
+        const bf16x4 b = __builtin_convertvector(v, bf16x4);
         *(uint2*)(orow + 32 * dt + 8 * g4 + 4 * h) = __builtin_bit_cast(uint2, b);
       }
     }
@@ -257,46 +372,56 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------ schedule
-// Counting sort of rows by cost (kept blocks), longest first, into the work
-// list; resets the work-queue cursor.  One workgroup.
-__global__ __launch_bounds__(1024) void k_sched(const int32_t* __restrict__ row_ptr, int64_t n_rows, int n_blk,
+// Work list for the attention grid: heads in decreasing total cost (kept
+// blocks, so the cheapest rows run last and the tail is short), each head's
+// query blocks in id order (neighbouring query blocks keep overlapping key
+// blocks, which the XCD dealing turns into L2 hits).  Also clears the
+// per-XCD cursors and exhaustion flags.  One workgroup.
+__global__ __launch_bounds__(1024) void k_sched(const int32_t* __restrict__ row_ptr, int n_blk, int n_bh,
                                                 int32_t* __restrict__ worklist, int32_t* __restrict__ cursor) {
-  __shared__ int hist[FVA_MAX_NBLK + 1];
-  __shared__ int part[1024];
+  __shared__ int cost[FVA_MAX_SCHED_HEADS];
+  __shared__ int rank[FVA_MAX_SCHED_HEADS];
   const int tid = threadIdx.x;
-  const int nb = n_blk + 1;
-  for (int i = tid; i < nb; i += 1024) hist[i] = 0;
+  for (int bh = tid; bh < n_bh; bh += 1024)
+    cost[bh] = row_ptr[(int64_t)(bh + 1) * n_blk] - row_ptr[(int64_t)bh * n_blk];
+  if (tid < 2 * kXcds) cursor[tid] = 0;
   __syncthreads();
+  for (int bh = tid; bh < n_bh; bh += 1024) {
+    int rk = 0;
+    const int c = cost[bh];
+    for (int o = 0; o < n_bh; ++o) rk += (cost[o] > c) || (cost[o] == c && o < bh);
+    rank[bh] = rk;
+  }
+  __syncthreads();
+  const int64_t n_rows = (int64_t)n_bh * n_blk;
   for (int64_t r = tid; r < n_rows; r += 1024) {
-    const int c = min(max(row_ptr[r + 1] - row_ptr[r], 0), n_blk);
-    atomicAdd(&hist[n_blk - c], 1);   // bin 0 = most expensive
+    const int bh = (int)(r / n_blk);
+    const int I = (int)(r - (int64_t)bh * n_blk);
+    worklist[(int64_t)rank[bh] * n_blk + I] = (int32_t)r;
   }
-  __syncthreads();
-  const int per = (nb + 1023) / 1024;
-  const int b0 = min(tid * per, nb), b1 = min(b0 + per, nb);
-  int s = 0;
-  for (int i = b0; i < b1; ++i) s += hist[i];
-  part[tid] = s;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    const int v = tid >= o ? part[tid - o] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
+}
+
+// LDS ring depth of the bf16 attention kernel (stages of 2*32*D*2 bytes);
+// FVA_ATTN_STAGES=2|3|4 overrides it for tuning.
+// Rows per XCD chunk of the work list; FVA_ATTN_CHUNK overrides it.
+int attn_chunk() {
+  static int n = -1;
+  if (n < 0) {
+    const char* v = getenv("FVA_ATTN_CHUNK");
+    n = v ? atoi(v) : 32;
+    if (n < 1 || n > 4096) n = 32;
   }
-  int run = part[tid] - s;
-  for (int i = b0; i < b1; ++i) {
-    const int c = hist[i];
-    hist[i] = run;
-    run += c;
+  return n;
+}
+
+int attn_stages() {
+  static int n = -1;
+  if (n < 0) {
+    const char* v = getenv("FVA_ATTN_STAGES");
+    n = v ? atoi(v) : 3;
+    if (n < 2 || n > 4) n = 3;
   }
-  __syncthreads();
-  for (int64_t r = tid; r < n_rows; r += 1024) {
-    const int c = min(max(row_ptr[r + 1] - row_ptr[r], 0), n_blk);
-    const int pos = atomicAdd(&hist[n_blk - c], 1);
-    worklist[pos] = (int32_t)r;
-  }
-  if (tid == 0) *cursor = 0;
+  return n;
 }
 
 template <typename K>
@@ -318,7 +443,8 @@ extern "C" int fva_attention(fva_plan_t plan, const void* q_perm, const void* k_
     return fva_fail(FVA_EINVAL, "unknown sched_mode %d", sched_mode);
   const fva_plan_desc& d = plan->desc;
   const fva_plan_info& in = plan->info;
-  hipLaunchKernelGGL(k_sched, dim3(1), dim3(1024), 0, stream, row_ptr, in.n_rows, in.n_blk, plan->worklist,
+  const int n_bh = d.batch * d.heads;
+  hipLaunchKernelGGL(k_sched, dim3(1), dim3(1024), 0, stream, row_ptr, in.n_blk, n_bh, plan->worklist,
                      plan->counters);
   AttnArgs a{};
   a.q = (const uint16_t*)q_perm;
@@ -338,19 +464,29 @@ extern "C" int fva_attention(fva_plan_t plan, const void* q_perm, const void* k_
   a.n_items = (int)in.n_rows;
   a.n_blk = in.n_blk;
   a.persistent = sched_mode == FVA_SCHED_PERSISTENT;
+  a.chunk = attn_chunk();
   a.scale = 1.0f / sqrtf((float)d.head_dim);
 
 #define FVA_LAUNCH(KERNEL, THREADS)                                                              \
   do {                                                                                           \
-    int grid = (int)in.n_rows;                                                                   \
+    const int deal = kXcds * a.chunk;                                                            \
+    int grid = (int)((in.n_rows + deal - 1) / deal * deal);                                      \
     if (a.persistent)                                                                            \
       grid = (int)std::min<int64_t>(std::min<int64_t>(in.n_rows, in.max_wg),                     \
                                     (int64_t)plan->num_cu * occupancy(KERNEL, THREADS));         \
     hipLaunchKernelGGL(KERNEL, dim3(grid), dim3(THREADS), 0, stream, a);                        \
   } while (0)
   if (d.dtype == FVA_DTYPE_BF16) {
-    if (d.head_dim == 128) FVA_LAUNCH(k_attn_bf16<128>, 128);
-    else FVA_LAUNCH(k_attn_bf16<64>, 128);
+    const int ns = attn_stages();
+    if (d.head_dim == 128) {
+      if (ns == 2) FVA_LAUNCH((k_attn_bf16<128, 2>), 128);
+      else if (ns == 3) FVA_LAUNCH((k_attn_bf16<128, 3>), 128);
+      else FVA_LAUNCH((k_attn_bf16<128, 4>), 128);
+    } else {
+      if (ns == 2) FVA_LAUNCH((k_attn_bf16<64, 2>), 128);
+      else if (ns == 3) FVA_LAUNCH((k_attn_bf16<64, 3>), 128);
+      else FVA_LAUNCH((k_attn_bf16<64, 4>), 128);
+    }
   } else {
     if (d.head_dim == 128) FVA_LAUNCH(k_attn_f32<128>, 256);
     else FVA_LAUNCH(k_attn_f32<64>, 256);

@@ -11,6 +11,7 @@
 #define FVA_BLK 64        // tokens per block (tile volume)
 #define FVA_MAX_PHEAD 512 // per-head p values passed by value to the kernels
 #define FVA_MAX_NBLK 4096 // blocks per head the selection kernels support
+#define FVA_MAX_SCHED_HEADS 4096  // B*H the attention scheduler supports
 
 struct fva_plan_s {
   fva_plan_desc desc;

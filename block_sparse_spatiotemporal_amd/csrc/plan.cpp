@@ -131,7 +131,10 @@ static int validate(const fva_plan_desc* d, fva_plan_info* info) {
     return fva_fail(FVA_EUNSUPPORTED, "B*H*n_blk^2 = %lld exceeds int32 block lists", (long long)in.max_nnz);
   if ((int64_t)d->batch * d->heads * in.n_pad * d->head_dim >= (int64_t(1) << 40))
     return fva_fail(FVA_EUNSUPPORTED, "tensor too large");
-  in.max_wg = (int32_t)std::max<int64_t>(in.n_rows, 4096);
+  if ((int64_t)d->batch * d->heads > FVA_MAX_SCHED_HEADS)
+    return fva_fail(FVA_EUNSUPPORTED, "B*H = %lld exceeds %d", (long long)d->batch * d->heads, FVA_MAX_SCHED_HEADS);
+  // plain launches round the grid up to a multiple of 8 XCDs x 4096-row chunks at most
+  in.max_wg = (int32_t)(std::max<int64_t>(in.n_rows, 4096) + 8 * 4096);
   if (info) *info = in;
   return FVA_OK;
 }
