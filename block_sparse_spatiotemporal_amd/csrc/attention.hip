@@ -125,68 +125,128 @@ __device__ __forceinline__ T sload(const T* p, int64_t i) {
   return ((const __attribute__((address_space(4))) T*)p)[i];
 }
 
-template <int D, int NST>
-__global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnArgs a) {
+// XOR swizzles of the LDS images (16-byte chunk index within a row).  They
+// keep every group of 8 and of 16 consecutive lanes of a ds_read_b128 on
+// distinct 16-byte bank slots.  K rows are D*2 bytes (KCH chunks); V^T rows
+// are 64 bytes (4 chunks).
+template <int D>
+__device__ __forceinline__ int kswz(int row) {
+  return D == 128 ? (row & 15) : ((row & 6) | ((row ^ (row >> 3)) & 1));
+}
+__device__ __forceinline__ int vswz(int d) {
+  return (((d >> 1) ^ (d >> 2)) & 1) | ((((d >> 2) ^ (d >> 3)) & 1) << 1);
+}
+
+// Union walk over the sorted block lists of the G rows of a group.  Each
+// call yields the next block id and the bit mask of the rows that list it
+// (every list entry is consumed exactly once, sorted or not).
+template <int G>
+struct UnionWalk {
+  int pos[G], end[G];
+  __device__ __forceinline__ bool next(const int32_t* col_idx, int* J, uint32_t* mask) {
+    int best = 0x7FFFFFFF;
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      if (pos[g] < end[g]) best = min(best, sload(col_idx, pos[g]));
+    if (best == 0x7FFFFFFF) return false;
+    uint32_t m = 0;
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      if (pos[g] < end[g] && sload(col_idx, pos[g]) == best) {
+        m |= 1u << g;
+        ++pos[g];
+      }
+    *J = best;
+    *mask = m;
+    return true;
+  }
+};
+
+// G query blocks per workgroup (2G waves; wave w serves block w/2, queries
+// 32*(w%2)..+31).  Steps walk the union of the G block lists half by half;
+// a stage is loaded once and used by every wave pair whose list holds it.
+template <int D, int NST, int G>
+__global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
+  constexpr int NW = 2 * G;             // waves per workgroup
   constexpr int KS = D / 16;            // k-steps of S^T
   constexpr int DT = D / 32;            // d tiles of O^T
   constexpr int KCH = D / 8;            // 16-byte chunks per K row
   constexpr int HALF = 32 * D * 2;      // bytes of one K half (and of one V^T half)
   constexpr int STAGE = 2 * HALF;
   constexpr int NI = HALF / 1024;       // 1 KB direct loads per half per workgroup
-  constexpr int PW = NI;                // loads per wave per step (NI for K + NI for V, split over 2 waves)
+  constexpr int LPW = NI / NW;          // loads per wave per half (K and V each)
+  constexpr int PW = 2 * LPW;           // direct loads per wave per step
   constexpr float kLazy = 8.0f;
-  static_assert(NI % 2 == 0, "loads split evenly over the two waves");
+  static_assert(NI % NW == 0, "loads split evenly over the waves");
   __shared__ __attribute__((aligned(1024))) uint4 ring[NST * STAGE / 16];
   __shared__ int s_item;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int qg = w >> 1, w2 = w & 1;    // query block of the group, half of the block
   const int h = lane >> 5, l32 = lane & 31;
   const uint64_t t0 = wall_clock64();
   const float sl2 = a.scale * 1.44269504088896340736f;   // scores in log2 units
   // Source offset (bytes, within a K half / V^T half) of this lane's 16 bytes
   // for each of the wave's direct loads.  Load i writes LDS bytes
   // [1024 i, 1024 i + 1024) of the half; lane L lands at 1024 i + 16 L.
-  // K rows are D*2 bytes: physical chunk pc of row r holds logical chunk
-  // pc ^ (r & 7).  V^T rows are 64 bytes: physical chunk pc of row d holds
-  // logical chunk pc ^ ((d >> 1) & 3).
-  uint32_t koff[NI / 2], voff[NI / 2];
+  // Physical chunk pc of K row r holds logical chunk pc ^ kswz(r); physical
+  // chunk pc of V^T row d holds logical chunk pc ^ vswz(d).
+  uint32_t koff[LPW], voff[LPW];
 #pragma unroll
-  for (int j = 0; j < NI / 2; ++j) {
-    const int off = (2 * j + w) * 1024 + lane * 16;
+  for (int j = 0; j < LPW; ++j) {
+    const int off = (NW * j + w) * 1024 + lane * 16;
     const int row = off / (KCH * 16), pc = (off / 16) % KCH;
-    koff[j] = row * (D * 2) + ((pc ^ (row & 7)) * 16);
+    koff[j] = row * (D * 2) + ((pc ^ kswz<D>(row)) * 16);
     const int d = off / 64, pv = (off / 16) & 3;
-    voff[j] = d * 64 + ((pv ^ ((d >> 1) & 3)) * 16);
+    voff[j] = d * 64 + ((pv ^ vswz(d)) * 16);
   }
+  const int ngh = (a.n_blk + G - 1) / G;   // groups per head
   for (int item = next_item(a, &s_item, true); item >= 0; item = next_item(a, &s_item, false)) {
-    const int r = sload(a.worklist, __builtin_amdgcn_readfirstlane(item));
-    const int bh = r / a.n_blk;
-    const int I = r - bh * a.n_blk;
+    const int gid = sload(a.worklist, __builtin_amdgcn_readfirstlane(item));
+    const int bh = gid / ngh;
+    const int I0 = (gid - bh * ngh) * G;
     const int64_t head = (int64_t)bh * a.n_pad;
-    const int e0 = sload(a.row_ptr, r);
-    const int e1 = sload(a.row_ptr, r + 1);
-    const int nsteps = 2 * (e1 - e0);
+    // Two identical walks over the union: one issues loads NST-1 steps
+    // ahead, the other follows the computation (no per-step state to keep).
+    UnionWalk<G> iw, cw;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int64_t rr = (int64_t)bh * a.n_blk + I0 + g;
+      const bool ok = I0 + g < a.n_blk;
+      iw.pos[g] = cw.pos[g] = ok ? sload(a.row_ptr, rr) : 0;
+      iw.end[g] = cw.end[g] = ok ? sload(a.row_ptr, rr + 1) : 0;
+    }
     const char* kbase = (const char*)(a.k + head * D);
     const char* vbase = (const char*)(a.vt + head * D);
-
-    // Issue the direct loads of step `st` (block e0 + st/2, half st%2) into its stage.
-    auto issue = [&](int st) {
-      int J = sload(a.col_idx, e0 + (st >> 1));
-      if ((unsigned)J >= (unsigned)a.n_blk) J = 0;   // ids outside the plan: load block 0, masked below
-      const int u = st & 1;
+    int issued = 0;       // steps whose loads are issued
+    int curJ = 0;
+    uint32_t curM = 0;
+    bool more = true;
+    // Issue the direct loads of the next step (block curJ, half issued%2).
+    auto issue_next = [&]() __attribute__((always_inline)) -> bool {
+      if ((issued & 1) == 0) {
+        more = iw.next(a.col_idx, &curJ, &curM);
+        if (!more) return false;
+      }
+      const int u = issued & 1;
+      const int J = (unsigned)curJ < (unsigned)a.n_blk ? curJ : 0;   // ids outside the plan: masked below
       const char* ksrc = kbase + ((int64_t)J * 64 + 32 * u) * D * 2;
       const char* vsrc = vbase + (int64_t)J * 64 * D * 2 + u * HALF;
-      char* dst = (char*)ring + (st % NST) * STAGE;
+      char* dst = (char*)ring + (issued % NST) * STAGE;
 #pragma unroll
-      for (int j = 0; j < NI / 2; ++j) {
-        const int i = 2 * j + w;                     // this wave's share of the 1 KB loads
+      for (int j = 0; j < LPW; ++j) {
+        const int i = NW * j + w;
         dma16(ksrc + koff[j], dst + i * 1024);
         dma16(vsrc + voff[j], dst + HALF + i * 1024);
       }
+      ++issued;
+      return true;
     };
 
+    const bool has_row = I0 + qg < a.n_blk;
+    const int I = has_row ? I0 + qg : I0;
     bf16x8 qreg[KS];
     {
-      const uint4* qrow = (const uint4*)(a.q + (head + (int64_t)I * 64 + 32 * w + l32) * D);
+      const uint4* qrow = (const uint4*)(a.q + (head + (int64_t)I * 64 + 32 * w2 + l32) * D);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qreg[ks] = as_bf16x8(qrow[2 * ks + h]);
     }
@@ -195,32 +255,34 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnArgs a) {
     for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
     float m_run = -INFINITY, l_run = 0.0f;
 
-    // prologue: NST-1 steps in flight
 #pragma unroll
     for (int st = 0; st < NST - 1; ++st)
-      if (st < nsteps) issue(st);
+      if (more) issue_next();
 
-    for (int st = 0; st < nsteps; ++st) {
+    int J = 0;
+    uint32_t M = 0;
+    for (int st = 0; st < issued; ++st) {
+      if ((st & 1) == 0) cw.next(a.col_idx, &J, &M);
       // wait for this wave's loads of step st; later steps may stay in flight
-      const int ahead = min(nsteps - 1 - st, NST - 2);
-      if (ahead >= 2) wait_vm<2 * PW>();
+      const int ahead = issued - 1 - st;
+      if (ahead >= 3) wait_vm<3 * PW>();
+      else if (ahead == 2) wait_vm<2 * PW>();
       else if (ahead == 1) wait_vm<PW>();
       else wait_vm<0>();
       barrier_no_fence();
-      if (st + NST - 1 < nsteps) issue(st + NST - 1);   // into the stage retired by the barrier
+      if (more) issue_next();   // into the stage retired by the barrier
 
-      const int J = sload(a.col_idx, e0 + (st >> 1));
       const int u = st & 1;
       uint32_t mh = 0;
-      if ((unsigned)J < (unsigned)a.n_blk) mh = (uint32_t)(sload(a.blk_mask, J) >> (32 * u));
-      if (mh == 0) continue;   // half of pad keys only (uniform over the workgroup)
+      if ((M >> qg & 1) && (unsigned)J < (unsigned)a.n_blk) mh = (uint32_t)(sload(a.blk_mask, J) >> (32 * u));
+      if (mh == 0) continue;   // not in this block's list, or a half of pad keys (uniform per wave)
       const uint4* kst = ring + (st % NST) * (STAGE / 16);
       const uint4* vst = kst + HALF / 16;
 
       f32x16 s = {};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kst[l32 * KCH + ((2 * ks + h) ^ (l32 & 7))]),
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kst[l32 * KCH + ((2 * ks + h) ^ kswz<D>(l32))]),
                                                     qreg[ks], s, 0, 0, 0);
       // s[i]: key 8*(i/4) + 4*h + i%4 of this half, query l32.  Pad keys get
       // -inf; the scale (1/sqrt(D) in log2 units, > 0) is applied after the max.
@@ -258,25 +320,27 @@ __global__ __launch_bounds__(128, 2) void k_attn_bf16(AttnArgs a) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const int d = 32 * dt + l32;
-        const int sw = (d >> 1) & 3;
+        const int sw = vswz(d);
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vst[d * 4 + ((0 + h) ^ sw)]), pb0, o[dt], 0, 0, 0);
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vst[d * 4 + ((2 + h) ^ sw)]), pb1, o[dt], 0, 0, 0);
       }
     }
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    const bool qvalid = sload(a.blk_mask, I) >> (32 * w + l32) & 1;
-    uint16_t* orow = (uint16_t*)a.o + (head + (int64_t)I * 64 + 32 * w + l32) * D;
+    if (has_row) {
+      const float l_tot = l_run + __shfl_xor(l_run, 32);
+      const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+      const bool qvalid = sload(a.blk_mask, I) >> (32 * w2 + l32) & 1;
+      uint16_t* orow = (uint16_t*)a.o + (head + (int64_t)I * 64 + 32 * w2 + l32) * D;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
+      for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        typedef float f32x4 __attribute__((ext_vector_type(4)));
-        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-        f32x4 v = {o[dt][4 * g4] * inv, o[dt][4 * g4 + 1] * inv, o[dt][4 * g4 + 2] * inv, o[dt][4 * g4 + 3] * inv};
-        if (!qvalid) v = f32x4{0.f, 0.f, 0.f, 0.f};
-        const bf16x4 b = __builtin_convertvector(v, bf16x4);
-        *(uint2*)(orow + 32 * dt + 8 * g4 + 4 * h) = __builtin_bit_cast(uint2, b);
+        for (int g4 = 0; g4 < 4; ++g4) {
+          typedef float f32x4 __attribute__((ext_vector_type(4)));
+          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+          f32x4 v = {o[dt][4 * g4] * inv, o[dt][4 * g4 + 1] * inv, o[dt][4 * g4 + 2] * inv, o[dt][4 * g4 + 3] * inv};
+          if (!qvalid) v = f32x4{0.f, 0.f, 0.f, 0.f};
+          const bf16x4 b = __builtin_convertvector(v, bf16x4);
+          *(uint2*)(orow + 32 * dt + 8 * g4 + 4 * h) = __builtin_bit_cast(uint2, b);
+        }
       }
     }
   }
@@ -377,7 +441,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a) {
 // query blocks in id order (neighbouring query blocks keep overlapping key
 // blocks, which the XCD dealing turns into L2 hits).  Also clears the
 // per-XCD cursors and exhaustion flags.  One workgroup.
-__global__ __launch_bounds__(1024) void k_sched(const int32_t* __restrict__ row_ptr, int n_blk, int n_bh,
+__global__ __launch_bounds__(1024) void k_sched(const int32_t* __restrict__ row_ptr, int n_blk, int n_bh, int G,
                                                 int32_t* __restrict__ worklist, int32_t* __restrict__ cursor) {
   __shared__ int cost[FVA_MAX_SCHED_HEADS];
   __shared__ int rank[FVA_MAX_SCHED_HEADS];
@@ -393,11 +457,13 @@ __global__ __launch_bounds__(1024) void k_sched(const int32_t* __restrict__ row_
     rank[bh] = rk;
   }
   __syncthreads();
-  const int64_t n_rows = (int64_t)n_bh * n_blk;
-  for (int64_t r = tid; r < n_rows; r += 1024) {
-    const int bh = (int)(r / n_blk);
-    const int I = (int)(r - (int64_t)bh * n_blk);
-    worklist[(int64_t)rank[bh] * n_blk + I] = (int32_t)r;
+  // work items are groups of G consecutive query blocks of one head
+  const int ngh = (n_blk + G - 1) / G;
+  const int64_t n_items = (int64_t)n_bh * ngh;
+  for (int64_t r = tid; r < n_items; r += 1024) {
+    const int bh = (int)(r / ngh);
+    const int k = (int)(r - (int64_t)bh * ngh);
+    worklist[(int64_t)rank[bh] * ngh + k] = (int32_t)r;
   }
 }
 
@@ -405,22 +471,25 @@ __global__ __launch_bounds__(1024) void k_sched(const int32_t* __restrict__ row_
 // FVA_ATTN_STAGES=2|3|4 overrides it for tuning.
 // Rows per XCD chunk of the work list; FVA_ATTN_CHUNK overrides it.
 int attn_chunk() {
-  static int n = -1;
-  if (n < 0) {
-    const char* v = getenv("FVA_ATTN_CHUNK");
-    n = v ? atoi(v) : 32;
-    if (n < 1 || n > 4096) n = 32;
-  }
+  const char* v = getenv("FVA_ATTN_CHUNK");
+  int n = v ? atoi(v) : 32;
+  if (n < 1 || n > 4096) n = 32;
+  return n;
+}
+
+// Query blocks per workgroup of the bf16 kernel (1, 2 or 4);
+// FVA_ATTN_GROUP overrides it.
+int attn_group() {
+  const char* v = getenv("FVA_ATTN_GROUP");
+  int n = v ? atoi(v) : 2;
+  if (n != 1 && n != 2 && n != 4) n = 2;
   return n;
 }
 
 int attn_stages() {
-  static int n = -1;
-  if (n < 0) {
-    const char* v = getenv("FVA_ATTN_STAGES");
-    n = v ? atoi(v) : 3;
-    if (n < 2 || n > 4) n = 3;
-  }
+  const char* v = getenv("FVA_ATTN_STAGES");
+  int n = v ? atoi(v) : 3;
+  if (n < 2 || n > 4) n = 3;
   return n;
 }
 
@@ -444,7 +513,9 @@ extern "C" int fva_attention(fva_plan_t plan, const void* q_perm, const void* k_
   const fva_plan_desc& d = plan->desc;
   const fva_plan_info& in = plan->info;
   const int n_bh = d.batch * d.heads;
-  hipLaunchKernelGGL(k_sched, dim3(1), dim3(1024), 0, stream, row_ptr, in.n_blk, n_bh, plan->worklist,
+  int G = d.dtype == FVA_DTYPE_BF16 ? attn_group() : 1;
+  if (d.head_dim == 64 && G > 2) G = 2;   // a 4 KB half splits over at most 4 waves
+  hipLaunchKernelGGL(k_sched, dim3(1), dim3(1024), 0, stream, row_ptr, in.n_blk, n_bh, G, plan->worklist,
                      plan->counters);
   AttnArgs a{};
   a.q = (const uint16_t*)q_perm;
@@ -461,7 +532,7 @@ extern "C" int fva_attention(fva_plan_t plan, const void* q_perm, const void* k_
   a.cursor = plan->counters;
   a.wg_times = wg_times;
   a.n_pad = in.n_pad;
-  a.n_items = (int)in.n_rows;
+  a.n_items = n_bh * ((in.n_blk + G - 1) / G);
   a.n_blk = in.n_blk;
   a.persistent = sched_mode == FVA_SCHED_PERSISTENT;
   a.chunk = attn_chunk();
@@ -470,27 +541,37 @@ extern "C" int fva_attention(fva_plan_t plan, const void* q_perm, const void* k_
 #define FVA_LAUNCH(KERNEL, THREADS)                                                              \
   do {                                                                                           \
     const int deal = kXcds * a.chunk;                                                            \
-    int grid = (int)((in.n_rows + deal - 1) / deal * deal);                                      \
+    int grid = (int)((a.n_items + deal - 1) / deal * deal);                                      \
     if (a.persistent)                                                                            \
-      grid = (int)std::min<int64_t>(std::min<int64_t>(in.n_rows, in.max_wg),                     \
+      grid = (int)std::min<int64_t>(std::min<int64_t>(a.n_items, in.max_wg),                     \
                                     (int64_t)plan->num_cu * occupancy(KERNEL, THREADS));         \
     hipLaunchKernelGGL(KERNEL, dim3(grid), dim3(THREADS), 0, stream, a);                        \
   } while (0)
   if (d.dtype == FVA_DTYPE_BF16) {
     const int ns = attn_stages();
+#define FVA_BF16_128(NS)                                                      \
+    if (G == 1) FVA_LAUNCH((k_attn_bf16<128, NS, 1>), 128);                   \
+    else if (G == 2) FVA_LAUNCH((k_attn_bf16<128, NS, 2>), 256);              \
+    else FVA_LAUNCH((k_attn_bf16<128, NS, 4>), 512);
+#define FVA_BF16_64(NS)                                                       \
+    if (G == 1) FVA_LAUNCH((k_attn_bf16<64, NS, 1>), 128);                    \
+    else FVA_LAUNCH((k_attn_bf16<64, NS, 2>), 256);
     if (d.head_dim == 128) {
-      if (ns == 2) FVA_LAUNCH((k_attn_bf16<128, 2>), 128);
-      else if (ns == 3) FVA_LAUNCH((k_attn_bf16<128, 3>), 128);
-      else FVA_LAUNCH((k_attn_bf16<128, 4>), 128);
+      if (ns == 2) { FVA_BF16_128(2) }
+      else if (ns == 3) { FVA_BF16_128(3) }
+      else { FVA_BF16_128(4) }
     } else {
-      if (ns == 2) FVA_LAUNCH((k_attn_bf16<64, 2>), 128);
-      else if (ns == 3) FVA_LAUNCH((k_attn_bf16<64, 3>), 128);
-      else FVA_LAUNCH((k_attn_bf16<64, 4>), 128);
+      if (ns == 2) { FVA_BF16_64(2) }
+      else if (ns == 3) { FVA_BF16_64(3) }
+      else { FVA_BF16_64(4) }
     }
+#undef FVA_BF16_128
+#undef FVA_BF16_64
   } else {
     if (d.head_dim == 128) FVA_LAUNCH(k_attn_f32<128>, 256);
     else FVA_LAUNCH(k_attn_f32<64>, 256);
   }
 #undef FVA_LAUNCH
   return fva_after_launch(stream, "fva_attention");
+
 }

@@ -53,6 +53,8 @@ int fva_fail(int code, const char* fmt, ...);
 int fva_hip_check(hipError_t e, const char* what);
 // After the launches of one call: with FVA_DEBUG=1, synchronise and check.
 int fva_after_launch(hipStream_t s, const char* what);
+// FVA_DEBUG=1 in the environment (read once).
+int fva_debug_enabled();
 
 struct SelectArgs {
   float p[FVA_MAX_PHEAD];

@@ -33,15 +33,19 @@ int fva_hip_check(hipError_t e, const char* what) {
   return fva_fail(FVA_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-int fva_after_launch(hipStream_t s, const char* what) {
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fva_fail(FVA_EHIP, "%s launch: %s", what, hipGetErrorString(e));
+int fva_debug_enabled() {
   static int debug = -1;
   if (debug < 0) {
     const char* v = getenv("FVA_DEBUG");
     debug = (v && v[0] == '1') ? 1 : 0;
   }
-  if (debug) {
+  return debug;
+}
+
+int fva_after_launch(hipStream_t s, const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fva_fail(FVA_EHIP, "%s launch: %s", what, hipGetErrorString(e));
+  if (fva_debug_enabled()) {
     e = hipStreamSynchronize(s);
     if (e != hipSuccess) return fva_fail(FVA_EHIP, "%s: %s", what, hipGetErrorString(e));
   }

@@ -231,3 +231,26 @@ def test_wg_times_recorded():
     t = wt.cpu().numpy().reshape(-1, 2)
     used = t[t[:, 0] > 0]
     assert len(used) > 0 and np.all(used[:, 1] >= used[:, 0])
+
+
+def test_launch_shapes_bitwise_equal(monkeypatch):
+    """Group size, LDS ring depth, XCD chunk and schedule change only the
+    order rows are taken in, never a row's arithmetic: outputs are bitwise
+    equal."""
+    w = synth.scaled(synth.WORKLOADS["wan1.3b_480p"], H=3, grid=(9, 10, 13))
+    plan, opl, (q, k, v), _, meta = _plan_and_inputs(w)
+    ref = None
+    for group, stages, chunk, sched in [("1", "3", "32", "persistent"), ("2", "2", "16", "plain"),
+                                        ("4", "4", "1", "persistent"), ("2", "3", "32", "persistent"),
+                                        ("4", "2", "64", "plain"), ("2", "4", "8", "plain")]:
+        monkeypatch.setenv("FVA_ATTN_GROUP", group)
+        monkeypatch.setenv("FVA_ATTN_STAGES", stages)
+        monkeypatch.setenv("FVA_ATTN_CHUNK", chunk)
+        b = fva.Buffers(plan)
+        out = torch.empty_like(q)
+        fva.attention_call(plan, q, k, v, out, 0.9, 16, b, sched=sched)
+        torch.cuda.synchronize()
+        if ref is None:
+            ref = out
+        else:
+            assert torch.equal(out, ref), (group, stages, chunk, sched)
