@@ -2,17 +2,24 @@
 one MI355X.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                  [--sched persistent|plain] [--no-cpu]
+                  [--sched persistent|plain] [--no-cpu] [--cpu-heads N]
+  python bench.py --copy-probe MIB     # plain device copy of a known size,
+                                       # the calibration run for HBM counters
 
 A step is one whole call: permute Q, K, V -> select (pool, score, Top-p with
 Top-k floor, CSR) -> block-sparse attention -> unpermute O, on one HIP stream
-with the inputs already resident in HBM.  Prints one JSON line.
+with the inputs already resident in HBM.  Events recorded on that stream
+between the stages of every timed step give the per-stage times (the
+attention stage is a single kernel launch after a tiny scheduling kernel).
+Prints one JSON line.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -23,7 +30,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector / matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
+ATTN_SOURCE = os.path.join(ROOT, "block_sparse_spatiotemporal_amd", "csrc", "attention.hip")
 
 
 def parse():
@@ -34,11 +43,32 @@ def parse():
     ap.add_argument("--workload", default="wan14b_480p_cfg")
     ap.add_argument("--sched", default="persistent", choices=["persistent", "plain"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-heads", type=int, default=2, help="(b,h) pairs in the CPU oracle sample")
+    ap.add_argument("--cpu-heads", type=int, default=4, help="(b,h) pairs in the CPU oracle sample")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (counter calibration)")
     return ap.parse_args()
 
 
-def cpu_baseline(w, q, k, v, n_heads):
+def source_digest(path=ATTN_SOURCE):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per attention launch from the committed counter summary,
+    if it was taken on the current attention source; else None."""
+    path = os.path.join(ROOT, "profiles", f"k_attn_bf16_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_src = re.search(r"source_sha256_16:\s*([0-9a-f]+)", txt)
+    m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not (m_src and m_b) or m_src.group(1) != source_digest():
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(w, q, k, v, n_heads, p_head):
     """The oracle, untuned, on the first n_heads (b, h) pairs of the same
     inputs; scaled linearly to one whole call."""
     from block_sparse_spatiotemporal_amd import synth
@@ -53,13 +83,37 @@ def cpu_baseline(w, q, k, v, n_heads):
     t0 = time.perf_counter()
     for b, h in pairs:
         sl = lambda a: synth.to_f64(a[b:b + 1, :, h:h + 1, :], w.dtype)
-        p = float(np.float32(w.p)) if not isinstance(w.p, tuple) else 0.75
-        O.run(sl(q), sl(k), sl(v), opl, p, w.k_min, "none")
+        O.run(sl(q), sl(k), sl(v), opl, float(p_head[b * w.H + h]), w.k_min, "none")
     dt = time.perf_counter() - t0
     scale = (w.B * w.H) / len(pairs)
     return {"value": round(dt * scale * 1e3, 1), "unit": "ms/call", "cores": int(blas_threads),
             "kind": "oracle",
-            "sample": f"{len(pairs)} of {w.B * w.H} (b,h) heads, full path, {dt:.1f} s, scaled x{scale:g}"}
+            "sample": f"{len(pairs)} of {w.B * w.H} (b,h) heads of the same inputs, full path "
+                      f"(plan, permute, pool, score, select, attention, unpermute; no slack fill), "
+                      f"{dt:.1f} s, scaled x{scale:g}"}
+
+
+def copy_probe(mib, steps):
+    import torch
+    n = mib * (1 << 20)
+    a = torch.ones(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": steps}), flush=True)
+
+
+def cu_idle(wg):
+    """From per-workgroup (start, end) stamps of a persistent launch: idle
+    fraction of the launch's workgroup slots over the kernel span, and
+    max / mean slot load."""
+    wg = wg.reshape(-1, 2).astype(np.int64)
+    wg = wg[wg[:, 1] > 0]
+    busy = wg[:, 1] - wg[:, 0]
+    span = wg[:, 1].max() - wg[:, 0].min()
+    return {"slots": int(len(wg)), "idle_frac": round(1.0 - busy.sum() / (len(wg) * span), 4),
+            "max_over_mean_load": round(float(busy.max() / busy.mean()), 3)}
 
 
 def main():
@@ -71,6 +125,10 @@ def main():
     import torch
     from block_sparse_spatiotemporal_amd import fva, synth
 
+    if args.copy_probe:
+        copy_probe(args.copy_probe, args.steps)
+        return
+
     w = synth.WORKLOADS[args.workload]
     q, k, v, meta = synth.make(w)
     dev = (lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()) if w.dtype == "bf16" \
@@ -79,56 +137,65 @@ def main():
     plan = fva.Plan(w.B, w.H, w.D, w.grid, tile=w.tile, order=w.order, sub=w.sub, dtype=w.dtype)
     bufs = fva.Buffers(plan)
     out = torch.empty_like(qd)
-    p = meta["p_head"].tolist() if isinstance(w.p, tuple) else float(meta["p_head"][0])
+    p_head = meta["p_head"]
+    p = p_head.tolist() if isinstance(w.p, tuple) else float(p_head[0])
 
-    def call():
-        fva.attention_call(plan, qd, kd, vd, out, p, w.k_min, bufs, slack=w.slack, sched=args.sched)
+    names = ["permute_q", "permute_k", "permute_v", "select", "attention", "unpermute"]
+
+    def call(ev=None):
+        # the same six C-ABI calls as fva.attention_call, with events between them
+        rec = (lambda i: ev[i].record()) if ev else (lambda i: None)
+        rec(0)
+        fva.fva_permute(plan, qd, bufs.q, fva.LAYOUT_ROWS); rec(1)
+        fva.fva_permute(plan, kd, bufs.k, fva.LAYOUT_ROWS); rec(2)
+        fva.fva_permute(plan, vd, bufs.vt, fva.LAYOUT_VT); rec(3)
+        fva.fva_select(plan, bufs.q, bufs.k, p, w.k_min, bufs.row_ptr, bufs.col_idx, slack=w.slack,
+                       head_nnz=bufs.head_nnz); rec(4)
+        fva.fva_attention(plan, bufs.q, bufs.k, bufs.vt, bufs.row_ptr, bufs.col_idx, bufs.o,
+                          sched=args.sched); rec(5)
+        fva.fva_unpermute(plan, bufs.o, out); rec(6)
 
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
 
-    # whole-call timing over exactly `steps` calls
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        call()
-    e1.record()
+    # exactly `steps` timed calls; events on the launch stream between stages
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    ms_call = e0.elapsed_time(e1) / args.steps
+    for i in range(args.steps):
+        call(evs[i])
+    torch.cuda.synchronize()
+    ms_call = evs[0][0].elapsed_time(evs[-1][6]) / args.steps
+    stage = {n: np.array([e[j].elapsed_time(e[j + 1]) for e in evs]) for j, n in enumerate(names)}
+    st_mean = {n: float(x.mean()) for n, x in stage.items()}
+    st_med = {n: float(np.median(x)) for n, x in stage.items()}
 
-    # per-stage timing (events between the calls of the same stream)
-    names = ["permute_q", "permute_k", "permute_v", "select", "attention", "unpermute"]
-    stage = {n: [] for n in names}
-    for _ in range(args.steps):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
-        ev[0].record()
-        fva.fva_permute(plan, qd, bufs.q, fva.LAYOUT_ROWS); ev[1].record()
-        fva.fva_permute(plan, kd, bufs.k, fva.LAYOUT_ROWS); ev[2].record()
-        fva.fva_permute(plan, vd, bufs.vt, fva.LAYOUT_VT); ev[3].record()
-        fva.fva_select(plan, bufs.q, bufs.k, p, w.k_min, bufs.row_ptr, bufs.col_idx, slack=w.slack,
-                       head_nnz=bufs.head_nnz); ev[4].record()
-        fva.fva_attention(plan, bufs.q, bufs.k, bufs.vt, bufs.row_ptr, bufs.col_idx, bufs.o,
-                          sched=args.sched); ev[5].record()
-        fva.fva_unpermute(plan, bufs.o, out); ev[6].record()
-        torch.cuda.synchronize()
-        for i, n in enumerate(names):
-            stage[n].append(ev[i].elapsed_time(ev[i + 1]))
-    st = {n: float(np.median(x)) for n, x in stage.items()}
+    # one extra, untimed call with per-workgroup stamps for the load balance
+    wg = torch.zeros(2 * plan.info.max_wg, dtype=torch.int64, device="cuda")
+    fva.fva_attention(plan, bufs.q, bufs.k, bufs.vt, bufs.row_ptr, bufs.col_idx, bufs.o, sched=args.sched,
+                      wg_times=wg)
+    torch.cuda.synchronize()
+    balance = cu_idle(wg.cpu().numpy().view(np.uint64)) if args.sched == "persistent" else None
 
     nnz = int(bufs.row_ptr[-1].item())
     head_nnz = bufs.head_nnz.cpu().numpy()
     n_blk = plan.n_blk
     sparse_flop = nnz * 4.0 * 64 * 64 * w.D
     dense_flop = 4.0 * w.B * w.H * float(w.n_tokens) ** 2 * w.D
-    attn_tflops = sparse_flop / (st["attention"] * 1e-3) / 1e12
+    attn_tflops = sparse_flop / (st_mean["attention"] * 1e-3) / 1e12
     dens = head_nnz / float(n_blk * n_blk)
 
-    # algorithmic bytes of the HBM-bound stages (valid rows, element size)
+    # algorithmic bytes of the HBM-bound stages (valid rows at the element size)
     es = 2 if w.dtype == "bf16" else 4
-    row = w.D * es
-    perm_bytes = w.B * w.H * (w.n_tokens * row + plan.n_pad * row)
-    unperm_bytes = w.B * w.H * 2 * w.n_tokens * row
+    BH, N, row = w.B * w.H, w.n_tokens, w.D * es
+    perm_bytes = BH * (N * row + plan.n_pad * row)        # read valid rows, write every padded row
+    unperm_bytes = BH * 2 * N * row
+    n_kbar = n_blk * (8 if w.sub[0] else 1)
+    sel_bytes = (2 * BH * N * row                           # pool reads Q and K once
+                 + BH * (n_blk + n_kbar) * w.D * 8          # pooled Q, K written (fp64)
+                 + BH * n_blk * n_blk * 4                   # fp32 scores, one pass
+                 + 4 * nnz + 4 * (plan.n_rows + 1))         # CSR out
+    traffic = measured_traffic(w.name)
 
     res = {
         "metric": "ms/attn call + dense-equiv TFLOPS & MFMA util %, 32760-tok 40-head bf16 at p=0.9",
@@ -151,17 +218,25 @@ def main():
         "attention_sparse_tflops": round(attn_tflops, 2),
         "mfma_util_pct": round(100.0 * attn_tflops / PEAK_BF16_TFLOPS, 2),
         "sparse_tflop_per_call": round(sparse_flop / 1e12, 3),
+        "nnz_blocks": nnz,
         "density": {"mean": round(float(dens.mean()), 4), "min": round(float(dens.min()), 4),
                     "max": round(float(dens.max()), 4)},
-        "stage_ms": {n: round(x, 4) for n, x in st.items()},
-        "permute_gbs": round((perm_bytes / (st["permute_q"] * 1e-3)) / 1e9, 1),
-        "unpermute_gbs": round((unperm_bytes / (st["unpermute"] * 1e-3)) / 1e9, 1),
+        "stage_ms_mean": {n: round(x, 4) for n, x in st_mean.items()},
+        "stage_ms_median": {n: round(x, 4) for n, x in st_med.items()},
+        "core_ms": round(st_mean["select"] + st_mean["attention"], 4),
+        "hbm_gbs": {"permute_rows": round(perm_bytes / (st_mean["permute_q"] * 1e-3) / 1e9, 1),
+                    "permute_vt": round(perm_bytes / (st_mean["permute_v"] * 1e-3) / 1e9, 1),
+                    "select": round(sel_bytes / (st_mean["select"] * 1e-3) / 1e9, 1),
+                    "unpermute": round(unperm_bytes / (st_mean["unpermute"] * 1e-3) / 1e9, 1),
+                    "peak": PEAK_HBM_GBS},
+        "load_balance": balance,
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "k_attn_bf16 (fva_attention)"},
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "kernel": "k_attn_bf16 (fva_attention)",
+                     "launch_ms": round(st_mean["attention"], 4)},
     }
     if not args.no_cpu:
-        res["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_heads)
+        res["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_heads, p_head)
     print(json.dumps(res), flush=True)
 
 

@@ -28,6 +28,7 @@ struct AttnArgs {
   const int32_t* row_ptr;
   const int32_t* col_idx;
   const uint64_t* blk_mask;
+  const uint64_t* blk_full; // [64] bitmap of blocks with every position valid
   void* o;
   const int32_t* worklist;
   int32_t* cursor;
@@ -137,27 +138,25 @@ __device__ __forceinline__ int vswz(int d) {
   return (((d >> 1) ^ (d >> 2)) & 1) | ((((d >> 2) ^ (d >> 3)) & 1) << 1);
 }
 
-// Union walk over the sorted block lists of the G rows of a group.  Each
-// call yields the next block id and the bit mask of the rows that list it
-// (every list entry is consumed exactly once, sorted or not).
-template <int G>
-struct UnionWalk {
-  int pos[G], end[G];
-  __device__ __forceinline__ bool next(const int32_t* col_idx, int* J, uint32_t* mask) {
-    int best = 0x7FFFFFFF;
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-      if (pos[g] < end[g]) best = min(best, sload(col_idx, pos[g]));
-    if (best == 0x7FFFFFFF) return false;
-    uint32_t m = 0;
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-      if (pos[g] < end[g] && sload(col_idx, pos[g]) == best) {
-        m |= 1u << g;
-        ++pos[g];
-      }
-    *J = best;
-    *mask = m;
+// Word w (blocks 64w..64w+63) of a block bitmap held one 64-bit word per
+// lane, read out as a wave-uniform value.
+__device__ __forceinline__ uint64_t lane_word(uint32_t lo, uint32_t hi, int w) {
+  return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, w) << 32) |
+         (uint32_t)__builtin_amdgcn_readlane((int)lo, w);
+}
+
+// Ascending walk over the set bits of such a bitmap; the state is
+// wave-uniform, so the walk is scalar arithmetic with no memory access.
+struct BitWalk {
+  uint64_t bits = 0;  // unvisited bits of word w
+  int w = -1;
+  __device__ __forceinline__ bool next(uint32_t lo, uint32_t hi, int nw, int* J) {
+    while (bits == 0) {
+      if (++w >= nw) return false;
+      bits = lane_word(lo, hi, w);
+    }
+    *J = 64 * w + __builtin_ctzll(bits);
+    bits &= bits - 1;
     return true;
   }
 };
@@ -180,8 +179,13 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
   static_assert(NI % NW == 0, "loads split evenly over the waves");
   __shared__ __attribute__((aligned(1024))) uint4 ring[NST * STAGE / 16];
   __shared__ int s_item;
+  __shared__ uint32_t s_bits[128 * G];  // per row of the group: 64 bitmap words of 64 bits
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int qg = w >> 1, w2 = w & 1;    // query block of the group, half of the block
+  const int nw = (a.n_blk + 63) >> 6;   // bitmap words in use (n_blk <= 4096)
+  // blocks with all 64 positions valid (no key mask needed), one word per lane
+  const uint64_t fw = lane < nw ? a.blk_full[lane] : 0;
+  const uint32_t full_lo = (uint32_t)fw, full_hi = (uint32_t)(fw >> 32);
   const int h = lane >> 5, l32 = lane & 31;
   const uint64_t t0 = wall_clock64();
   const float sl2 = a.scale * 1.44269504088896340736f;   // scores in log2 units
@@ -205,30 +209,45 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
     const int bh = gid / ngh;
     const int I0 = (gid - bh * ngh) * G;
     const int64_t head = (int64_t)bh * a.n_pad;
-    // Two identical walks over the union: one issues loads NST-1 steps
-    // ahead, the other follows the computation (no per-step state to keep).
-    UnionWalk<G> iw, cw;
+    // The G rows' block sets as bitmaps: LDS words filled from the CSR
+    // lists (ids outside the plan are dropped), then one 64-bit word per
+    // lane for the union and for this wave's own row.
+    s_bits[tid] = 0;
+    __syncthreads();
+    {
+      const int64_t rr = (int64_t)bh * a.n_blk + I0 + qg;
+      if (I0 + qg < a.n_blk) {
+        const int beg = sload(a.row_ptr, rr), end = sload(a.row_ptr, rr + 1);
+        for (int j = beg + (tid & 127); j < end; j += 128) {
+          const int J = a.col_idx[j];
+          if ((unsigned)J < (unsigned)a.n_blk) atomicOr(&s_bits[128 * qg + (J >> 5)], 1u << (J & 31));
+        }
+      }
+    }
+    __syncthreads();
+    uint32_t own_lo = s_bits[128 * qg + 2 * lane], own_hi = s_bits[128 * qg + 2 * lane + 1];
+    uint32_t un_lo = 0, un_hi = 0;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const int64_t rr = (int64_t)bh * a.n_blk + I0 + g;
-      const bool ok = I0 + g < a.n_blk;
-      iw.pos[g] = cw.pos[g] = ok ? sload(a.row_ptr, rr) : 0;
-      iw.end[g] = cw.end[g] = ok ? sload(a.row_ptr, rr + 1) : 0;
+      un_lo |= s_bits[128 * g + 2 * lane];
+      un_hi |= s_bits[128 * g + 2 * lane + 1];
     }
+    // Two identical walks over the union: one issues loads NST-1 steps
+    // ahead, the other follows the computation.
+    BitWalk iw, cw;
     const char* kbase = (const char*)(a.k + head * D);
     const char* vbase = (const char*)(a.vt + head * D);
     int issued = 0;       // steps whose loads are issued
     int curJ = 0;
-    uint32_t curM = 0;
     bool more = true;
     // Issue the direct loads of the next step (block curJ, half issued%2).
     auto issue_next = [&]() __attribute__((always_inline)) -> bool {
       if ((issued & 1) == 0) {
-        more = iw.next(a.col_idx, &curJ, &curM);
+        more = iw.next(un_lo, un_hi, nw, &curJ);
         if (!more) return false;
       }
       const int u = issued & 1;
-      const int J = (unsigned)curJ < (unsigned)a.n_blk ? curJ : 0;   // ids outside the plan: masked below
+      const int J = curJ;
       const char* ksrc = kbase + ((int64_t)J * 64 + 32 * u) * D * 2;
       const char* vsrc = vbase + (int64_t)J * 64 * D * 2 + u * HALF;
       char* dst = (char*)ring + (issued % NST) * STAGE;
@@ -260,9 +279,13 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
       if (more) issue_next();
 
     int J = 0;
-    uint32_t M = 0;
+    bool mine = false, full = false;
     for (int st = 0; st < issued; ++st) {
-      if ((st & 1) == 0) cw.next(a.col_idx, &J, &M);
+      if ((st & 1) == 0) {
+        cw.next(un_lo, un_hi, nw, &J);
+        mine = lane_word(own_lo, own_hi, J >> 6) >> (J & 63) & 1;
+        full = lane_word(full_lo, full_hi, J >> 6) >> (J & 63) & 1;
+      }
       // wait for this wave's loads of step st; later steps may stay in flight
       const int ahead = issued - 1 - st;
       if (ahead >= 3) wait_vm<3 * PW>();
@@ -274,8 +297,8 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
 
       const int u = st & 1;
       uint32_t mh = 0;
-      if ((M >> qg & 1) && (unsigned)J < (unsigned)a.n_blk) mh = (uint32_t)(sload(a.blk_mask, J) >> (32 * u));
-      if (mh == 0) continue;   // not in this block's list, or a half of pad keys (uniform per wave)
+      if (mine) mh = full ? 0xFFFFFFFFu : (uint32_t)(sload(a.blk_mask, J) >> (32 * u));
+      if (mh == 0) continue;   // not in this row's list, or a half of pad keys (uniform per wave)
       const uint4* kst = ring + (st % NST) * (STAGE / 16);
       const uint4* vst = kst + HALF / 16;
 
@@ -527,6 +550,7 @@ extern "C" int fva_attention(fva_plan_t plan, const void* q_perm, const void* k_
   a.row_ptr = row_ptr;
   a.col_idx = col_idx;
   a.blk_mask = plan->blk_mask;
+  a.blk_full = plan->blk_full;
   a.o = o_perm;
   a.worklist = plan->worklist;
   a.cursor = plan->counters;

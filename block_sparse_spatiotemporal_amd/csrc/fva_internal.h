@@ -25,6 +25,7 @@ struct fva_plan_s {
   // device tables (uploaded once at creation)
   int32_t* perm;      // [n_pad] raster token or -1
   uint64_t* blk_mask; // [n_blk] valid-position bitmask
+  uint64_t* blk_full; // [64] bit J set when block J has all 64 positions valid
   int32_t* blk_cnt;   // [n_blk] valid tokens
   uint8_t* sub_pos;   // [n_blk][8][8] local positions of each sub-block
   int32_t* sub_cnt;   // [n_blk][8] valid tokens per sub-block

@@ -174,6 +174,7 @@ static void layout_workspace(const fva_plan_desc* d, const fva_plan_info& in, si
   offs[14] = c.take(sizeof(int32_t) * in.n_rows);                        // worklist
   offs[15] = c.take(sizeof(int32_t) * 64);                               // counters
   offs[16] = c.take(sizeof(float) * bh * in.n_blk * in.n_blk);           // sbuf
+  offs[17] = c.take(sizeof(uint64_t) * 64);                              // blk_full
   *total = c.off;
 }
 
@@ -252,7 +253,7 @@ extern "C" int fva_plan_dims(const fva_plan_desc* desc, fva_plan_info* info) {
   if (!info) return fva_fail(FVA_EINVAL, "info is NULL");
   int rc = validate(desc, info);
   if (rc) return rc;
-  size_t offs[17], total;
+  size_t offs[18], total;
   layout_workspace(desc, *info, offs, &total);
   info->workspace_bytes = (int64_t)total;
   return FVA_OK;
@@ -277,7 +278,7 @@ extern "C" int fva_plan_create(fva_plan_t* out, const fva_plan_desc* desc, hipSt
   fva_plan_info in;
   int rc = validate(desc, &in);
   if (rc) return rc;
-  size_t offs[17], total;
+  size_t offs[18], total;
   layout_workspace(desc, in, offs, &total);
   in.workspace_bytes = (int64_t)total;
 
@@ -322,12 +323,19 @@ extern "C" int fva_plan_create(fva_plan_t* out, const fva_plan_desc* desc, hipSt
   p->worklist = (int32_t*)(b + offs[14]);
   p->counters = (int32_t*)(b + offs[15]);
   p->sbuf = (float*)(b + offs[16]);
+  p->blk_full = (uint64_t*)(b + offs[17]);
 
   // Synchronous upload from pageable memory: the tables are small and this
   // happens once per plan, outside any timed path.
   rc = fva_hip_check(hipMemcpy(p->perm, t.perm.data(), sizeof(int32_t) * in.n_pad, hipMemcpyHostToDevice), "upload perm");
   if (!rc) rc = fva_hip_check(hipMemcpy(p->blk_mask, t.mask.data(), sizeof(uint64_t) * in.n_blk, hipMemcpyHostToDevice), "upload mask");
   if (!rc) rc = fva_hip_check(hipMemcpy(p->blk_cnt, t.cnt.data(), sizeof(int32_t) * in.n_blk, hipMemcpyHostToDevice), "upload cnt");
+  if (!rc) {
+    uint64_t full[64] = {};
+    for (int64_t j = 0; j < in.n_blk; ++j)
+      if (t.cnt[j] == FVA_BLK) full[j >> 6] |= 1ull << (j & 63);
+    rc = fva_hip_check(hipMemcpy(p->blk_full, full, sizeof(full), hipMemcpyHostToDevice), "upload full");
+  }
   if (!rc && in.n_sub) {
     rc = fva_hip_check(hipMemcpy(p->sub_pos, t.sub_pos.data(), t.sub_pos.size(), hipMemcpyHostToDevice), "upload sub_pos");
     if (!rc) rc = fva_hip_check(hipMemcpy(p->sub_cnt, t.sub_cnt.data(), sizeof(int32_t) * t.sub_cnt.size(), hipMemcpyHostToDevice), "upload sub_cnt");

@@ -193,8 +193,10 @@ int fva_select(fva_plan_t plan, const void* q_perm, const void* k_perm, const fl
  * over the valid key tokens j of the blocks listed in row (b, h, I).  Pad
  * query rows of o_perm are written as zero; a row with no blocks gives zero.
  *   q_perm, k_perm  FVA_LAYOUT_ROWS;  vt_perm  FVA_LAYOUT_VT.
- *   row_ptr, col_idx  any valid CSR over the plan's rows (ids in
- *                   [0, n_blk), ascending or not), e.g. from fva_select.
+ *   row_ptr, col_idx  any valid CSR over the plan's rows, e.g. from
+ *                   fva_select: each row lists a set of block ids, in any
+ *                   order; an id listed twice counts once and ids outside
+ *                   [0, n_blk) are ignored.
  *   o_perm          [B, H, N_pad, D], plan dtype.
  *   sched_mode      FVA_SCHED_PERSISTENT: a persistent grid pops rows from a
  *                   device work list sorted by decreasing cost;
