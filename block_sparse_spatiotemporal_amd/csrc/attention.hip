@@ -97,8 +97,18 @@ __device__ __forceinline__ int next_item(const AttnArgs& a, int* s_item, bool fi
 // The running max is raised lazily: P may grow to 2^kLazy before O and l are
 // rescaled, which skips most rescales once the row maximum is found.
 
-__device__ __forceinline__ void dma16(const void* g, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+// Direct global->LDS load of 16 bytes per lane from the wave-uniform base
+// plus the lane's 32-bit byte offset; lane i's bytes land at lds_base + 16*i.
+// Written as inline assembly on purpose: the compiler cannot tell which ring
+// stage a direct load writes, so for the builtin it makes every later LDS
+// read wait for all direct loads in flight, which would drain the prefetch
+// pipeline each step.  Ordering is kept by hand instead: each wave waits on
+// its own vector-memory count (wait_vm) and a workgroup barrier publishes
+// the stage before any wave reads it.
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, void* lds_base) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_base);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(m) : "memory", "m0");
 }
 
 // s_waitcnt with only the vector-memory count limited to n (other counters
@@ -254,8 +264,8 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
 #pragma unroll
       for (int j = 0; j < LPW; ++j) {
         const int i = NW * j + w;
-        dma16(ksrc + koff[j], dst + i * 1024);
-        dma16(vsrc + voff[j], dst + HALF + i * 1024);
+        dma16(ksrc, koff[j], dst + i * 1024);
+        dma16(vsrc, voff[j], dst + HALF + i * 1024);
       }
       ++issued;
       return true;
@@ -268,6 +278,10 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
       const uint4* qrow = (const uint4*)(a.q + (head + (int64_t)I * 64 + 32 * w2 + l32) * D);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qreg[ks] = as_bf16x8(qrow[2 * ks + h]);
+      // Settle the Q loads before any direct load is issued: a wait left to
+      // the first use inside the step loop would also count, every step, the
+      // direct loads in flight behind them.
+      wait_vm<0>();
     }
     f32x16 o[DT];
 #pragma unroll
