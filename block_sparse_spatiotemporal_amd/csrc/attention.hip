@@ -98,17 +98,21 @@ __device__ __forceinline__ int next_item(const AttnArgs& a, int* s_item, bool fi
 // rescaled, which skips most rescales once the row maximum is found.
 
 // Direct global->LDS load of 16 bytes per lane from the wave-uniform base
-// plus the lane's 32-bit byte offset; lane i's bytes land at lds_base + 16*i.
+// plus the lane's 32-bit byte offset; lane i's bytes land at LDS address
+// lds_addr + 16*i (lds_addr wave-uniform).
 // Written as inline assembly on purpose: the compiler cannot tell which ring
 // stage a direct load writes, so for the builtin it makes every later LDS
 // read wait for all direct loads in flight, which would drain the prefetch
 // pipeline each step.  Ordering is kept by hand instead: each wave waits on
 // its own vector-memory count (wait_vm) and a workgroup barrier publishes
 // the stage before any wave reads it.
-__device__ __forceinline__ void dma16(const void* base, uint32_t off, void* lds_base) {
-  const uint32_t m = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_base);
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(m) : "memory", "m0");
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds_addr) : "memory", "m0");
+}
+
+// LDS byte address of a shared-memory object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
 // s_waitcnt with only the vector-memory count limited to n (other counters
@@ -190,7 +194,8 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) uint4 ring[NST * STAGE / 16];
   __shared__ int s_item;
   __shared__ uint32_t s_bits[128 * G];  // per row of the group: 64 bitmap words of 64 bits
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
   const int qg = w >> 1, w2 = w & 1;    // query block of the group, half of the block
   const int nw = (a.n_blk + 63) >> 6;   // bitmap words in use (n_blk <= 4096)
   // blocks with all 64 positions valid (no key mask needed), one word per lane
@@ -260,7 +265,7 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
       const int J = curJ;
       const char* ksrc = kbase + ((int64_t)J * 64 + 32 * u) * D * 2;
       const char* vsrc = vbase + (int64_t)J * 64 * D * 2 + u * HALF;
-      char* dst = (char*)ring + (issued % NST) * STAGE;
+      const uint32_t dst = lds_addr(ring) + (issued % NST) * STAGE;
 #pragma unroll
       for (int j = 0; j < LPW; ++j) {
         const int i = NW * j + w;
@@ -525,8 +530,8 @@ int attn_group() {
 
 int attn_stages() {
   const char* v = getenv("FVA_ATTN_STAGES");
-  int n = v ? atoi(v) : 3;
-  if (n < 2 || n > 4) n = 3;
+  int n = v ? atoi(v) : 4;
+  if (n < 2 || n > 4) n = 4;
   return n;
 }
 
