@@ -83,7 +83,7 @@ def cpu_baseline(w, q, k, v, n_heads, p_head):
     t0 = time.perf_counter()
     for b, h in pairs:
         sl = lambda a: synth.to_f64(a[b:b + 1, :, h:h + 1, :], w.dtype)
-        O.run(sl(q), sl(k), sl(v), opl, float(p_head[b * w.H + h]), w.k_min, "none")
+        O.run(sl(q), sl(k), sl(v), opl, float(p_head[h]), w.k_min, "none")
     dt = time.perf_counter() - t0
     scale = (w.B * w.H) / len(pairs)
     return {"value": round(dt * scale * 1e3, 1), "unit": "ms/call", "cores": int(blas_threads),
