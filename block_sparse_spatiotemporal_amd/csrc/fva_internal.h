@@ -40,6 +40,7 @@ struct fva_plan_s {
   uint64_t* rowmask;  // [n_rows*nw] kept-block bitmask per row
   int32_t* headcnt;   // [B*H]
   int32_t* deficit;   // [B*H] slack blocks to add per head
+  int32_t* headoff;   // [B*H] first CSR entry of each head
   uint64_t* slack_thr;// [B*H]
   int32_t* worklist;  // [n_rows] attention rows in schedule order
   int32_t* counters;  // [64] work-queue cursor and misc counters

@@ -84,30 +84,47 @@ __device__ __forceinline__ int vt_slot_key(int s) {
   return 16 * c + 8 * (j >> 2) + 4 * g + (j & 3);
 }
 
-// One workgroup per (b, h, block): gather the block's 64 rows into LDS, then
-// write the two [D][32] halves.  T is the element type (2 or 4 bytes).
+// One workgroup per (b, h, block).  The block's 64 rows come in as 16-byte
+// chunks into an LDS tile (rows padded by one chunk); each 16-byte output
+// chunk of the two [D][32] halves (one d, E consecutive key slots) is then
+// gathered from the tile and written with one 16-byte store.  T is the
+// element type (2 or 4 bytes).
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void k_permute_vt(const T* __restrict__ src, T* __restrict__ dst,
                                                          const int32_t* __restrict__ perm,
                                                          int64_t n_tok, int heads, int n_blk) {
-  constexpr int kStride = D + (sizeof(T) == 2 ? 2 : 1);   // odd word stride between LDS rows
-  __shared__ T tile[64 * kStride];
+  constexpr int E = 16 / sizeof(T);        // elements per 16-byte chunk
+  constexpr int CPR = D / E;               // chunks per row
+  constexpr int RS = (CPR + 1) * E;        // tile row stride in elements
+  constexpr int NCH = 64 * CPR;            // chunks per block, in and out
+  constexpr int OPD = 32 / E;              // output chunks per d row of a half
+  __shared__ uint4 tile16[64 * (CPR + 1)];
+  const T* tile = (const T*)tile16;
   const int blk = blockIdx.x;
   const int bh = blockIdx.y;
   const int b = bh / heads, h = bh - b * heads;
-  // load: 64 rows x D elements, one element per thread-iteration (small block)
-  for (int e = threadIdx.x; e < 64 * D; e += kThreads) {
-    const int key = e / D, d = e - key * D;
+  const uint4* src16 = (const uint4*)src;
+#pragma unroll
+  for (int e = threadIdx.x; e < NCH; e += kThreads) {
+    const int key = e / CPR, c = e - key * CPR;
     const int tok = perm[(int64_t)blk * 64 + key];
-    tile[key * kStride + d] = tok >= 0 ? src[(((int64_t)b * n_tok + tok) * heads + h) * D + d] : T(0);
+    tile16[key * (CPR + 1) + c] =
+        tok >= 0 ? src16[(((int64_t)b * n_tok + tok) * heads + h) * CPR + c] : make_uint4(0, 0, 0, 0);
   }
   __syncthreads();
-  T* out = dst + ((int64_t)bh * n_blk + blk) * 64 * D;
-  for (int e = threadIdx.x; e < 64 * D; e += kThreads) {
-    const int half = e / (32 * D);
-    const int rem = e - half * 32 * D;
-    const int d = rem >> 5, s = rem & 31;
-    out[e] = tile[(32 * half + vt_slot_key(s)) * kStride + d];
+  uint4* out = (uint4*)(dst + ((int64_t)bh * n_blk + blk) * 64 * D);
+#pragma unroll
+  for (int o = threadIdx.x; o < NCH; o += kThreads) {
+    const int half = o / (D * OPD);
+    const int rem = o - half * (D * OPD);
+    const int d = rem / OPD, s0 = (rem - d * OPD) * E;
+    union {
+      T e[E];
+      uint4 v;
+    } u;
+#pragma unroll
+    for (int i = 0; i < E; ++i) u.e[i] = tile[(32 * half + vt_slot_key(s0 + i)) * RS + d];
+    out[o] = u.v;
   }
 }
 

@@ -175,6 +175,7 @@ static void layout_workspace(const fva_plan_desc* d, const fva_plan_info& in, si
   offs[15] = c.take(sizeof(int32_t) * 64);                               // counters
   offs[16] = c.take(sizeof(float) * bh * in.n_blk * in.n_blk);           // sbuf
   offs[17] = c.take(sizeof(uint64_t) * 64);                              // blk_full
+  offs[18] = c.take(sizeof(int32_t) * bh);                               // headoff
   *total = c.off;
 }
 
@@ -253,7 +254,7 @@ extern "C" int fva_plan_dims(const fva_plan_desc* desc, fva_plan_info* info) {
   if (!info) return fva_fail(FVA_EINVAL, "info is NULL");
   int rc = validate(desc, info);
   if (rc) return rc;
-  size_t offs[18], total;
+  size_t offs[19], total;
   layout_workspace(desc, *info, offs, &total);
   info->workspace_bytes = (int64_t)total;
   return FVA_OK;
@@ -278,7 +279,7 @@ extern "C" int fva_plan_create(fva_plan_t* out, const fva_plan_desc* desc, hipSt
   fva_plan_info in;
   int rc = validate(desc, &in);
   if (rc) return rc;
-  size_t offs[18], total;
+  size_t offs[19], total;
   layout_workspace(desc, in, offs, &total);
   in.workspace_bytes = (int64_t)total;
 
@@ -324,6 +325,7 @@ extern "C" int fva_plan_create(fva_plan_t* out, const fva_plan_desc* desc, hipSt
   p->counters = (int32_t*)(b + offs[15]);
   p->sbuf = (float*)(b + offs[16]);
   p->blk_full = (uint64_t*)(b + offs[17]);
+  p->headoff = (int32_t*)(b + offs[18]);
 
   // Synchronous upload from pageable memory: the tables are small and this
   // happens once per plan, outside any timed path.

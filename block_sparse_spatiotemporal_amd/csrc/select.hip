@@ -159,7 +159,18 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, 
     }
   }
   const double* kb = kbar + (int64_t)bh * nkeys * D + QD * g;
-  double* yrow = y + ((int64_t)bh * n_blk + min(qi, n_blk - 1)) * n_blk;
+  // Logits go out through a per-wave LDS tile of 16 query rows x 64 block
+  // columns, written back as whole 512-byte row pieces.
+  constexpr int TPF = SUB ? 32 : 4;   // key tiles per flush (64 block columns)
+  __shared__ double yt[4][16][65];
+  double* yw = y + ((int64_t)bh * n_blk + q0) * n_blk;
+  auto flush = [&](int kt) {
+    wave_sync_lds();
+    const int j = (kt / TPF) * 64 + lane;
+    for (int q = 0; q < 16 && q0 + q < n_blk; ++q)
+      if (j < n_blk) yw[(int64_t)q * n_blk + j] = yt[w][q][lane];
+    wave_sync_lds();
+  };
   double m_run = -INFINITY, s_run = 0.0;
   for (int kt = 0; kt < ntiles; ++kt) {
     const int kidx = kt * 16 + l16;
@@ -189,13 +200,8 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, 
         s_run = s_run * exp(m_run - m_new) + add;
         m_run = m_new;
       }
-      if (qvalid) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = kt * 16 + g + 4 * i;
-          if (j < n_blk) yrow[j] = yv[i];
-        }
-      }
+      for (int i = 0; i < 4; ++i) yt[w][l16][(kt % TPF) * 16 + g + 4 * i] = yv[i];
     } else {
       // sub-key m = g + 4*i of the tile is sub-block m%8 of block kt*2 + m/8:
       // acc[2*b2] and acc[2*b2+1] are sub-blocks g and g+4 of block kt*2+b2.
@@ -224,11 +230,12 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, 
         s_run = s_run * exp(m_run - m_new) + exp(y0 - m_new) + exp(y1 - m_new);
         m_run = m_new;
       }
-      if (qvalid && g == 0) {
-        if (kt * 2 < n_blk) yrow[kt * 2] = yb[0];
-        if (kt * 2 + 1 < n_blk) yrow[kt * 2 + 1] = yb[1];
+      if (g == 0) {
+        yt[w][l16][(kt % TPF) * 2] = yb[0];
+        yt[w][l16][(kt % TPF) * 2 + 1] = yb[1];
       }
     }
+    if (kt % TPF == TPF - 1 || kt == ntiles - 1) flush(kt);
   }
   // merge (max, sum) over the four lane groups that share query l16
 #pragma unroll
@@ -271,10 +278,10 @@ __global__ __launch_bounds__(256) void k_select(const double* __restrict__ z, co
 
   uint32_t bits[NI];
   {
-    double m = 0.0, sum = 1.0;
+    double m = 0.0, inv = 1.0;
     if (!scores_in) {
       const double2 st = rowstat[r];
-      m = st.x, sum = st.y;
+      m = st.x, inv = 1.0 / st.y;
     }
     const double* zr = z + r * n;
     const float* sr = scores_in ? scores_in + r * n : nullptr;
@@ -284,7 +291,7 @@ __global__ __launch_bounds__(256) void k_select(const double* __restrict__ z, co
       const int j = lane + 64 * i;
       bits[i] = 0;
       if (j < n) {
-        const float s = sr ? sr[j] : (float)(exp(zr[j] - m) / sum);
+        const float s = sr ? sr[j] : (float)(exp(zr[j] - m) * inv);
         if (so) so[j] = s;
         bits[i] = clamp_bits(s);
       }
@@ -543,47 +550,74 @@ __global__ __launch_bounds__(256) void k_slack_apply(const float* __restrict__ S
 }
 
 // ------------------------------------------------------------------ CSR
-// Exclusive scan of kept counts into row_ptr (one workgroup) and per-head
-// totals.
-__global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ cnt, int64_t n_rows,
-                                               int32_t* __restrict__ row_ptr, int32_t* __restrict__ head_nnz,
-                                               int n_blk, int n_bh) {
-  __shared__ int part[1024];
-  const int tid = threadIdx.x;
-  const int64_t per = (n_rows + 1023) / 1024;
-  const int64_t b0 = min<int64_t>(tid * per, n_rows), b1 = min<int64_t>(b0 + per, n_rows);
-  int s = 0;
-  for (int64_t i = b0; i < b1; ++i) s += cnt[i];
-  part[tid] = s;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    const int v = tid >= o ? part[tid - o] : 0;
+// Row pointers in two levels: k_scan_rows writes each head's exclusive scan
+// of its rows' kept counts (head-local) and the head's total; k_scan_heads
+// turns the totals into head offsets, head_nnz and row_ptr[n_rows]; k_emit
+// adds the head offset, writes the final row_ptr[r] and the column ids.
+__global__ __launch_bounds__(1024) void k_scan_rows(const int32_t* __restrict__ cnt, int n_blk,
+                                                    int32_t* __restrict__ row_ptr, int32_t* __restrict__ headcnt) {
+  __shared__ int wsum[16];
+  const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int32_t* c = cnt + (int64_t)bh * n_blk;
+  int32_t* out = row_ptr + (int64_t)bh * n_blk;
+  int carry = 0;
+  for (int base = 0; base < n_blk; base += 1024) {
+    const int i = base + tid;
+    const int v = i < n_blk ? c[i] : 0;
+    const int incl = wave_incl_scan<int>(v, lane);
+    if (lane == 63) wsum[wv] = incl;
     __syncthreads();
-    part[tid] += v;
-    __syncthreads();
-  }
-  int run = part[tid] - s;
-  for (int64_t i = b0; i < b1; ++i) {
-    row_ptr[i] = run;
-    run += cnt[i];
-  }
-  if (tid == 1023) row_ptr[n_rows] = part[1023];
-  if (head_nnz) {
-    for (int bh = tid; bh < n_bh; bh += 1024) {
-      int hs = 0;
-      for (int i = 0; i < n_blk; ++i) hs += cnt[(int64_t)bh * n_blk + i];
-      head_nnz[bh] = hs;
+    int before = 0, total = 0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      before += k < wv ? wsum[k] : 0;
+      total += wsum[k];
     }
+    if (i < n_blk) out[i] = carry + before + incl - v;
+    carry += total;
+    __syncthreads();
   }
+  if (tid == 0) headcnt[bh] = carry;
 }
 
-// Kept-id bitmask -> ascending column indices at row_ptr[r].
-__global__ __launch_bounds__(256) void k_emit(const uint64_t* __restrict__ rowmask, const int32_t* __restrict__ row_ptr,
-                                              int32_t* __restrict__ col_idx, int nw, int64_t n_rows) {
+__global__ __launch_bounds__(1024) void k_scan_heads(const int32_t* __restrict__ headcnt, int n_bh,
+                                                     int32_t* __restrict__ headoff, int32_t* __restrict__ head_nnz,
+                                                     int32_t* __restrict__ row_ptr, int64_t n_rows) {
+  __shared__ int wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int carry = 0;
+  for (int base = 0; base < n_bh; base += 1024) {
+    const int i = base + tid;
+    const int v = i < n_bh ? headcnt[i] : 0;
+    const int incl = wave_incl_scan<int>(v, lane);
+    if (lane == 63) wsum[wv] = incl;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      before += k < wv ? wsum[k] : 0;
+      total += wsum[k];
+    }
+    if (i < n_bh) {
+      headoff[i] = carry + before + incl - v;
+      if (head_nnz) head_nnz[i] = v;
+    }
+    carry += total;
+    __syncthreads();
+  }
+  if (tid == 0) row_ptr[n_rows] = carry;
+}
+
+// Kept-id bitmask -> ascending column indices at row_ptr[r] (after adding
+// the head offset to the head-local pointer).
+__global__ __launch_bounds__(256) void k_emit(const uint64_t* __restrict__ rowmask, int32_t* __restrict__ row_ptr,
+                                              const int32_t* __restrict__ headoff, int32_t* __restrict__ col_idx,
+                                              int nw, int n_blk, int64_t n_rows) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int64_t r = (int64_t)blockIdx.x * 4 + wv;
   if (r >= n_rows) return;
-  int base = row_ptr[r];
+  int base = row_ptr[r] + headoff[r / n_blk];
+  if (lane == 0) row_ptr[r] = base;
   const uint64_t below = (1ull << lane) - 1;
   for (int i = 0; i < nw; ++i) {
     const uint64_t m = rowmask[r * nw + i];
@@ -658,7 +692,9 @@ extern "C" int fva_select(fva_plan_t plan, const void* q_perm, const void* k_per
     if (d.head_dim == 128) launch_score<128>(plan, stream);
     else launch_score<64>(plan, stream);
   }
-  float* s_out = scores_out ? scores_out : (scores_in ? nullptr : plan->sbuf);
+  // fp32 scores are kept in the workspace only when the slack fill reads them
+  float* s_out = scores_out ? scores_out
+                            : (scores_in || slack_mode != FVA_SLACK_MEDIAN ? nullptr : plan->sbuf);
   const float* s_read = scores_in ? scores_in : s_out;
   const unsigned sel_grid = (unsigned)((in.n_rows + 3) / 4);
   const int ni = (in.n_blk + 63) / 64;
@@ -681,9 +717,11 @@ extern "C" int fva_select(fva_plan_t plan, const void* q_perm, const void* k_per
     hipLaunchKernelGGL(k_slack_apply, dim3(sel_grid), dim3(256), 0, stream, s_read, plan->rowmask,
                        plan->rowcnt, plan->nw, in.n_blk, in.n_rows, plan->deficit, plan->slack_thr);
   }
-  hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, stream, plan->rowcnt, in.n_rows, row_ptr, head_nnz,
-                     in.n_blk, n_bh);
-  hipLaunchKernelGGL(k_emit, dim3(sel_grid), dim3(256), 0, stream, plan->rowmask, row_ptr, col_idx, plan->nw,
-                     in.n_rows);
+  hipLaunchKernelGGL(k_scan_rows, dim3(n_bh), dim3(1024), 0, stream, plan->rowcnt, in.n_blk, row_ptr,
+                     plan->headcnt);
+  hipLaunchKernelGGL(k_scan_heads, dim3(1), dim3(1024), 0, stream, plan->headcnt, n_bh, plan->headoff, head_nnz,
+                     row_ptr, in.n_rows);
+  hipLaunchKernelGGL(k_emit, dim3(sel_grid), dim3(256), 0, stream, plan->rowmask, row_ptr, plan->headoff, col_idx,
+                     plan->nw, in.n_blk, in.n_rows);
   return fva_after_launch(stream, "fva_select");
 }
