@@ -41,7 +41,9 @@ struct fva_plan_s {
   int32_t* headcnt;   // [B*H]
   int32_t* deficit;   // [B*H] slack blocks to add per head
   int32_t* headoff;   // [B*H] first CSR entry of each head
-  uint64_t* slack_thr;// [B*H]
+  uint64_t* slack_thr;// [B*H] slack key threshold (radix prefix while it is built)
+  uint32_t* slack_hist;// [B*H][256] digit histogram of the slack radix select (kept zero between calls)
+  int32_t* slack_need; // [B*H] pairs still to place below the current prefix
   int32_t* worklist;  // [n_rows] attention rows in schedule order
   int32_t* counters;  // [64] work-queue cursor and misc counters
 

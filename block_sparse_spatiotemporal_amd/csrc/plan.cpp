@@ -176,6 +176,8 @@ static void layout_workspace(const fva_plan_desc* d, const fva_plan_info& in, si
   offs[16] = c.take(sizeof(float) * bh * in.n_blk * in.n_blk);           // sbuf
   offs[17] = c.take(sizeof(uint64_t) * 64);                              // blk_full
   offs[18] = c.take(sizeof(int32_t) * bh);                               // headoff
+  offs[19] = c.take(sizeof(uint32_t) * 256 * bh);                        // slack_hist
+  offs[20] = c.take(sizeof(int32_t) * bh);                               // slack_need
   *total = c.off;
 }
 
@@ -254,7 +256,7 @@ extern "C" int fva_plan_dims(const fva_plan_desc* desc, fva_plan_info* info) {
   if (!info) return fva_fail(FVA_EINVAL, "info is NULL");
   int rc = validate(desc, info);
   if (rc) return rc;
-  size_t offs[19], total;
+  size_t offs[21], total;
   layout_workspace(desc, *info, offs, &total);
   info->workspace_bytes = (int64_t)total;
   return FVA_OK;
@@ -279,7 +281,7 @@ extern "C" int fva_plan_create(fva_plan_t* out, const fva_plan_desc* desc, hipSt
   fva_plan_info in;
   int rc = validate(desc, &in);
   if (rc) return rc;
-  size_t offs[19], total;
+  size_t offs[21], total;
   layout_workspace(desc, in, offs, &total);
   in.workspace_bytes = (int64_t)total;
 
@@ -326,6 +328,8 @@ extern "C" int fva_plan_create(fva_plan_t* out, const fva_plan_desc* desc, hipSt
   p->sbuf = (float*)(b + offs[16]);
   p->blk_full = (uint64_t*)(b + offs[17]);
   p->headoff = (int32_t*)(b + offs[18]);
+  p->slack_hist = (uint32_t*)(b + offs[19]);
+  p->slack_need = (int32_t*)(b + offs[20]);
 
   // Synchronous upload from pageable memory: the tables are small and this
   // happens once per plan, outside any timed path.
@@ -343,6 +347,8 @@ extern "C" int fva_plan_create(fva_plan_t* out, const fva_plan_desc* desc, hipSt
     if (!rc) rc = fva_hip_check(hipMemcpy(p->sub_cnt, t.sub_cnt.data(), sizeof(int32_t) * t.sub_cnt.size(), hipMemcpyHostToDevice), "upload sub_cnt");
   }
   if (!rc) rc = fva_hip_check(hipMemsetAsync(p->counters, 0, sizeof(int32_t) * 64, stream), "clear counters");
+  if (!rc)
+    rc = fva_hip_check(hipMemsetAsync(p->slack_hist, 0, sizeof(uint32_t) * 256 * (size_t)desc->batch * desc->heads, stream), "clear slack histogram");
   if (!rc) rc = fva_hip_check(hipStreamSynchronize(stream), "plan upload sync");
   if (rc) {
     (void)hipFree(p->dev_base);

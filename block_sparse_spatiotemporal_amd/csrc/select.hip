@@ -472,51 +472,66 @@ __global__ __launch_bounds__(1024) void k_slack_target(const int32_t* __restrict
 }
 
 // Per deficient head: the key (score bits << 32 | ~(I*n + J)) of the d-th best
-// unselected pair, by an 8-level MSD radix select over all n^2 pairs.
-__global__ __launch_bounds__(1024) void k_slack_thresh(const float* __restrict__ S,
-                                                       const uint64_t* __restrict__ rowmask, int nw,
-                                                       int n_blk, const int32_t* __restrict__ deficit,
-                                                       uint64_t* __restrict__ slack_thr) {
-  __shared__ unsigned int hist[256];
-  __shared__ uint64_t prefix;
-  __shared__ int need;
-  const int bh = blockIdx.x;
-  const int d = deficit[bh];
-  if (d <= 0) return;
+// unselected pair, by an 8-level MSD radix select over all n^2 pairs.  Each
+// level is two launches: k_slack_hist spreads a head's pairs over many
+// workgroups (LDS histogram of the level's 8-bit digit among the pairs that
+// match the prefix so far, merged into the head's global histogram), then
+// k_slack_pick finds the digit where the count crosses the remaining need.
+constexpr int kSlackChunk = 16384;   // pairs per histogram workgroup
+
+__global__ __launch_bounds__(256) void k_slack_hist(const float* __restrict__ S,
+                                                    const uint64_t* __restrict__ rowmask, int nw, int n_blk,
+                                                    const int32_t* __restrict__ deficit,
+                                                    const uint64_t* __restrict__ prefix, int level,
+                                                    uint32_t* __restrict__ hist) {
+  __shared__ unsigned int h[256];
+  const int bh = blockIdx.y;
+  if (deficit[bh] <= 0) return;
+  const int shift = 56 - 8 * level;
+  const uint64_t pre = prefix[bh];
+  h[threadIdx.x] = 0;
+  __syncthreads();
   const int64_t n = n_blk, nn = n * n;
   const float* Sh = S + (int64_t)bh * nn;
   const uint64_t* mh = rowmask + (int64_t)bh * n * nw;
+  const int64_t e0 = (int64_t)blockIdx.x * kSlackChunk, e1 = min<int64_t>(e0 + kSlackChunk, nn);
+  for (int64_t e = e0 + threadIdx.x; e < e1; e += 256) {
+    const int64_t I = e / n, J = e - I * n;
+    if (mh[I * nw + (J >> 6)] >> (J & 63) & 1) continue;
+    const uint64_t key = ((uint64_t)clamp_bits(Sh[e]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+    if (level > 0 && (key >> (shift + 8)) != (pre >> (shift + 8))) continue;
+    atomicAdd(&h[(key >> shift) & 0xFF], 1u);
+  }
+  __syncthreads();
+  const unsigned v = h[threadIdx.x];
+  if (v) atomicAdd(&hist[bh * 256 + threadIdx.x], v);
+}
+
+// Per head: keep the digit where the count of larger keys crosses the need,
+// extend the prefix, and clear the histogram for the next level.
+__global__ __launch_bounds__(256) void k_slack_pick(uint32_t* __restrict__ hist, const int32_t* __restrict__ deficit,
+                                                    int32_t* __restrict__ need, uint64_t* __restrict__ prefix,
+                                                    int level) {
+  __shared__ unsigned int h[256];
+  const int bh = blockIdx.x;
+  if (deficit[bh] <= 0) return;
+  h[threadIdx.x] = hist[bh * 256 + threadIdx.x];
+  hist[bh * 256 + threadIdx.x] = 0;
+  __syncthreads();
   if (threadIdx.x == 0) {
-    prefix = 0;
-    need = d;
-  }
-  for (int level = 0; level < 8; ++level) {
     const int shift = 56 - 8 * level;
-    for (int t = threadIdx.x; t < 256; t += 1024) hist[t] = 0;
-    __syncthreads();
-    const uint64_t pre = prefix;
-    for (int64_t e = threadIdx.x; e < nn; e += 1024) {
-      const int64_t I = e / n, J = e - I * n;
-      if (mh[I * nw + (J >> 6)] >> (J & 63) & 1) continue;
-      const uint64_t key = ((uint64_t)clamp_bits(Sh[e]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
-      if (level > 0 && (key >> (shift + 8)) != (pre >> (shift + 8))) continue;
-      atomicAdd(&hist[(key >> shift) & 0xFF], 1u);
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      int acc = 0;
-      for (int b = 255; b >= 0; --b) {
-        if (acc + (int)hist[b] >= need) {
-          prefix = pre | ((uint64_t)b << shift);
-          need -= acc;
-          break;
-        }
-        acc += hist[b];
+    const int nd = level == 0 ? deficit[bh] : need[bh];
+    const uint64_t pre = level == 0 ? 0 : prefix[bh];
+    int acc = 0;
+    for (int b = 255; b >= 0; --b) {
+      if (acc + (int)h[b] >= nd) {
+        prefix[bh] = pre | ((uint64_t)b << shift);
+        need[bh] = nd - acc;
+        break;
       }
+      acc += h[b];
     }
-    __syncthreads();
   }
-  if (threadIdx.x == 0) slack_thr[bh] = prefix;
 }
 
 // Add the pairs at or above a deficient head's threshold to its rows.
@@ -712,8 +727,13 @@ extern "C" int fva_select(fva_plan_t plan, const void* q_perm, const void* k_per
   if (slack_mode == FVA_SLACK_MEDIAN) {
     hipLaunchKernelGGL(k_slack_target, dim3(1), dim3(1024), 0, stream, plan->rowcnt, in.n_blk, n_bh,
                        plan->headcnt, plan->deficit);
-    hipLaunchKernelGGL(k_slack_thresh, dim3(n_bh), dim3(1024), 0, stream, s_read, plan->rowmask, plan->nw,
-                       in.n_blk, plan->deficit, plan->slack_thr);
+    const unsigned chunks = (unsigned)(((int64_t)in.n_blk * in.n_blk + kSlackChunk - 1) / kSlackChunk);
+    for (int level = 0; level < 8; ++level) {
+      hipLaunchKernelGGL(k_slack_hist, dim3(chunks, n_bh), dim3(256), 0, stream, s_read, plan->rowmask, plan->nw,
+                         in.n_blk, plan->deficit, plan->slack_thr, level, plan->slack_hist);
+      hipLaunchKernelGGL(k_slack_pick, dim3(n_bh), dim3(256), 0, stream, plan->slack_hist, plan->deficit,
+                         plan->slack_need, plan->slack_thr, level);
+    }
     hipLaunchKernelGGL(k_slack_apply, dim3(sel_grid), dim3(256), 0, stream, s_read, plan->rowmask,
                        plan->rowcnt, plan->nw, in.n_blk, in.n_rows, plan->deficit, plan->slack_thr);
   }
