@@ -143,8 +143,7 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, 
   const int bh = blockIdx.y;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, l16 = lane & 15;
-  const int q0 = blockIdx.x * 64 + w * 16;
-  if (q0 >= n_blk) return;    // whole wave idle; no workgroup barrier below
+  const int q0 = blockIdx.x * 64 + w * 16;   // a wave past the last query still helps load keys
   const int qi = q0 + l16;
   const bool qvalid = qi < n_blk;
   const int nkeys = SUB ? n_blk * 8 : n_blk;
@@ -158,7 +157,42 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, 
       qv[2 * c] = t.x, qv[2 * c + 1] = t.y;
     }
   }
-  const double* kb = kbar + (int64_t)bh * nkeys * D + QD * g;
+  // Key tiles (16 keys x D) are shared by the workgroup's four waves through
+  // a double-buffered LDS tile: each thread prefetches its share of tile
+  // kt+1 into registers while tile kt is multiplied, then stores it.
+  constexpr int KS = D + 2;                        // padded LDS row (doubles)
+  constexpr int KV = 16 * D / 2 / 256;             // double2 per thread per tile
+  __shared__ double ks_lds[2][16][KS];
+  const double* kh = kbar + (int64_t)bh * nkeys * D;
+  double2 kn[KV];
+  auto kfetch = [&](int kt) {
+#pragma unroll
+    for (int v = 0; v < KV; ++v) {
+      const int e = threadIdx.x + 256 * v;         // double2 index within the tile
+      const int r = e / (D / 2), d2 = e - r * (D / 2);
+      kn[v] = *(const double2*)(kh + (int64_t)min(kt * 16 + r, nkeys - 1) * D + 2 * d2);
+    }
+  };
+  auto kstore = [&](int buf) {
+#pragma unroll
+    for (int v = 0; v < KV; ++v) {
+      const int e = threadIdx.x + 256 * v;
+      const int r = e / (D / 2), d2 = e - r * (D / 2);
+      *(double2*)&ks_lds[buf][r][2 * d2] = kn[v];
+    }
+  };
+  // non-empty sub-blocks of every block, one byte per block (bit s: sub-block s)
+  __shared__ uint8_t sub_ok[SUB ? FVA_MAX_NBLK : 1];
+  if (SUB)
+    for (int j = threadIdx.x; j < n_blk; j += 256) {
+      uint32_t mbits = 0;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) mbits |= (sub_cnt[j * 8 + t] > 0 ? 1u : 0u) << t;
+      sub_ok[j] = (uint8_t)mbits;
+    }
+  kfetch(0);
+  kstore(0);
+  __syncthreads();
   // Logits go out through a per-wave LDS tile of 16 query rows x 64 block
   // columns, written back as whole 512-byte row pieces.
   constexpr int TPF = SUB ? 32 : 4;   // key tiles per flush (64 block columns)
@@ -173,8 +207,8 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, 
   };
   double m_run = -INFINITY, s_run = 0.0;
   for (int kt = 0; kt < ntiles; ++kt) {
-    const int kidx = kt * 16 + l16;
-    const double2* ks = (const double2*)(kb + (int64_t)min(kidx, nkeys - 1) * D);
+    if (kt + 1 < ntiles) kfetch(kt + 1);
+    const double2* ks = (const double2*)&ks_lds[kt & 1][l16][QD * g];
     f64x4 acc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int c = 0; c < QD / 2; ++c) {
@@ -192,13 +226,13 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, 
         yv[i] = j < n_blk ? acc[i] * scale : -INFINITY;
         tmax = fmax(tmax, yv[i]);
       }
-      const double m_new = fmax(m_run, tmax);
-      if (m_new > -INFINITY) {
-        double add = 0.0;
+      if (tmax > m_run) {   // rescale only when the running max grows
+        s_run *= exp(m_run - tmax);
+        m_run = tmax;
+      }
+      if (m_run > -INFINITY) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) add += exp(yv[i] - m_new);
-        s_run = s_run * exp(m_run - m_new) + add;
-        m_run = m_new;
+        for (int i = 0; i < 4; ++i) s_run += exp(yv[i] - m_run);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) yt[w][l16][(kt % TPF) * 16 + g + 4 * i] = yv[i];
@@ -209,33 +243,35 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, 
 #pragma unroll
       for (int b2 = 0; b2 < 2; ++b2) {
         const int blk = kt * 2 + b2;
-        const int bc = min(blk, n_blk - 1) * 8;
-        const double v0 = (blk < n_blk && sub_cnt[bc + g] > 0) ? acc[2 * b2] * scale : -INFINITY;
-        const double v1 = (blk < n_blk && sub_cnt[bc + g + 4] > 0) ? acc[2 * b2 + 1] * scale : -INFINITY;
+        const uint32_t ok = blk < n_blk ? sub_ok[blk] : 0u;
+        const double v0 = (ok >> g & 1) ? acc[2 * b2] * scale : -INFINITY;
+        const double v1 = (ok >> (g + 4) & 1) ? acc[2 * b2 + 1] * scale : -INFINITY;
+        // log-sum-exp over the block's 8 sub-blocks (2 per lane, 4 lane groups):
+        // the max first, then one exponential per sub-block and one log
         double c = fmax(v0, v1);
+        c = fmax(c, __shfl_xor(c, 16));
+        c = fmax(c, __shfl_xor(c, 32));
         double e = c > -INFINITY ? exp(v0 - c) + exp(v1 - c) : 0.0;
-#pragma unroll
-        for (int o = 16; o <= 32; o <<= 1) {
-          const double c2 = __shfl_xor(c, o), e2 = __shfl_xor(e, o);
-          const double cc = fmax(c, c2);
-          e = (c > -INFINITY ? e * exp(c - cc) : 0.0) + (c2 > -INFINITY ? e2 * exp(c2 - cc) : 0.0);
-          c = cc;
-        }
+        e += __shfl_xor(e, 16);
+        e += __shfl_xor(e, 32);
         yb[b2] = c > -INFINITY ? c + log(e) : -INFINITY;
       }
-      // every lane group now holds both block logits; group 0 counts and writes them
-      const double y0 = g == 0 ? yb[0] : -INFINITY, y1 = g == 0 ? yb[1] : -INFINITY;
-      const double m_new = fmax(m_run, fmax(y0, y1));
-      if (m_new > -INFINITY) {
-        s_run = s_run * exp(m_run - m_new) + exp(y0 - m_new) + exp(y1 - m_new);
-        m_run = m_new;
+      // every lane group now holds both block logits; for the row statistics
+      // group 0 counts block kt*2 and group 1 block kt*2+1 (merged at the end)
+      const double yo = g == 0 ? yb[0] : (g == 1 ? yb[1] : -INFINITY);
+      if (yo > m_run) {
+        s_run *= exp(m_run - yo);
+        m_run = yo;
       }
+      if (yo > -INFINITY) s_run += exp(yo - m_run);
       if (g == 0) {
         yt[w][l16][(kt % TPF) * 2] = yb[0];
         yt[w][l16][(kt % TPF) * 2 + 1] = yb[1];
       }
     }
     if (kt % TPF == TPF - 1 || kt == ntiles - 1) flush(kt);
+    if (kt + 1 < ntiles) kstore((kt + 1) & 1);
+    __syncthreads();
   }
   // merge (max, sum) over the four lane groups that share query l16
 #pragma unroll
