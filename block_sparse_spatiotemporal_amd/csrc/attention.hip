@@ -134,6 +134,17 @@ __device__ __forceinline__ void barrier_no_fence() {
   asm volatile("" ::: "memory");
 }
 
+// Combine lane l with lane l^32 without an LDS round trip: v_permlane32_swap
+// of x with itself leaves x[l%32] in one result and x[l%32 + 32] in the other.
+__device__ __forceinline__ float xhalf_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Wave-uniform reads of read-only metadata through the scalar cache.
 template <typename T>
 __device__ __forceinline__ T sload(const T* p, int64_t i) {
@@ -339,7 +350,7 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
 #pragma unroll
       for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s[i]), s[i + 1]);
       mx = fmaxf(mx, s[15]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+      mx = xhalf_max(mx) * sl2;
       if (__ballot(mx > m_run + kLazy)) {   // raise the running max (first step always)
         const float m_new = fmaxf(m_run, mx);
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -368,7 +379,7 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
       }
     }
     if (has_row) {
-      const float l_tot = l_run + __shfl_xor(l_run, 32);
+      const float l_tot = xhalf_sum(l_run);
       const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
       const bool qvalid = sload(a.blk_mask, I) >> (32 * w2 + l32) & 1;
       uint16_t* orow = (uint16_t*)a.o + (head + (int64_t)I * 64 + 32 * w2 + l32) * D;
