@@ -69,32 +69,46 @@ __device__ __forceinline__ void wave_sync_lds() {
 // ------------------------------------------------------------------ pool
 // Mean of the 64 rows of one block (pads are zero rows, so the sum over all
 // rows is the sum over valid rows), divided by the valid count, in fp64.
-// One wave per (block, b*h, tensor); lanes own 16-byte column chunks of
-// interleaved rows.
+// One wave per (block, b*h, tensor), four blocks per workgroup; lanes own
+// 16-byte column chunks of interleaved rows.
 template <typename T, int D>
-__global__ __launch_bounds__(64) void k_pool(const T* __restrict__ q, const T* __restrict__ k,
-                                             double* __restrict__ qbar, double* __restrict__ kbar,
-                                             const int32_t* __restrict__ blk_cnt, int n_blk, int64_t n_pad) {
+__global__ __launch_bounds__(256) void k_pool(const T* __restrict__ q, const T* __restrict__ k,
+                                              double* __restrict__ qbar, double* __restrict__ kbar,
+                                              const int32_t* __restrict__ blk_cnt, int n_blk, int64_t n_pad) {
   constexpr int EPC = 16 / sizeof(T);   // elements per 16-byte chunk
   constexpr int CPR = D / EPC;          // chunks per row
   constexpr int RG = 64 / CPR;          // row groups
-  __shared__ double part[RG][D];
-  const int blk = blockIdx.x, bh = blockIdx.y;
+  __shared__ double part_all[4][RG][D];
+  const int wv = threadIdx.x >> 6;
+  const int blk = blockIdx.x * 4 + wv, bh = blockIdx.y;
+  if (blk >= n_blk) return;             // whole wave; only wave-level syncs below
+  double (*part)[D] = part_all[wv];
   const T* src = (blockIdx.z == 0 ? q : k) + ((int64_t)bh * n_pad + (int64_t)blk * 64) * D;
   double* dst = (blockIdx.z == 0 ? qbar : kbar) + ((int64_t)bh * n_blk + blk) * D;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int ch = lane % CPR, g = lane / CPR;
   double acc[EPC];
 #pragma unroll
   for (int e = 0; e < EPC; ++e) acc[e] = 0.0;
-  for (int r = g; r < 64; r += RG) {
-    const T* row = src + (int64_t)r * D + ch * EPC;
+  // 16-byte loads, eight rows in flight per lane before they are summed
+  constexpr int RPL = 64 / RG;          // rows per lane
+  constexpr int BATCH = RPL < 8 ? RPL : 8;
+  const uint4* src16 = (const uint4*)src;
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) acc[e] += (double)ld_elem(row + e);
+  for (int r0 = 0; r0 < RPL; r0 += BATCH) {
+    uint4 v[BATCH];
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i) v[i] = src16[(g + (r0 + i) * RG) * CPR + ch];
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i) {
+      const T* e16 = (const T*)&v[i];
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc[e] += (double)ld_elem(e16 + e);
+    }
   }
 #pragma unroll
   for (int e = 0; e < EPC; ++e) part[g][ch * EPC + e] = acc[e];
-  __syncthreads();
+  wave_sync_lds();
   const double cnt = (double)blk_cnt[blk];
   for (int d = lane; d < D; d += 64) {
     double s = 0.0;
@@ -682,8 +696,8 @@ void launch_pool(fva_plan_t plan, const void* q, const void* k, hipStream_t s) {
   const fva_plan_info& in = plan->info;
   const int bh = plan->desc.batch * plan->desc.heads;
   const bool sub = in.n_sub != 0;
-  dim3 grid(in.n_blk, bh, sub ? 1 : 2);
-  hipLaunchKernelGGL((k_pool<T, D>), grid, dim3(64), 0, s, (const T*)q, (const T*)k, plan->qbar, plan->kbar,
+  dim3 grid((in.n_blk + 3) / 4, bh, sub ? 1 : 2);
+  hipLaunchKernelGGL((k_pool<T, D>), grid, dim3(256), 0, s, (const T*)q, (const T*)k, plan->qbar, plan->kbar,
                      plan->blk_cnt, in.n_blk, in.n_pad);
   if (sub)
     hipLaunchKernelGGL((k_pool_sub<T, D>), dim3(in.n_blk, bh), dim3(64), 0, s, (const T*)k, plan->kbar,

@@ -242,7 +242,8 @@ def test_launch_shapes_bitwise_equal(monkeypatch):
     ref = None
     for group, stages, chunk, sched in [("1", "3", "32", "persistent"), ("2", "2", "16", "plain"),
                                         ("4", "4", "1", "persistent"), ("2", "3", "32", "persistent"),
-                                        ("4", "2", "64", "plain"), ("2", "4", "8", "plain")]:
+                                        ("4", "2", "64", "plain"), ("2", "4", "8", "plain"),
+                                        ("2", "4", "32", "persistent"), ("1", "4", "8", "persistent")]:
         monkeypatch.setenv("FVA_ATTN_GROUP", group)
         monkeypatch.setenv("FVA_ATTN_STAGES", stages)
         monkeypatch.setenv("FVA_ATTN_CHUNK", chunk)
