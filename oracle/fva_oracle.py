@@ -384,3 +384,45 @@ def run(q, k, v, pl: Plan, p_head, k_min: int, slack: str = "none"):
     o_perm = attention(qp, kp, vp, row_ptr, col_idx, pl)
     return dict(q_perm=qp, k_perm=kp, v_perm=vp, qbar=qbar, scores=S, row_ptr=row_ptr,
                 col_idx=col_idx, o_perm=o_perm, o=unpermute(o_perm, pl))
+
+
+# --------------------------------------------------------------------------
+# 3D rotary position encoding with a global time index ([CausalRoPE-SP]
+# "Accelerating Video Generation Inference with Sequential-Parallel 3D
+# Positional Encoding Using a Global Time Index", section 2.2: each chunk of
+# frames uses t_global = t_local + s with its start frame s, so a chunk can be
+# encoded without the rest of the sequence).  Readings (the page gives no
+# split or convention): the D/2 rotation pairs are split as evenly as
+# possible over the (t, h, w) axes, t first; pair p rotates dims (2p, 2p+1);
+# within an axis with P pairs, pair i turns by pos * base**(-i / P).
+def rope_pairs(head_dim: int):
+    """Number of rotation pairs given to the t, h and w axes."""
+    n = head_dim // 2
+    pw = n // 3
+    ph = n // 3
+    return n - ph - pw, ph, pw
+
+
+def rope_angles(grid, head_dim: int, t_offset: int = 0, base: float = 10000.0):
+    """Angle of every rotation pair at every raster token: [N, D/2] (fp64)."""
+    T, Hh, W = grid
+    counts = rope_pairs(head_dim)
+    t, h, w = np.meshgrid(np.arange(T) + t_offset, np.arange(Hh), np.arange(W), indexing="ij")
+    pos = [t.reshape(-1), h.reshape(-1), w.reshape(-1)]
+    cols = []
+    for axis, P in enumerate(counts):
+        inv = base ** (-np.arange(P, dtype=np.float64) / P)
+        cols.append(pos[axis][:, None].astype(np.float64) * inv[None, :])
+    return np.concatenate(cols, axis=1)
+
+
+def rope(x_raster: np.ndarray, grid, t_offset: int = 0, base: float = 10000.0) -> np.ndarray:
+    """Rotate raster [B, N, H, D] fp64 tokens by their 3D position."""
+    D = x_raster.shape[-1]
+    ang = rope_angles(grid, D, t_offset, base)[None, :, None, :]     # [1, N, 1, D/2]
+    c, s = np.cos(ang), np.sin(ang)
+    x0, x1 = x_raster[..., 0::2], x_raster[..., 1::2]
+    out = np.empty_like(x_raster)
+    out[..., 0::2] = x0 * c - x1 * s
+    out[..., 1::2] = x0 * s + x1 * c
+    return out
