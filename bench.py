@@ -170,6 +170,16 @@ def main():
     st_mean = {n: float(x.mean()) for n, x in stage.items()}
     st_med = {n: float(np.median(x)) for n, x in stage.items()}
 
+    # the fused permute + 3D rotary encoding (outside the attention call),
+    # timed alone on Q of the same workload
+    e_r0, e_r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e_r0.record()
+    for _ in range(args.steps):
+        fva.fva_permute_rope(plan, qd, bufs.q, t_offset=3)
+    e_r1.record()
+    torch.cuda.synchronize()
+    rope_ms = e_r0.elapsed_time(e_r1) / args.steps
+
     # one extra, untimed call with per-workgroup stamps for the load balance
     wg = torch.zeros(2 * plan.info.max_wg, dtype=torch.int64, device="cuda")
     fva.fva_attention(plan, bufs.q, bufs.k, bufs.vt, bufs.row_ptr, bufs.col_idx, bufs.o, sched=args.sched,
@@ -230,6 +240,8 @@ def main():
                     "unpermute": round(unperm_bytes / (st_mean["unpermute"] * 1e-3) / 1e9, 1),
                     "peak": PEAK_HBM_GBS},
         "load_balance": balance,
+        "permute_rope_ms": round(rope_ms, 4),
+        "permute_rope_gbs": round(perm_bytes / (rope_ms * 1e-3) / 1e9, 1),
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "kernel": "k_attn_bf16 (fva_attention)",

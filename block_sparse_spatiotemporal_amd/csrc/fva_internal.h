@@ -44,6 +44,7 @@ struct fva_plan_s {
   uint64_t* slack_thr;// [B*H] slack key threshold (radix prefix while it is built)
   uint32_t* slack_hist;// [B*H][256] digit histogram of the slack radix select (kept zero between calls)
   int32_t* slack_need; // [B*H] pairs still to place below the current prefix
+  double2* rope_tab;  // [(T+H+W) * D/2] rotary (cos, sin) of the last fva_permute_rope call
   int32_t* worklist;  // [n_rows] attention rows in schedule order
   int32_t* counters;  // [64] work-queue cursor and misc counters
 

@@ -4,11 +4,35 @@
 // accesses, each 64-token block row-run read and written contiguously.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "fva_internal.h"
 
 namespace {
 
 constexpr int kThreads = 256;
+
+// Element loads/stores for the rotary path: bf16 (uint16 bit patterns) or
+// fp32.  st_val rounds an fp64 value once to the element type.
+__device__ __forceinline__ float ld_val(const uint16_t* p) { return __uint_as_float((uint32_t)(*p) << 16); }
+__device__ __forceinline__ float ld_val(const float* p) { return *p; }
+template <typename T>
+__device__ __forceinline__ T st_val(double v);
+// Correctly rounded fp64 -> bf16 (nearest, ties to even).  f = (float)v is
+// within half an fp32 ulp of v, so the two bf16 values around f, lo (f
+// truncated) and hi (one bf16 ulp further from zero), bracket v's nearest
+// bf16; the distances are exact in fp64.  Infinity and NaN pass through.
+template <>
+__device__ __forceinline__ uint16_t st_val<uint16_t>(double v) {
+  const uint32_t fb = __float_as_uint((float)v);
+  if ((fb & 0x7F800000u) == 0x7F800000u) return (uint16_t)((fb >> 16) | ((fb & 0x7FFFFFu) ? 0x40u : 0u));
+  const uint32_t lo = fb & 0xFFFF0000u, hi = lo + 0x10000u;
+  const double dlo = fabs(v - (double)__uint_as_float(lo)), dhi = fabs(v - (double)__uint_as_float(hi));
+  const uint32_t r = dlo < dhi ? lo : (dhi < dlo ? hi : (((lo >> 16) & 1u) ? hi : lo));
+  return (uint16_t)(r >> 16);
+}
+template <>
+__device__ __forceinline__ float st_val<float>(double v) { return (float)v; }
 constexpr int kUnroll = 4;  // 16-byte chunks per thread per block of work
 
 // x_perm[b,h,pos,:] = x_raster[b, perm[pos], h, :] (or zero for a pad).
@@ -128,6 +152,85 @@ __global__ __launch_bounds__(kThreads) void k_permute_vt(const T* __restrict__ s
   }
 }
 
+// --------------------------------------------------------------- rotary
+// Pairs of the t, h and w axes for a head dimension: D/2 split as evenly as
+// possible, t first.
+__host__ __device__ inline void rope_split(int D, int* pt, int* ph, int* pw) {
+  const int n = D / 2;
+  *ph = n / 3;
+  *pw = n / 3;
+  *pt = n - *ph - *pw;
+}
+
+// cos/sin table of one call: rows are axis positions (T rows for t, then H
+// for h, then W for w), each with D/2 columns of (cos, sin); only the
+// columns of the row's own axis are filled.
+__global__ __launch_bounds__(256) void k_rope_table(double2* __restrict__ tab, int T, int Hh, int W, int D,
+                                                    int t_offset, double base) {
+  int pt, ph, pw;
+  rope_split(D, &pt, &ph, &pw);
+  const int rows = T + Hh + W, np = D / 2;
+  for (int e = blockIdx.x * 256 + threadIdx.x; e < rows * np; e += gridDim.x * 256) {
+    const int row = e / np, p = e - row * np;
+    int axis, pos, first, cnt;
+    if (row < T) axis = 0, pos = row + t_offset, first = 0, cnt = pt;
+    else if (row < T + Hh) axis = 1, pos = row - T, first = pt, cnt = ph;
+    else axis = 2, pos = row - T - Hh, first = pt + ph, cnt = pw;
+    (void)axis;
+    double2 cs = make_double2(1.0, 0.0);
+    if (p >= first && p < first + cnt) {
+      const double ang = (double)pos * pow(base, -(double)(p - first) / (double)cnt);
+      double sn, c;
+      sincos(ang, &sn, &c);
+      cs = make_double2(c, sn);
+    }
+    tab[e] = cs;
+  }
+}
+
+// x_perm[b,h,pos,:] = rope(x_raster[b, perm[pos], h, :]) (zero for a pad):
+// one thread per 16-byte chunk of a row (E/2 dimension pairs), 16-byte loads
+// and stores, the rotation in fp64 with the call's (cos, sin) table.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_permute_rope(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                           const int32_t* __restrict__ perm,
+                                                           const double2* __restrict__ tab, int64_t n_tok,
+                                                           int heads, int64_t n_pad, int D, int Tg, int Hg,
+                                                           int Wg) {
+  constexpr int E = 16 / sizeof(T);       // elements per chunk
+  const int bh = blockIdx.y;
+  const int b = bh / heads, h = bh - b * heads;
+  const int cpr = D / E, np = D / 2;
+  const int64_t total = n_pad * cpr;
+  int pt, ph, pw;
+  rope_split(D, &pt, &ph, &pw);
+  for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < total; e += (int64_t)gridDim.x * kThreads) {
+    const int64_t pos = e / cpr;
+    const int c = (int)(e - pos * cpr);
+    const int tok = perm[pos];
+    union {
+      uint4 v;
+      T x[E];
+    } in, out;
+    out.v = make_uint4(0, 0, 0, 0);
+    if (tok >= 0) {
+      in.v = src[(((int64_t)b * n_tok + tok) * heads + h) * cpr + c];
+      const int w = tok % Wg, th = tok / Wg;
+      const int hh = th % Hg, t = th / Hg;
+#pragma unroll
+      for (int j = 0; j < E / 2; ++j) {
+        const int p = c * (E / 2) + j;
+        const int row = p < pt ? t : (p < pt + ph ? Tg + hh : Tg + Hg + w);
+        const double2 cs = tab[(int64_t)row * np + p];
+        const double x0 = (double)ld_val(&in.x[2 * j]), x1 = (double)ld_val(&in.x[2 * j + 1]);
+        out.x[2 * j] = st_val<T>(x0 * cs.x - x1 * cs.y);
+        out.x[2 * j + 1] = st_val<T>(x0 * cs.y + x1 * cs.x);
+      }
+    }
+    dst[(int64_t)bh * total + e] = out.v;
+  }
+}
+
 int check_common(fva_plan_t plan, const void* a, const void* b) {
   if (!plan) return fva_fail(FVA_EINVAL, "plan is NULL");
   if (!a || !b) return fva_fail(FVA_EINVAL, "tensor pointer is NULL");
@@ -183,4 +286,28 @@ extern "C" int fva_unpermute(fva_plan_t plan, const void* x_perm, void* x_raster
   hipLaunchKernelGGL(k_unpermute_rows, grid, dim3(kThreads), 0, stream, (const uint4*)x_perm,
                      (uint4*)x_raster, plan->perm, in.n_tokens, d.heads, in.n_pad, cpr);
   return fva_after_launch(stream, "fva_unpermute");
+}
+
+extern "C" int fva_permute_rope(fva_plan_t plan, const void* x_raster, void* x_perm, int32_t t_offset, double base,
+                                hipStream_t stream) {
+  int rc = check_common(plan, x_raster, x_perm);
+  if (rc) return rc;
+  if (t_offset < 0) return fva_fail(FVA_EINVAL, "t_offset %d must be >= 0", t_offset);
+  if (!(base > 1.0)) return fva_fail(FVA_EINVAL, "base %g must be > 1", base);
+  const fva_plan_desc& d = plan->desc;
+  const fva_plan_info& in = plan->info;
+  const int T = d.grid[0], Hg = d.grid[1], Wg = d.grid[2], D = d.head_dim;
+  const int entries = (T + Hg + Wg) * (D / 2);
+  hipLaunchKernelGGL(k_rope_table, dim3((entries + 255) / 256), dim3(256), 0, stream, plan->rope_tab, T, Hg, Wg, D,
+                     t_offset, base);
+  const int64_t total = in.n_pad * (D * plan->esize / 16);
+  const unsigned gx = (unsigned)std::min<int64_t>((total + kThreads - 1) / kThreads, 4096);
+  dim3 grid(gx, d.batch * d.heads);
+  if (d.dtype == FVA_DTYPE_BF16)
+    hipLaunchKernelGGL((k_permute_rope<uint16_t>), grid, dim3(kThreads), 0, stream, (const uint4*)x_raster,
+                       (uint4*)x_perm, plan->perm, plan->rope_tab, in.n_tokens, d.heads, in.n_pad, D, T, Hg, Wg);
+  else
+    hipLaunchKernelGGL((k_permute_rope<float>), grid, dim3(kThreads), 0, stream, (const uint4*)x_raster,
+                       (uint4*)x_perm, plan->perm, plan->rope_tab, in.n_tokens, d.heads, in.n_pad, D, T, Hg, Wg);
+  return fva_after_launch(stream, "fva_permute_rope");
 }

@@ -62,6 +62,7 @@ def lib() -> ctypes.CDLL:
             "fva_plan_query": (c_i32, [c_vp, P(fva_plan_info)]),
             "fva_plan_destroy": (None, [c_vp]),
             "fva_permute": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_vp]),
+            "fva_permute_rope": (c_i32, [c_vp, c_vp, c_vp, c_i32, ctypes.c_double, c_vp]),
             "fva_select": (c_i32, [c_vp, c_vp, c_vp, P(ctypes.c_float), c_i32, c_i32, c_i32, c_vp, c_vp,
                                    c_vp, c_vp, c_vp, c_vp]),
             "fva_attention": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp]),
@@ -186,6 +187,15 @@ def fva_permute(plan: Plan, x_raster, x_perm, layout=LAYOUT_ROWS, stream=None):
             or x_perm.dtype != plan.torch_dtype:
         raise ValueError("x_perm has the wrong size or dtype")
     _check(lib().fva_permute(plan.handle, _ptr(x_raster), _ptr(x_perm), int(layout), _stream(stream)))
+
+
+def fva_permute_rope(plan: Plan, x_raster, x_perm, t_offset=0, base=10000.0, stream=None):
+    """Raster -> block-order rows with the 3D rotary encoding applied
+    (global time index t + t_offset)."""
+    _expect(x_raster, plan.raster_shape(), plan.torch_dtype, "x_raster")
+    _expect(x_perm, plan.perm_shape(), plan.torch_dtype, "x_perm")
+    _check(lib().fva_permute_rope(plan.handle, _ptr(x_raster), _ptr(x_perm), int(t_offset), float(base),
+                                  _stream(stream)))
 
 
 def fva_unpermute(plan: Plan, x_perm, x_raster, stream=None):

@@ -149,6 +149,23 @@ void fva_plan_destroy(fva_plan_t plan);
 int fva_permute(fva_plan_t plan, const void* x_raster, void* x_perm, int32_t layout,
                 hipStream_t stream);
 
+/* fva_permute (FVA_LAYOUT_ROWS) fused with a 3D rotary position encoding
+ * that uses a global time index ("Accelerating Video Generation Inference
+ * with Sequential-Parallel 3D Positional Encoding Using a Global Time Index",
+ * section 2.2: a chunk of frames is encoded with t_global = t_local +
+ * t_offset, so it needs no other chunk; section 2.3: the frequencies are
+ * precomputed as one contiguous table).  For the raster token at grid
+ * position (t, h, w) the D/2 dimension pairs (2p, 2p+1) are split over the
+ * axes as evenly as possible, t first (D = 128: 22, 21, 21 pairs); pair i of
+ * an axis with P pairs turns by pos * base^(-i/P), pos being t + t_offset,
+ * h or w.  The angles' cosines and sines are tabulated in fp64 on the device
+ * for this call; the rotation runs in fp64 and is rounded once to the plan
+ * dtype.  Use it for Q and K (V takes plain fva_permute).
+ *   t_offset >= 0; base > 1.  Errors: FVA_EINVAL for bad arguments.
+ * x_raster and x_perm must not overlap. */
+int fva_permute_rope(fva_plan_t plan, const void* x_raster, void* x_perm, int32_t t_offset, double base,
+                     hipStream_t stream);
+
 /* Coarse stage and routing ("Video Sparse Attention" dialogue and section 3;
  * "FVAttn" sections 00 and 02; "DFSAttn" trick 2):
  *   pool   q_bar_I = mean of the valid rows of Q block I (k_bar likewise; with
