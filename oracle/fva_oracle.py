@@ -426,3 +426,20 @@ def rope(x_raster: np.ndarray, grid, t_offset: int = 0, base: float = 10000.0) -
     out[..., 0::2] = x0 * c - x1 * s
     out[..., 1::2] = x0 * s + x1 * c
     return out
+
+
+# --------------------------------------------------------------------------
+# Mask reuse across denoising steps ([DFSAttn] trick 3: blocks that mattered
+# at an earlier step are kept instead of re-evaluated; "FVAttn" section 02
+# makes the same selection per step).  The decision to reuse a cached mask
+# reads how much two selections agree: per (b, h), the sizes of the
+# intersection and of the union of the kept (I, J) pairs.
+def mask_overlap(rp_a, ci_a, rp_b, ci_b, B: int, H: int, n_blk: int) -> np.ndarray:
+    """[B*H, 2] int64: |A & B| and |A | B| over the (I, J) pairs of each head."""
+    a_rows, b_rows = from_csr(rp_a, ci_a), from_csr(rp_b, ci_b)
+    out = np.zeros((B * H, 2), dtype=np.int64)
+    for r in range(B * H * n_blk):
+        sa, sb = set(int(j) for j in a_rows[r]), set(int(j) for j in b_rows[r])
+        out[r // n_blk, 0] += len(sa & sb)
+        out[r // n_blk, 1] += len(sa | sb)
+    return out

@@ -358,3 +358,23 @@ def test_full_pipeline_toy_p1_is_dense():
     t = lambda a: torch.from_numpy(a.astype(np.float64)).permute(0, 2, 1, 3)
     ref = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v)).permute(0, 2, 1, 3).numpy()
     assert np.allclose(res["o"], ref, atol=1e-12)
+
+
+def test_mask_overlap_brute_force():
+    """Per-head intersection / union sizes of two CSR selections, against an
+    explicit pair-set count."""
+    rng = np.random.default_rng(4)
+    B, H, n = 1, 3, 6
+    def rand_csr():
+        rows = [np.sort(rng.choice(n, size=rng.integers(0, n + 1), replace=False)) for _ in range(B * H * n)]
+        rp = np.zeros(len(rows) + 1, dtype=np.int64)
+        rp[1:] = np.cumsum([len(r) for r in rows])
+        return rp, (np.concatenate(rows) if rows else np.zeros(0, np.int64)).astype(np.int64)
+    (ra, ca), (rb, cb) = rand_csr(), rand_csr()
+    got = O.mask_overlap(ra, ca, rb, cb, B, H, n)
+    for bh in range(B * H):
+        pa = {(i, int(j)) for i in range(n) for j in ca[ra[bh * n + i]:ra[bh * n + i + 1]]}
+        pb = {(i, int(j)) for i in range(n) for j in cb[rb[bh * n + i]:rb[bh * n + i + 1]]}
+        assert got[bh, 0] == len(pa & pb) and got[bh, 1] == len(pa | pb)
+    same = O.mask_overlap(ra, ca, ra, ca, B, H, n)
+    assert np.array_equal(same[:, 0], same[:, 1])
