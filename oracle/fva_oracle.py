@@ -439,7 +439,8 @@ def mask_overlap(rp_a, ci_a, rp_b, ci_b, B: int, H: int, n_blk: int) -> np.ndarr
     a_rows, b_rows = from_csr(rp_a, ci_a), from_csr(rp_b, ci_b)
     out = np.zeros((B * H, 2), dtype=np.int64)
     for r in range(B * H * n_blk):
-        sa, sb = set(int(j) for j in a_rows[r]), set(int(j) for j in b_rows[r])
+        sa = set(int(j) for j in a_rows[r] if 0 <= j < n_blk)   # rows are sets of plan blocks
+        sb = set(int(j) for j in b_rows[r] if 0 <= j < n_blk)
         out[r // n_blk, 0] += len(sa & sb)
         out[r // n_blk, 1] += len(sa | sb)
     return out
