@@ -180,6 +180,27 @@ def main():
     torch.cuda.synchronize()
     rope_ms = e_r0.elapsed_time(e_r1) / args.steps
 
+    # a call that reuses the cached selection (no fva_select) and the cost of
+    # deciding to: the overlap of two selections
+    def call_reuse():
+        fva.fva_permute(plan, qd, bufs.q, fva.LAYOUT_ROWS)
+        fva.fva_permute(plan, kd, bufs.k, fva.LAYOUT_ROWS)
+        fva.fva_permute(plan, vd, bufs.vt, fva.LAYOUT_VT)
+        fva.fva_attention(plan, bufs.q, bufs.k, bufs.vt, bufs.row_ptr, bufs.col_idx, bufs.o, sched=args.sched)
+        fva.fva_unpermute(plan, bufs.o, out)
+    counts = torch.empty(w.B * w.H, 2, dtype=torch.int64, device="cuda")
+    e_u0, e_u1, e_u2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    e_u0.record()
+    for _ in range(args.steps):
+        call_reuse()
+    e_u1.record()
+    for _ in range(args.steps):
+        fva.fva_mask_overlap(plan, bufs.row_ptr, bufs.col_idx, bufs.row_ptr, bufs.col_idx, counts)
+    e_u2.record()
+    torch.cuda.synchronize()
+    reuse_ms = e_u0.elapsed_time(e_u1) / args.steps
+    overlap_ms = e_u1.elapsed_time(e_u2) / args.steps
+
     # one extra, untimed call with per-workgroup stamps for the load balance
     wg = torch.zeros(2 * plan.info.max_wg, dtype=torch.int64, device="cuda")
     fva.fva_attention(plan, bufs.q, bufs.k, bufs.vt, bufs.row_ptr, bufs.col_idx, bufs.o, sched=args.sched,
@@ -241,6 +262,7 @@ def main():
                     "peak": PEAK_HBM_GBS},
         "load_balance": balance,
         "permute_rope_ms": round(rope_ms, 4),
+        "reuse": {"ms_per_call_cached_selection": round(reuse_ms, 4), "mask_overlap_ms": round(overlap_ms, 4)},
         "permute_rope_gbs": round(perm_bytes / (rope_ms * 1e-3) / 1e9, 1),
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),

@@ -795,3 +795,64 @@ extern "C" int fva_select(fva_plan_t plan, const void* q_perm, const void* k_per
                      plan->nw, in.n_blk, in.n_rows);
   return fva_after_launch(stream, "fva_select");
 }
+
+// ------------------------------------------------------------------ reuse
+namespace {
+
+__global__ __launch_bounds__(256) void k_zero_i64(int64_t* __restrict__ p, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0;
+}
+
+// One wave per row: both rows' id sets become LDS bitmaps, lane l then
+// counts word l of their intersection and union; per-head totals by atomics.
+__global__ __launch_bounds__(256) void k_mask_overlap(const int32_t* __restrict__ rpa, const int32_t* __restrict__ cia,
+                                                      const int32_t* __restrict__ rpb, const int32_t* __restrict__ cib,
+                                                      int n_blk, int64_t n_rows, unsigned long long* __restrict__ counts) {
+  __shared__ unsigned int bits[4][2][128];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t r = (int64_t)blockIdx.x * 4 + wv;
+  if (r >= n_rows) return;   // whole wave; only wave-level syncs below
+  for (int t = lane; t < 256; t += 64) bits[wv][t >> 7][t & 127] = 0;
+  wave_sync_lds();
+  for (int j = rpa[r] + lane; j < rpa[r + 1]; j += 64) {
+    const int J = cia[j];
+    if ((unsigned)J < (unsigned)n_blk) atomicOr(&bits[wv][0][J >> 5], 1u << (J & 31));
+  }
+  for (int j = rpb[r] + lane; j < rpb[r + 1]; j += 64) {
+    const int J = cib[j];
+    if ((unsigned)J < (unsigned)n_blk) atomicOr(&bits[wv][1][J >> 5], 1u << (J & 31));
+  }
+  wave_sync_lds();
+  unsigned long long inter = 0, uni = 0;
+  for (int t = lane; t < (n_blk + 31) / 32; t += 64) {
+    const unsigned a = bits[wv][0][t], b = bits[wv][1][t];
+    inter += __popc(a & b);
+    uni += __popc(a | b);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    inter += __shfl_xor(inter, o);
+    uni += __shfl_xor(uni, o);
+  }
+  if (lane == 0) {
+    const int64_t bh = r / n_blk;
+    atomicAdd(&counts[2 * bh], inter);
+    atomicAdd(&counts[2 * bh + 1], uni);
+  }
+}
+
+}  // namespace
+
+extern "C" int fva_mask_overlap(fva_plan_t plan, const int32_t* row_ptr_a, const int32_t* col_idx_a,
+                                const int32_t* row_ptr_b, const int32_t* col_idx_b, int64_t* counts,
+                                hipStream_t stream) {
+  if (!plan) return fva_fail(FVA_EINVAL, "plan is NULL");
+  if (!row_ptr_a || !col_idx_a || !row_ptr_b || !col_idx_b || !counts)
+    return fva_fail(FVA_EINVAL, "CSR or counts pointer is NULL");
+  const fva_plan_info& in = plan->info;
+  const int n_bh = plan->desc.batch * plan->desc.heads;
+  hipLaunchKernelGGL(k_zero_i64, dim3((2 * n_bh + 255) / 256), dim3(256), 0, stream, counts, 2 * n_bh);
+  hipLaunchKernelGGL(k_mask_overlap, dim3((unsigned)((in.n_rows + 3) / 4)), dim3(256), 0, stream, row_ptr_a,
+                     col_idx_a, row_ptr_b, col_idx_b, (int)in.n_blk, in.n_rows, (unsigned long long*)counts);
+  return fva_after_launch(stream, "fva_mask_overlap");
+}

@@ -67,6 +67,7 @@ def lib() -> ctypes.CDLL:
                                    c_vp, c_vp, c_vp, c_vp]),
             "fva_attention": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp]),
             "fva_unpermute": (c_i32, [c_vp, c_vp, c_vp, c_vp]),
+            "fva_mask_overlap": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
             "fva_last_error": (ctypes.c_char_p, []),
         }
         for name, (res, args) in sig.items():
@@ -196,6 +197,22 @@ def fva_permute_rope(plan: Plan, x_raster, x_perm, t_offset=0, base=10000.0, str
     _expect(x_perm, plan.perm_shape(), plan.torch_dtype, "x_perm")
     _check(lib().fva_permute_rope(plan.handle, _ptr(x_raster), _ptr(x_perm), int(t_offset), float(base),
                                   _stream(stream)))
+
+
+def fva_mask_overlap(plan: Plan, row_ptr_a, col_idx_a, row_ptr_b, col_idx_b, counts=None, stream=None):
+    """Per-head |A & B| and |A | B| of two CSR selections: int64 [B*H, 2]."""
+    nbh = plan.desc.batch * plan.desc.heads
+    for t, name in ((row_ptr_a, "row_ptr_a"), (row_ptr_b, "row_ptr_b")):
+        _expect(t, (plan.n_rows + 1,), torch.int32, name)
+    for t, name in ((col_idx_a, "col_idx_a"), (col_idx_b, "col_idx_b")):
+        if t.dtype != torch.int32 or not t.is_cuda:
+            raise ValueError(f"{name} must be an int32 device tensor")
+    if counts is None:
+        counts = torch.empty(nbh, 2, dtype=torch.int64, device="cuda")
+    _expect(counts, (nbh, 2), torch.int64, "counts")
+    _check(lib().fva_mask_overlap(plan.handle, _ptr(row_ptr_a), _ptr(col_idx_a), _ptr(row_ptr_b), _ptr(col_idx_b),
+                                  _ptr(counts), _stream(stream)))
+    return counts
 
 
 def fva_unpermute(plan: Plan, x_perm, x_raster, stream=None):

@@ -227,6 +227,19 @@ int fva_attention(fva_plan_t plan, const void* q_perm, const void* k_perm, const
                   const int32_t* row_ptr, const int32_t* col_idx, void* o_perm,
                   int32_t sched_mode, uint64_t* wg_times, hipStream_t stream);
 
+/* Agreement of two block selections, for reusing a cached selection across
+ * denoising steps ("DFSAttn" explainer, trick 3: blocks that mattered at an
+ * earlier step are remembered instead of re-evaluated; fva_attention accepts
+ * any cached CSR).  For every (b, h): counts[2*bh] = |A & B| and
+ * counts[2*bh + 1] = |A | B| over its (I, J) block pairs, with each row read
+ * as a set (repeated ids count once, ids outside [0, n_blk) are ignored).
+ *   row_ptr_*, col_idx_*  device CSR over the plan's rows.
+ *   counts                device int64 [2*B*H], overwritten.
+ * Errors: FVA_EINVAL for NULL pointers. */
+int fva_mask_overlap(fva_plan_t plan, const int32_t* row_ptr_a, const int32_t* col_idx_a,
+                     const int32_t* row_ptr_b, const int32_t* col_idx_b, int64_t* counts,
+                     hipStream_t stream);
+
 /* Scatter block-order [B, H, N_pad, D] (FVA_LAYOUT_ROWS) back to raster
  * [B, N, H, D], dropping pad positions.  Inverse of fva_permute. */
 int fva_unpermute(fva_plan_t plan, const void* x_perm, void* x_raster, hipStream_t stream);
