@@ -444,3 +444,26 @@ def mask_overlap(rp_a, ci_a, rp_b, ci_b, B: int, H: int, n_blk: int) -> np.ndarr
         out[r // n_blk, 0] += len(sa & sb)
         out[r // n_blk, 1] += len(sa | sb)
     return out
+
+
+# --------------------------------------------------------------------------
+# Static calibrated selections ("Calibrated Sparse Attention" page: an
+# offline pass keeps the block patterns that stay stable across calibration
+# inputs, per layer, head and diffusion step, and inference then skips the
+# rest).  Reading: count, per (b, h, I, J), in how many calibration runs the
+# pair was selected; keep the pairs selected in at least min_count runs
+# (min_count 1: the union of the runs; min_count = runs: their intersection).
+def calib_counts(csrs, B: int, H: int, n_blk: int) -> np.ndarray:
+    """[B*H*n_blk, n_blk] int64 selection counts over a list of (row_ptr, col_idx)."""
+    counts = np.zeros((B * H * n_blk, n_blk), dtype=np.int64)
+    for rp, ci in csrs:
+        for r, row in enumerate(from_csr(rp, ci)):
+            for j in set(int(x) for x in row if 0 <= x < n_blk):
+                counts[r, j] += 1
+    return counts
+
+
+def calib_select(counts: np.ndarray, min_count: int):
+    """CSR (ascending ids) of the pairs counted at least min_count times."""
+    rows = [np.nonzero(c >= min_count)[0] for c in counts]
+    return to_csr(rows)

@@ -378,3 +378,25 @@ def test_mask_overlap_brute_force():
         assert got[bh, 0] == len(pa & pb) and got[bh, 1] == len(pa | pb)
     same = O.mask_overlap(ra, ca, ra, ca, B, H, n)
     assert np.array_equal(same[:, 0], same[:, 1])
+
+
+def test_calibrated_selection_union_intersection_and_nesting():
+    """Counting selections over calibration runs: threshold 1 is the union of
+    the runs' pair sets, threshold = runs the intersection, and raising the
+    threshold only removes pairs (brute force over explicit pair sets)."""
+    rng = np.random.default_rng(6)
+    B, H, n, runs = 1, 2, 5, 3
+    csrs = []
+    for _ in range(runs):
+        rows = [np.sort(rng.choice(n, size=rng.integers(0, n + 1), replace=False)) for _ in range(B * H * n)]
+        csrs.append(O.to_csr(rows))
+    counts = O.calib_counts(csrs, B, H, n)
+    sets = [{(r, int(j)) for r in range(B * H * n) for j in ci[rp[r]:rp[r + 1]]} for rp, ci in csrs]
+    def pairs(rp, ci):
+        return {(r, int(j)) for r in range(B * H * n) for j in ci[rp[r]:rp[r + 1]]}
+    assert pairs(*O.calib_select(counts, 1)) == set.union(*sets)
+    assert pairs(*O.calib_select(counts, runs)) == set.intersection(*sets)
+    assert pairs(*O.calib_select(counts, 2)) <= pairs(*O.calib_select(counts, 1))
+    rp, ci = O.calib_select(counts, 1)
+    for r in range(B * H * n):
+        assert np.all(np.diff(ci[rp[r]:rp[r + 1]]) > 0)
