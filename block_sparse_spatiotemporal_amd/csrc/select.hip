@@ -841,7 +841,73 @@ __global__ __launch_bounds__(256) void k_mask_overlap(const int32_t* __restrict_
   }
 }
 
+// Row r of a selection, as a set, added into its row of counts.
+__global__ __launch_bounds__(256) void k_mask_accumulate(const int32_t* __restrict__ rp, const int32_t* __restrict__ ci,
+                                                         int n_blk, int64_t n_rows, int32_t* __restrict__ counts) {
+  __shared__ unsigned int bits[4][128];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t r = (int64_t)blockIdx.x * 4 + wv;
+  if (r >= n_rows) return;   // whole wave; only wave-level syncs below
+  for (int t = lane; t < 128; t += 64) bits[wv][t] = 0;
+  wave_sync_lds();
+  for (int j = rp[r] + lane; j < rp[r + 1]; j += 64) {
+    const int J = ci[j];
+    if ((unsigned)J < (unsigned)n_blk) atomicOr(&bits[wv][J >> 5], 1u << (J & 31));
+  }
+  wave_sync_lds();
+  int32_t* c = counts + r * n_blk;
+  for (int J = lane; J < n_blk; J += 64)
+    if (bits[wv][J >> 5] >> (J & 31) & 1) c[J] += 1;
+}
+
+// Kept-pair bitmask and count of each row from the counts.
+__global__ __launch_bounds__(256) void k_mask_threshold(const int32_t* __restrict__ counts, int32_t min_count,
+                                                        int n_blk, int64_t n_rows, int nw,
+                                                        uint64_t* __restrict__ rowmask, int32_t* __restrict__ rowcnt) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t r = (int64_t)blockIdx.x * 4 + wv;
+  if (r >= n_rows) return;
+  const int32_t* c = counts + r * n_blk;
+  int kept = 0;
+  for (int i = 0; i < nw; ++i) {
+    const int J = 64 * i + lane;
+    const uint64_t b = __ballot(J < n_blk && c[J] >= min_count);
+    if (lane == 0) rowmask[r * nw + i] = b;
+    kept += __popcll(b);
+  }
+  if (lane == 0) rowcnt[r] = kept;
+}
+
 }  // namespace
+
+extern "C" int fva_mask_accumulate(fva_plan_t plan, const int32_t* row_ptr, const int32_t* col_idx, int32_t* counts,
+                                   hipStream_t stream) {
+  if (!plan) return fva_fail(FVA_EINVAL, "plan is NULL");
+  if (!row_ptr || !col_idx || !counts) return fva_fail(FVA_EINVAL, "CSR or counts pointer is NULL");
+  const fva_plan_info& in = plan->info;
+  hipLaunchKernelGGL(k_mask_accumulate, dim3((unsigned)((in.n_rows + 3) / 4)), dim3(256), 0, stream, row_ptr, col_idx,
+                     (int)in.n_blk, in.n_rows, counts);
+  return fva_after_launch(stream, "fva_mask_accumulate");
+}
+
+extern "C" int fva_mask_from_counts(fva_plan_t plan, const int32_t* counts, int32_t min_count, int32_t* row_ptr,
+                                    int32_t* col_idx, int32_t* head_nnz, hipStream_t stream) {
+  if (!plan) return fva_fail(FVA_EINVAL, "plan is NULL");
+  if (!counts || !row_ptr || !col_idx) return fva_fail(FVA_EINVAL, "counts / row_ptr / col_idx is NULL");
+  if (min_count < 1) return fva_fail(FVA_EINVAL, "min_count %d must be >= 1", min_count);
+  const fva_plan_info& in = plan->info;
+  const int n_bh = plan->desc.batch * plan->desc.heads;
+  const unsigned g = (unsigned)((in.n_rows + 3) / 4);
+  hipLaunchKernelGGL(k_mask_threshold, dim3(g), dim3(256), 0, stream, counts, min_count, (int)in.n_blk, in.n_rows,
+                     plan->nw, plan->rowmask, plan->rowcnt);
+  hipLaunchKernelGGL(k_scan_rows, dim3(n_bh), dim3(1024), 0, stream, plan->rowcnt, (int)in.n_blk, row_ptr,
+                     plan->headcnt);
+  hipLaunchKernelGGL(k_scan_heads, dim3(1), dim3(1024), 0, stream, plan->headcnt, n_bh, plan->headoff, head_nnz,
+                     row_ptr, in.n_rows);
+  hipLaunchKernelGGL(k_emit, dim3(g), dim3(256), 0, stream, plan->rowmask, row_ptr, plan->headoff, col_idx, plan->nw,
+                     (int)in.n_blk, in.n_rows);
+  return fva_after_launch(stream, "fva_mask_from_counts");
+}
 
 extern "C" int fva_mask_overlap(fva_plan_t plan, const int32_t* row_ptr_a, const int32_t* col_idx_a,
                                 const int32_t* row_ptr_b, const int32_t* col_idx_b, int64_t* counts,

@@ -68,6 +68,8 @@ def lib() -> ctypes.CDLL:
             "fva_attention": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp]),
             "fva_unpermute": (c_i32, [c_vp, c_vp, c_vp, c_vp]),
             "fva_mask_overlap": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
+            "fva_mask_accumulate": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp]),
+            "fva_mask_from_counts": (c_i32, [c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp]),
             "fva_last_error": (ctypes.c_char_p, []),
         }
         for name, (res, args) in sig.items():
@@ -213,6 +215,23 @@ def fva_mask_overlap(plan: Plan, row_ptr_a, col_idx_a, row_ptr_b, col_idx_b, cou
     _check(lib().fva_mask_overlap(plan.handle, _ptr(row_ptr_a), _ptr(col_idx_a), _ptr(row_ptr_b), _ptr(col_idx_b),
                                   _ptr(counts), _stream(stream)))
     return counts
+
+
+def fva_mask_accumulate(plan: Plan, row_ptr, col_idx, counts, stream=None):
+    """counts[r, J] += 1 for every kept pair of a selection (counts: int32 [n_rows, n_blk])."""
+    _expect(row_ptr, (plan.n_rows + 1,), torch.int32, "row_ptr")
+    _expect(counts, (plan.n_rows, plan.n_blk), torch.int32, "counts")
+    _check(lib().fva_mask_accumulate(plan.handle, _ptr(row_ptr), _ptr(col_idx), _ptr(counts), _stream(stream)))
+
+
+def fva_mask_from_counts(plan: Plan, counts, min_count, row_ptr, col_idx, head_nnz=None, stream=None):
+    """CSR of the pairs counted at least min_count times."""
+    _expect(counts, (plan.n_rows, plan.n_blk), torch.int32, "counts")
+    _expect(row_ptr, (plan.n_rows + 1,), torch.int32, "row_ptr")
+    if col_idx.dtype != torch.int32 or col_idx.numel() < plan.info.max_nnz:
+        raise ValueError("col_idx must be int32 with capacity max_nnz")
+    _check(lib().fva_mask_from_counts(plan.handle, _ptr(counts), int(min_count), _ptr(row_ptr), _ptr(col_idx),
+                                      _ptr(head_nnz), _stream(stream)))
 
 
 def fva_unpermute(plan: Plan, x_perm, x_raster, stream=None):

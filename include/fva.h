@@ -240,6 +240,24 @@ int fva_mask_overlap(fva_plan_t plan, const int32_t* row_ptr_a, const int32_t* c
                      const int32_t* row_ptr_b, const int32_t* col_idx_b, int64_t* counts,
                      hipStream_t stream);
 
+/* Static calibrated selections ("Calibrated Sparse Attention" page: an
+ * offline pass keeps the block patterns that stay stable across calibration
+ * inputs, per layer, head and diffusion step; inference then computes only
+ * those).  fva_mask_accumulate adds one selection to per-pair counts:
+ * counts[r*n_blk + J] += 1 for every id J of row r (a row is read as a set
+ * of plan blocks).  fva_mask_from_counts emits the CSR of the pairs counted
+ * at least min_count times (ids ascending), usable by fva_attention at every
+ * later call: min_count = 1 gives the union of the calibration runs,
+ * min_count = runs their intersection.
+ *   counts    device int32 [n_rows * n_blk], zeroed by the caller before the
+ *             first run, owned by the caller.
+ *   row_ptr, col_idx, head_nnz  as for fva_select (head_nnz nullable).
+ * Errors: FVA_EINVAL for NULL pointers or min_count < 1. */
+int fva_mask_accumulate(fva_plan_t plan, const int32_t* row_ptr, const int32_t* col_idx, int32_t* counts,
+                        hipStream_t stream);
+int fva_mask_from_counts(fva_plan_t plan, const int32_t* counts, int32_t min_count, int32_t* row_ptr,
+                         int32_t* col_idx, int32_t* head_nnz, hipStream_t stream);
+
 /* Scatter block-order [B, H, N_pad, D] (FVA_LAYOUT_ROWS) back to raster
  * [B, N, H, D], dropping pad positions.  Inverse of fva_permute. */
 int fva_unpermute(fva_plan_t plan, const void* x_perm, void* x_raster, hipStream_t stream);
