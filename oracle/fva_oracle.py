@@ -467,3 +467,41 @@ def calib_select(counts: np.ndarray, min_count: int):
     """CSR (ascending ids) of the pairs counted at least min_count times."""
     rows = [np.nonzero(c >= min_count)[0] for c in counts]
     return to_csr(rows)
+
+
+# --------------------------------------------------------------------------
+# Backward pass of the block-sparse attention on the same lists (the pages'
+# trained sparse attention, "Video Sparse Attention" explainer section 3,
+# needs gradients through the fine stage).  For every valid query token i of
+# block I, over the valid key tokens j of I's listed blocks:
+#   P_ij = softmax_j(q_i . k_j / sqrt(D)),  o_i = sum_j P_ij v_j
+#   dv_j += P_ij do_i;  dP_ij = do_i . v_j;  dS_ij = P_ij (dP_ij - sum_j' P_ij' dP_ij')
+#   dq_i = sum_j dS_ij k_j / sqrt(D);  dk_j += dS_ij q_i / sqrt(D)
+# (the gradient of o with respect to q, k, v; pad rows get zero gradients).
+def attention_backward(q_perm, k_perm, v_perm, do_perm, row_ptr, col_idx, pl: Plan):
+    """(dq, dk, dv) in block order, fp64."""
+    B, H, n_pad, D = q_perm.shape
+    n, bs = pl.n_blk, pl.blk_size
+    dq, dk, dv = np.zeros_like(q_perm), np.zeros_like(k_perm), np.zeros_like(v_perm)
+    valid = pl.perm >= 0
+    scale = 1.0 / math.sqrt(D)
+    for b in range(B):
+        for h in range(H):
+            for i in range(n):
+                r = (b * H + h) * n + i
+                blocks = col_idx[row_ptr[r]:row_ptr[r + 1]]
+                qrows = np.nonzero(valid[i * bs:(i + 1) * bs])[0] + i * bs
+                if len(blocks) == 0 or len(qrows) == 0:
+                    continue
+                krows = np.concatenate([np.nonzero(valid[j * bs:(j + 1) * bs])[0] + j * bs for j in blocks])
+                Q, K, V, dO = q_perm[b, h, qrows], k_perm[b, h, krows], v_perm[b, h, krows], do_perm[b, h, qrows]
+                z = Q @ K.T * scale
+                z -= z.max(axis=1, keepdims=True)
+                P = np.exp(z)
+                P /= P.sum(axis=1, keepdims=True)
+                dP = dO @ V.T
+                dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+                dq[b, h, qrows] += dS @ K * scale
+                np.add.at(dk[b, h], krows, dS.T @ Q * scale)
+                np.add.at(dv[b, h], krows, P.T @ dO)
+    return dq, dk, dv
