@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfva.so")
-SOURCES = ["plan.cpp", "permute.hip", "select.hip", "attention.hip"]
+SOURCES = ["plan.cpp", "permute.hip", "select.hip", "attention.hip", "backward.hip"]
 
 
 def hipcc() -> str:

@@ -10,13 +10,12 @@
 #include <cmath>
 #include <cstdlib>
 
+#include "attn_common.h"
 #include "fva_internal.h"
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+using namespace fva_attn;
 
 struct AttnArgs {
   const uint16_t* q;        // [B*H, n_pad, D] rows
@@ -33,6 +32,8 @@ struct AttnArgs {
   const int32_t* worklist;
   int32_t* cursor;
   uint64_t* wg_times;
+  float* lse;               // optional [B*H, n_pad]: log2 sum exp2 of the scaled scores
+  float* o32;               // optional [B*H, n_pad, D]: the output before rounding to bf16
   int64_t n_pad;
   int n_items;
   int n_blk;
@@ -41,16 +42,6 @@ struct AttnArgs {
   float scale;              // 1/sqrt(D)
 };
 
-constexpr int kXcds = 8;    // MI355X: 8 XCDs, workgroups dealt round-robin
-
-// Work-list position of the k-th row an XCD takes: the list is cut into
-// chunks of `chunk` rows dealt round-robin to the XCDs, so the workgroups of
-// one XCD (one L2) walk contiguous query blocks of the same head.
-__device__ __forceinline__ int64_t xcd_item(int x, int64_t k, int chunk) {
-  return ((k / chunk) * kXcds + x) * chunk + k % chunk;
-}
-
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // Next row for this workgroup, or -1 when the work list is exhausted.
 // Plain: workgroup b is on XCD b % 8 and takes its XCD's (b / 8)-th row.
@@ -96,95 +87,6 @@ __device__ __forceinline__ int next_item(const AttnArgs& a, int* s_item, bool fi
 // load writes lane i's 16 bytes at offset 16*i of its 1 KB destination.
 // The running max is raised lazily: P may grow to 2^kLazy before O and l are
 // rescaled, which skips most rescales once the row maximum is found.
-
-// Direct global->LDS load of 16 bytes per lane from the wave-uniform base
-// plus the lane's 32-bit byte offset; lane i's bytes land at LDS address
-// lds_addr + 16*i (lds_addr wave-uniform).
-// Written as inline assembly on purpose: the compiler cannot tell which ring
-// stage a direct load writes, so for the builtin it makes every later LDS
-// read wait for all direct loads in flight, which would drain the prefetch
-// pipeline each step.  Ordering is kept by hand instead: each wave waits on
-// its own vector-memory count (wait_vm) and a workgroup barrier publishes
-// the stage before any wave reads it.
-__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds_addr) : "memory", "m0");
-}
-
-// LDS byte address of a shared-memory object.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// s_waitcnt with only the vector-memory count limited to n (other counters
-// left free).  gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] |
-// vmcnt_hi[15:14].
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Workgroup barrier without the memory fence __syncthreads() implies: the
-// fence would drain every outstanding vector load, including the direct
-// loads of the steps still in flight.  The empty asm statements keep the
-// compiler from moving LDS accesses across the barrier.
-__device__ __forceinline__ void barrier_no_fence() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// Combine lane l with lane l^32 without an LDS round trip: v_permlane32_swap
-// of x with itself leaves x[l%32] in one result and x[l%32 + 32] in the other.
-__device__ __forceinline__ float xhalf_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float xhalf_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Wave-uniform reads of read-only metadata through the scalar cache.
-template <typename T>
-__device__ __forceinline__ T sload(const T* p, int64_t i) {
-  return ((const __attribute__((address_space(4))) T*)p)[i];
-}
-
-// XOR swizzles of the LDS images (16-byte chunk index within a row).  They
-// keep every group of 8 and of 16 consecutive lanes of a ds_read_b128 on
-// distinct 16-byte bank slots.  K rows are D*2 bytes (KCH chunks); V^T rows
-// are 64 bytes (4 chunks).
-template <int D>
-__device__ __forceinline__ int kswz(int row) {
-  return D == 128 ? (row & 15) : ((row & 6) | ((row ^ (row >> 3)) & 1));
-}
-__device__ __forceinline__ int vswz(int d) {
-  return (((d >> 1) ^ (d >> 2)) & 1) | ((((d >> 2) ^ (d >> 3)) & 1) << 1);
-}
-
-// Word w (blocks 64w..64w+63) of a block bitmap held one 64-bit word per
-// lane, read out as a wave-uniform value.
-__device__ __forceinline__ uint64_t lane_word(uint32_t lo, uint32_t hi, int w) {
-  return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, w) << 32) |
-         (uint32_t)__builtin_amdgcn_readlane((int)lo, w);
-}
-
-// Ascending walk over the set bits of such a bitmap; the state is
-// wave-uniform, so the walk is scalar arithmetic with no memory access.
-struct BitWalk {
-  uint64_t bits = 0;  // unvisited bits of word w
-  int w = -1;
-  __device__ __forceinline__ bool next(uint32_t lo, uint32_t hi, int nw, int* J) {
-    while (bits == 0) {
-      if (++w >= nw) return false;
-      bits = lane_word(lo, hi, w);
-    }
-    *J = 64 * w + __builtin_ctzll(bits);
-    bits &= bits - 1;
-    return true;
-  }
-};
 
 // G query blocks per workgroup (2G waves; wave w serves block w/2, queries
 // 32*(w%2)..+31).  Steps walk the union of the G block lists half by half;
@@ -383,6 +285,8 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
       const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
       const bool qvalid = sload(a.blk_mask, I) >> (32 * w2 + l32) & 1;
       uint16_t* orow = (uint16_t*)a.o + (head + (int64_t)I * 64 + 32 * w2 + l32) * D;
+      if (a.lse && h == 0)   // P_ij = exp2(s_ij * scale * log2(e) - lse_i) for the backward pass
+        a.lse[head + (int64_t)I * 64 + 32 * w2 + l32] = qvalid && l_tot > 0.0f ? m_run + __log2f(l_tot) : 0.0f;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
@@ -393,6 +297,8 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
           if (!qvalid) v = f32x4{0.f, 0.f, 0.f, 0.f};
           const bf16x4 b = __builtin_convertvector(v, bf16x4);
           *(uint2*)(orow + 32 * dt + 8 * g4 + 4 * h) = __builtin_bit_cast(uint2, b);
+          if (a.o32)
+            *(f32x4*)(a.o32 + (head + (int64_t)I * 64 + 32 * w2 + l32) * D + 32 * dt + 8 * g4 + 4 * h) = v;
         }
       }
     }
@@ -555,9 +461,9 @@ int occupancy(K kernel, int threads) {
 
 }  // namespace
 
-extern "C" int fva_attention(fva_plan_t plan, const void* q_perm, const void* k_perm, const void* vt_perm,
-                             const int32_t* row_ptr, const int32_t* col_idx, void* o_perm, int32_t sched_mode,
-                             uint64_t* wg_times, hipStream_t stream) {
+static int attention_launch(fva_plan_t plan, const void* q_perm, const void* k_perm, const void* vt_perm,
+                            const int32_t* row_ptr, const int32_t* col_idx, void* o_perm, int32_t sched_mode,
+                            uint64_t* wg_times, float* lse, float* o32, hipStream_t stream) {
   if (!plan) return fva_fail(FVA_EINVAL, "plan is NULL");
   if (!q_perm || !k_perm || !vt_perm || !o_perm) return fva_fail(FVA_EINVAL, "tensor pointer is NULL");
   if (!row_ptr || !col_idx) return fva_fail(FVA_EINVAL, "row_ptr / col_idx is NULL");
@@ -585,6 +491,8 @@ extern "C" int fva_attention(fva_plan_t plan, const void* q_perm, const void* k_
   a.worklist = plan->worklist;
   a.cursor = plan->counters;
   a.wg_times = wg_times;
+  a.lse = lse;
+  a.o32 = o32;
   a.n_pad = in.n_pad;
   a.n_items = n_bh * ((in.n_blk + G - 1) / G);
   a.n_blk = in.n_blk;
@@ -628,4 +536,21 @@ extern "C" int fva_attention(fva_plan_t plan, const void* q_perm, const void* k_
 #undef FVA_LAUNCH
   return fva_after_launch(stream, "fva_attention");
 
+}
+
+extern "C" int fva_attention(fva_plan_t plan, const void* q_perm, const void* k_perm, const void* vt_perm,
+                             const int32_t* row_ptr, const int32_t* col_idx, void* o_perm, int32_t sched_mode,
+                             uint64_t* wg_times, hipStream_t stream) {
+  return attention_launch(plan, q_perm, k_perm, vt_perm, row_ptr, col_idx, o_perm, sched_mode, wg_times, nullptr,
+                          nullptr, stream);
+}
+
+extern "C" int fva_attention_lse(fva_plan_t plan, const void* q_perm, const void* k_perm, const void* vt_perm,
+                                 const int32_t* row_ptr, const int32_t* col_idx, void* o_perm, float* o32,
+                                 float* lse, hipStream_t stream) {
+  if (!plan) return fva_fail(FVA_EINVAL, "plan is NULL");
+  if (!lse || !o32) return fva_fail(FVA_EINVAL, "lse / o32 is NULL");
+  if (plan->desc.dtype != FVA_DTYPE_BF16) return fva_fail(FVA_EUNSUPPORTED, "the training path is bf16 only");
+  return attention_launch(plan, q_perm, k_perm, vt_perm, row_ptr, col_idx, o_perm, FVA_SCHED_PERSISTENT, nullptr,
+                          lse, o32, stream);
 }

@@ -1,0 +1,512 @@
+// Backward pass of the block-sparse attention over the same block lists as
+// the forward pass ("Video Sparse Attention" explainer, section 3: the
+// sparse kernel serves training as well as inference).  With scaled scores
+// s_ij = q_i . k_j / sqrt(D), P = softmax over the selected keys of each
+// query, and dO the gradient of the output:
+//   dP = dO V^T,  delta_i = sum_d dO_id O_id,  dS = P * (dP - delta)
+//   dQ = dS K / sqrt(D),  dK = dS^T Q / sqrt(D),  dV = P^T dO
+// Two kernels, each owning its outputs outright (no atomics):
+//   k_bwd_dq    one workgroup per query block, walking the block's row of
+//               the selection (like the forward pass);
+//   k_bwd_dkdv  one workgroup per key block, walking the transposed
+//               selection (the query blocks that listed it).
+// P is recomputed from the forward pass's per-query log-sum-exp.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+
+#include "attn_common.h"
+#include "fva_internal.h"
+
+namespace {
+
+using namespace fva_attn;
+
+// ------------------------------------------------------------------ lists
+// CSR -> one 64-bit-word bitmap per row (a row read as a set; ids outside
+// [0, n_blk) dropped).  One wave per row.
+__global__ __launch_bounds__(256) void k_csr_bits(const int32_t* __restrict__ row_ptr,
+                                                  const int32_t* __restrict__ col_idx, int n_blk, int nw,
+                                                  int64_t n_rows, uint64_t* __restrict__ bits) {
+  __shared__ unsigned long long wbuf[4][64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t r = (int64_t)blockIdx.x * 4 + wv;
+  wbuf[wv][lane] = 0;
+  __syncthreads();
+  if (r < n_rows) {
+    const int beg = row_ptr[r], end = row_ptr[r + 1];
+    for (int j = beg + lane; j < end; j += 64) {
+      const int J = col_idx[j];
+      if ((unsigned)J < (unsigned)n_blk) atomicOr(&wbuf[wv][J >> 6], 1ull << (J & 63));
+    }
+  }
+  __syncthreads();
+  if (r < n_rows && lane < nw) bits[r * nw + lane] = wbuf[wv][lane];
+}
+
+// Per-head transpose of the block bitmap, one 64 x 64 bit tile per wave:
+// lane i holds word wj of row 64*wi + i; the ballot of bit c over the lanes
+// is word wi of row 64*wj + c of the transpose.  grid (ceil(nw*nw / 4), B*H).
+__global__ __launch_bounds__(256) void k_bits_transpose(const uint64_t* __restrict__ bits, int n_blk, int nw,
+                                                        uint64_t* __restrict__ bits_t) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= nw * nw) return;   // whole waves; no barrier follows
+  const int wi = t / nw, wj = t - wi * nw;
+  const int64_t head = (int64_t)blockIdx.y * n_blk;
+  const int I = 64 * wi + lane;
+  const uint64_t x = I < n_blk ? bits[(head + I) * nw + wj] : 0;
+  uint64_t out = 0;
+#pragma unroll 8
+  for (int c = 0; c < 64; ++c) {
+    const uint64_t b = __ballot((x >> c) & 1);
+    if (lane == c) out = b;
+  }
+  const int J = 64 * wj + lane;
+  if (J < n_blk) bits_t[(head + J) * nw + wi] = out;
+}
+
+// ------------------------------------------------------------------ kernels
+struct BwdArgs {
+  const uint16_t* q;        // [B*H, n_pad, D] rows
+  const uint16_t* qt;       // Q in the VT layout
+  const uint16_t* k;        // rows
+  const uint16_t* kt;       // K in the VT layout
+  const uint16_t* v;        // rows
+  const float* o32;         // forward output before rounding, rows
+  const float* lse;         // [B*H, n_pad] log2-sum-exp2 of the scaled scores (forward pass)
+  const uint16_t* dout;     // dO rows
+  const uint16_t* dot;      // dO in the VT layout
+  const uint64_t* bits;     // [n_rows][nw] query block -> key blocks
+  const uint64_t* bits_t;   // [n_rows][nw] key block -> query blocks
+  const uint64_t* blk_mask;
+  const uint64_t* blk_full;
+  float* delta;             // [B*H, n_pad]
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  int64_t n_pad;
+  int n_blk;
+  int nw;
+  int n_items;              // B*H*n_blk
+  int chunk;
+  float scale;              // 1/sqrt(D)
+};
+
+// Block handled by this workgroup, dealt XCD-aware (neighbouring blocks of
+// one head share an L2), or -1 past the end.  Wave-uniform.
+__device__ __forceinline__ int bwd_item(const BwdArgs& a) {
+  const int64_t it = xcd_item(blockIdx.x % kXcds, blockIdx.x / kXcds, a.chunk);
+  return it < a.n_items ? (int)it : -1;
+}
+
+// Wait until at most `ahead` steps of this wave's direct loads (PW each) are
+// still in flight.
+template <int PW, int NST>
+__device__ __forceinline__ void wait_steps(int ahead) {
+  static_assert(NST >= 2 && NST <= 3 && (NST - 1) * PW < 64, "vmcnt range");
+  if (NST == 3 && ahead >= 2) wait_vm<(NST == 3 ? 2 * PW : 0)>();
+  else if (ahead >= 1) wait_vm<PW>();
+  else wait_vm<0>();
+}
+
+// bf16x4 store of 4 consecutive fp32 values (times f), or zeros.
+__device__ __forceinline__ void store4(uint16_t* dst, const f32x16& acc, int g4, float f, bool ok) {
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  f32x4 v = {acc[4 * g4] * f, acc[4 * g4 + 1] * f, acc[4 * g4 + 2] * f, acc[4 * g4 + 3] * f};
+  if (!ok) v = f32x4{0.f, 0.f, 0.f, 0.f};
+  *(uint2*)dst = __builtin_bit_cast(uint2, __builtin_convertvector(v, bf16x4));
+}
+
+// Source offsets (bytes within one 32-row half) of a wave's direct loads of
+// a row tile (K-like: XOR swizzle kswz by row) and of a VT tile (vswz by d).
+// Load j of wave w fills LDS bytes [1024 (2j + w), +1024) of the half.
+template <int D, int LPW>
+__device__ __forceinline__ void tile_offsets(int w, int lane, uint32_t* roff, uint32_t* toff) {
+  constexpr int KCH = D / 8;
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) {
+    const int off = (2 * j + w) * 1024 + lane * 16;
+    const int row = off / (KCH * 16), pc = (off / 16) % KCH;
+    roff[j] = row * (D * 2) + ((pc ^ kswz<D>(row)) * 16);
+    const int d = off / 64, pv = (off / 16) & 3;
+    toff[j] = d * 64 + ((pv ^ vswz(d)) * 16);
+  }
+}
+
+// dQ and delta.  Workgroup = 2 waves = one 64-query block; wave w owns
+// queries 32w..32w+31, one per lane pair (lanes l and l+32 split D).  A step
+// is one 32-key half of a listed block:
+//   S^T  (32 keys x 32 queries) = K_half . Q^T      (Q in registers)
+//   dP^T (32 keys x 32 queries) = V_half . dO^T     (dO in registers)
+//   dS^T = P^T * (dP^T - delta),  P^T = exp2(S^T * scale * log2 e - lse)
+//   dQ^T (D x 32 queries) += K^T_half . dS^T        (dS^T straight from the accumulators)
+// K rows, V rows and K^T (VT layout) of each half stream through an
+// NST-stage LDS ring of direct loads, published by one barrier per step.
+template <int D, int NST>
+__global__ __launch_bounds__(128) void k_bwd_dq(BwdArgs a) {
+  constexpr int KS = D / 16, DT = D / 32, KCH = D / 8;
+  constexpr int HALF = 32 * D * 2;
+  constexpr int STAGE = 3 * HALF;
+  constexpr int LPW = HALF / 1024 / 2;  // direct loads per wave per tile
+  constexpr int PW = 3 * LPW;           // per wave per step
+  __shared__ __attribute__((aligned(1024))) uint4 ring[NST * STAGE / 16];
+  const int item = bwd_item(a);
+  if (item < 0) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, l32 = lane & 31;
+  const int bh = item / a.n_blk, I = item - bh * a.n_blk;
+  const int64_t head = (int64_t)bh * a.n_pad;
+  const int64_t tok = head + (int64_t)I * 64 + 32 * w + l32;
+  const float sl2 = a.scale * 1.44269504088896340736f;
+  const bool qvalid = sload(a.blk_mask, I) >> (32 * w + l32) & 1;
+
+  uint32_t roff[LPW], toff[LPW];
+  tile_offsets<D, LPW>(w, lane, roff, toff);
+  const uint64_t rw = lane < a.nw ? a.bits[(int64_t)item * a.nw + lane] : 0;
+  const uint32_t row_lo = (uint32_t)rw, row_hi = (uint32_t)(rw >> 32);
+  const uint64_t fw = lane < a.nw ? a.blk_full[lane] : 0;
+  const uint32_t full_lo = (uint32_t)fw, full_hi = (uint32_t)(fw >> 32);
+
+  // Q, dO in registers (lane: d chunk 2ks + h of its query); delta from O.
+  bf16x8 qreg[KS], doreg[KS];
+  float lse2, delta;
+  {
+    const uint4* qrow = (const uint4*)(a.q + tok * D);
+    const uint4* drow = (const uint4*)(a.dout + tok * D);
+    const f32x8* orow = (const f32x8*)(a.o32 + tok * D);
+    float dl = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qreg[ks] = as_bf16x8(qrow[2 * ks + h]);
+      doreg[ks] = as_bf16x8(drow[2 * ks + h]);
+      const f32x8 ov = orow[2 * ks + h];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dl = fmaf((float)doreg[ks][e], ov[e], dl);
+    }
+    const float dsum = xhalf_sum(dl);   // lanes l and l+32 hold the two halves of D
+    delta = qvalid ? dsum : 0.0f;
+    lse2 = qvalid ? a.lse[tok] : INFINITY;   // pad queries: P = 0
+    // settle these loads before the ring's direct loads are counted
+    wait_vm<0>();
+    if (h == 0) a.delta[tok] = delta;
+  }
+
+  BitWalk iw, cw;
+  const char* kbase = (const char*)(a.k + head * D);
+  const char* vbase = (const char*)(a.v + head * D);
+  const char* tbase = (const char*)(a.kt + head * D);
+  int issued = 0, curJ = 0;
+  bool more = true;
+  auto issue_next = [&]() __attribute__((always_inline)) {
+    if ((issued & 1) == 0) {
+      more = iw.next(row_lo, row_hi, a.nw, &curJ);
+      if (!more) return;
+    }
+    const int u = issued & 1;
+    const int64_t roff0 = ((int64_t)curJ * 64 + 32 * u) * D * 2;
+    const int64_t toff0 = (int64_t)curJ * 64 * D * 2 + u * HALF;
+    const uint32_t dst = lds_addr(ring) + (issued % NST) * STAGE;
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+      const uint32_t o1 = (2 * j + w) * 1024;
+      dma16(kbase + roff0, roff[j], dst + o1);
+      dma16(vbase + roff0, roff[j], dst + HALF + o1);
+      dma16(tbase + toff0, toff[j], dst + 2 * HALF + o1);
+    }
+    ++issued;
+  };
+
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+#pragma unroll
+  for (int st = 0; st < NST - 1; ++st)
+    if (more) issue_next();
+
+  int J = 0;
+  bool full = false;
+  for (int st = 0; st < issued; ++st) {
+    if ((st & 1) == 0) {
+      cw.next(row_lo, row_hi, a.nw, &J);
+      full = lane_word(full_lo, full_hi, J >> 6) >> (J & 63) & 1;
+    }
+    wait_steps<PW, NST>(issued - 1 - st);
+    barrier_no_fence();
+    if (more) issue_next();
+
+    const int u = st & 1;
+    const uint32_t mh = full ? 0xFFFFFFFFu : (uint32_t)(sload(a.blk_mask, J) >> (32 * u));
+    if (mh == 0) continue;   // a half of pad keys
+    const uint4* kst = ring + (st % NST) * (STAGE / 16);
+    const uint4* vst = kst + HALF / 16;
+    const uint4* tst = kst + 2 * HALF / 16;
+    f32x16 s = {}, dp = {};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int c = l32 * KCH + ((2 * ks + h) ^ kswz<D>(l32));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kst[c]), qreg[ks], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vst[c]), doreg[ks], dp, 0, 0, 0);
+    }
+    // element i: key 8*(i/4) + 4*h + i%4 of this half, query l32
+    f32x8 d0, d1;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = 8 * (i >> 2) + 4 * h + (i & 3);
+      float p = __builtin_amdgcn_exp2f(fmaf(s[i], sl2, -lse2));
+      if (!(mh >> key & 1)) p = 0.0f;
+      const float ds = p * (dp[i] - delta);
+      if (i < 8) d0[i] = ds;
+      else d1[i - 8] = ds;
+    }
+    const bf16x8 db0 = __builtin_convertvector(d0, bf16x8);
+    const bf16x8 db1 = __builtin_convertvector(d1, bf16x8);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int d = 32 * dt + l32;
+      const int sw = vswz(d);
+      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(tst[d * 4 + ((0 + h) ^ sw)]), db0, acc[dt], 0, 0, 0);
+      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(tst[d * 4 + ((2 + h) ^ sw)]), db1, acc[dt], 0, 0, 0);
+    }
+  }
+  // acc[dt][r]: dQ^T[32 dt + 8 (r/4) + 4 h + r%4][query l32]
+  uint16_t* out = a.dq + tok * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) store4(out + 32 * dt + 8 * g4 + 4 * h, acc[dt], g4, a.scale, qvalid);
+}
+
+// dK and dV.  Workgroup = 2 waves = one 64-key block; wave w owns keys
+// 32w..32w+31 (K and V rows in registers).  A step is one 32-query half of
+// a query block that listed this key block:
+//   S  (32 queries x 32 keys) = Q_half . K^T,   dP = dO_half . V^T
+//   P = exp2(S * scale * log2 e - lse),  dS = P * (dP - delta)
+//   dV^T (D x 32 keys) += dO^T_half . P,   dK^T += Q^T_half . dS
+// The ring stage holds Q rows, dO rows, Q^T and dO^T (VT layout) of the
+// half, and the half's 32 lse and 32 delta values.
+template <int D, int NST>
+__global__ __launch_bounds__(128) void k_bwd_dkdv(BwdArgs a) {
+  constexpr int KS = D / 16, DT = D / 32, KCH = D / 8;
+  constexpr int HALF = 32 * D * 2;
+  constexpr int STAGE = 4 * HALF + 256;
+  constexpr int LPW = HALF / 1024 / 2;
+  constexpr int PW = 4 * LPW + 1;
+  __shared__ __attribute__((aligned(1024))) uint4 ring[NST * STAGE / 16];
+  const int item = bwd_item(a);
+  if (item < 0) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, l32 = lane & 31;
+  const int bh = item / a.n_blk, J = item - bh * a.n_blk;
+  const int64_t head = (int64_t)bh * a.n_pad;
+  const int64_t tok = head + (int64_t)J * 64 + 32 * w + l32;   // this lane's key token
+  const float sl2 = a.scale * 1.44269504088896340736f;
+  const uint32_t kmask = (uint32_t)(sload(a.blk_mask, J) >> (32 * w));
+  const bool kvalid = kmask >> l32 & 1;
+
+  uint32_t roff[LPW], toff[LPW];
+  tile_offsets<D, LPW>(w, lane, roff, toff);
+  const uint64_t cwd = lane < a.nw ? a.bits_t[(int64_t)item * a.nw + lane] : 0;
+  const uint32_t col_lo = (uint32_t)cwd, col_hi = (uint32_t)(cwd >> 32);
+
+  bf16x8 kreg[KS], vreg[KS];
+  {
+    const uint4* krow = (const uint4*)(a.k + tok * D);
+    const uint4* vrow = (const uint4*)(a.v + tok * D);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kreg[ks] = as_bf16x8(krow[2 * ks + h]);
+      vreg[ks] = as_bf16x8(vrow[2 * ks + h]);
+    }
+    wait_vm<0>();
+  }
+
+  BitWalk iw, cw;
+  const char* qbase = (const char*)(a.q + head * D);
+  const char* dbase = (const char*)(a.dout + head * D);
+  const char* qtbase = (const char*)(a.qt + head * D);
+  const char* dtbase = (const char*)(a.dot + head * D);
+  // wave 0 brings the half's lse values, wave 1 its delta values
+  const float* lbase = (w == 0 ? a.lse : (const float*)a.delta) + head;
+  int issued = 0, curI = 0;
+  bool more = true;
+  auto issue_next = [&]() __attribute__((always_inline)) {
+    if ((issued & 1) == 0) {
+      more = iw.next(col_lo, col_hi, a.nw, &curI);
+      if (!more) return;
+    }
+    const int u = issued & 1;
+    const int64_t roff0 = ((int64_t)curI * 64 + 32 * u) * D * 2;
+    const int64_t toff0 = (int64_t)curI * 64 * D * 2 + u * HALF;
+    const uint32_t dst = lds_addr(ring) + (issued % NST) * STAGE;
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+      const uint32_t o1 = (2 * j + w) * 1024;
+      dma16(qbase + roff0, roff[j], dst + o1);
+      dma16(dbase + roff0, roff[j], dst + HALF + o1);
+      dma16(qtbase + toff0, toff[j], dst + 2 * HALF + o1);
+      dma16(dtbase + toff0, toff[j], dst + 3 * HALF + o1);
+    }
+    if (lane < 8) dma16(lbase + (int64_t)curI * 64 + 32 * u, lane * 16, dst + 4 * HALF + 128 * w);
+    ++issued;
+  };
+
+  f32x16 dk[DT], dv[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dk[dt] = dv[dt] = f32x16{};
+#pragma unroll
+  for (int st = 0; st < NST - 1; ++st)
+    if (more) issue_next();
+
+  int I = 0;
+  uint64_t qm64 = 0;
+  for (int st = 0; st < issued; ++st) {
+    if ((st & 1) == 0) {
+      cw.next(col_lo, col_hi, a.nw, &I);
+      qm64 = sload(a.blk_mask, I);
+    }
+    wait_steps<PW, NST>(issued - 1 - st);
+    barrier_no_fence();
+    if (more) issue_next();
+
+    const int u = st & 1;
+    const uint32_t qm = (uint32_t)(qm64 >> (32 * u));
+    if (qm == 0 || kmask == 0) continue;   // a half of pad queries, or a wave of pad keys
+    const uint4* qst = ring + (st % NST) * (STAGE / 16);
+    const uint4* dst_ = qst + HALF / 16;
+    const uint4* qtst = qst + 2 * HALF / 16;
+    const uint4* dtst = qst + 3 * HALF / 16;
+    const float* lds_l = (const float*)(qst + 4 * HALF / 16);
+    f32x16 s = {}, dp = {};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int c = l32 * KCH + ((2 * ks + h) ^ kswz<D>(l32));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qst[c]), kreg[ks], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(dst_[c]), vreg[ks], dp, 0, 0, 0);
+    }
+    // element r: query 8*(r/4) + 4*h + r%4 of this half, key l32
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    f32x8 p0, p1, d0, d1;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const f32x4 L = *(const f32x4*)(lds_l + 8 * c + 4 * h);
+      const f32x4 Dl = *(const f32x4*)(lds_l + 32 + 8 * c + 4 * h);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 4 * c + j, qi = 8 * c + 4 * h + j;
+        float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -L[j]));
+        if (!(qm >> qi & 1) || !kvalid) p = 0.0f;
+        const float ds = p * (dp[r] - Dl[j]);
+        if (r < 8) { p0[r] = p; d0[r] = ds; }
+        else { p1[r - 8] = p; d1[r - 8] = ds; }
+      }
+    }
+    const bf16x8 pb0 = __builtin_convertvector(p0, bf16x8), pb1 = __builtin_convertvector(p1, bf16x8);
+    const bf16x8 db0 = __builtin_convertvector(d0, bf16x8), db1 = __builtin_convertvector(d1, bf16x8);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int d = 32 * dt + l32;
+      const int sw = vswz(d);
+      const int c0 = d * 4 + ((0 + h) ^ sw), c1 = d * 4 + ((2 + h) ^ sw);
+      dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(dtst[c0]), pb0, dv[dt], 0, 0, 0);
+      dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(dtst[c1]), pb1, dv[dt], 0, 0, 0);
+      dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qtst[c0]), db0, dk[dt], 0, 0, 0);
+      dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qtst[c1]), db1, dk[dt], 0, 0, 0);
+    }
+  }
+  // dk[dt][r], dv[dt][r]: [32 dt + 8 (r/4) + 4 h + r%4][key l32]
+  uint16_t* ok = a.dk + tok * D;
+  uint16_t* ov = a.dv + tok * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      store4(ok + 32 * dt + 8 * g4 + 4 * h, dk[dt], g4, a.scale, kvalid);
+      store4(ov + 32 * dt + 8 * g4 + 4 * h, dv[dt], g4, 1.0f, kvalid);
+    }
+}
+
+// Blocks per XCD chunk of the backward grids; FVA_BWD_CHUNK overrides it.
+int bwd_chunk() {
+  const char* v = getenv("FVA_BWD_CHUNK");
+  int n = v ? atoi(v) : 16;
+  if (n < 1 || n > 4096) n = 16;
+  return n;
+}
+
+// Row bitmaps of a CSR and their per-head transpose into the plan's workspace.
+void launch_lists(fva_plan_t plan, const int32_t* row_ptr, const int32_t* col_idx, hipStream_t stream) {
+  const fva_plan_info& in = plan->info;
+  const int n_bh = plan->desc.batch * plan->desc.heads;
+  hipLaunchKernelGGL(k_csr_bits, dim3((unsigned)((in.n_rows + 3) / 4)), dim3(256), 0, stream, row_ptr, col_idx,
+                     (int)in.n_blk, plan->nw, in.n_rows, plan->rowmask);
+  hipLaunchKernelGGL(k_bits_transpose, dim3((unsigned)((plan->nw * plan->nw + 3) / 4), n_bh), dim3(256), 0, stream,
+                     plan->rowmask, (int)in.n_blk, plan->nw, plan->bits_t);
+}
+
+}  // namespace
+
+extern "C" int fva_mask_transpose(fva_plan_t plan, const int32_t* row_ptr, const int32_t* col_idx,
+                                  int32_t* t_row_ptr, int32_t* t_col_idx, hipStream_t stream) {
+  if (!plan) return fva_fail(FVA_EINVAL, "plan is NULL");
+  if (!row_ptr || !col_idx || !t_row_ptr || !t_col_idx)
+    return fva_fail(FVA_EINVAL, "row_ptr / col_idx / t_row_ptr / t_col_idx is NULL");
+  launch_lists(plan, row_ptr, col_idx, stream);
+  const int rc = fva_bits_to_csr(plan, plan->bits_t, t_row_ptr, t_col_idx, stream);
+  if (rc != FVA_OK) return rc;
+  return fva_after_launch(stream, "fva_mask_transpose");
+}
+
+extern "C" int fva_attention_backward(fva_plan_t plan, const void* q_perm, const void* q_vt, const void* k_perm,
+                                      const void* k_vt, const void* v_perm, const float* o32, const float* lse,
+                                      const void* do_perm, const void* do_vt, const int32_t* row_ptr,
+                                      const int32_t* col_idx, void* dq_perm, void* dk_perm, void* dv_perm,
+                                      hipStream_t stream) {
+  if (!plan) return fva_fail(FVA_EINVAL, "plan is NULL");
+  if (!q_perm || !q_vt || !k_perm || !k_vt || !v_perm || !o32 || !lse || !do_perm || !do_vt)
+    return fva_fail(FVA_EINVAL, "input pointer is NULL");
+  if (!row_ptr || !col_idx) return fva_fail(FVA_EINVAL, "row_ptr / col_idx is NULL");
+  if (!dq_perm || !dk_perm || !dv_perm) return fva_fail(FVA_EINVAL, "gradient pointer is NULL");
+  const fva_plan_desc& d = plan->desc;
+  const fva_plan_info& in = plan->info;
+  if (d.dtype != FVA_DTYPE_BF16) return fva_fail(FVA_EUNSUPPORTED, "the backward pass is bf16 only");
+  launch_lists(plan, row_ptr, col_idx, stream);
+  BwdArgs a{};
+  a.q = (const uint16_t*)q_perm;
+  a.qt = (const uint16_t*)q_vt;
+  a.k = (const uint16_t*)k_perm;
+  a.kt = (const uint16_t*)k_vt;
+  a.v = (const uint16_t*)v_perm;
+  a.o32 = o32;
+  a.lse = lse;
+  a.dout = (const uint16_t*)do_perm;
+  a.dot = (const uint16_t*)do_vt;
+  a.bits = plan->rowmask;
+  a.bits_t = plan->bits_t;
+  a.blk_mask = plan->blk_mask;
+  a.blk_full = plan->blk_full;
+  a.delta = plan->bwd_delta;
+  a.dq = (uint16_t*)dq_perm;
+  a.dk = (uint16_t*)dk_perm;
+  a.dv = (uint16_t*)dv_perm;
+  a.n_pad = in.n_pad;
+  a.n_blk = (int)in.n_blk;
+  a.nw = plan->nw;
+  a.n_items = (int)in.n_rows;
+  a.chunk = bwd_chunk();
+  a.scale = 1.0f / sqrtf((float)d.head_dim);
+  const int deal = kXcds * a.chunk;
+  const dim3 grid((unsigned)((a.n_items + deal - 1) / deal * deal));
+  if (d.head_dim == 128) {
+    hipLaunchKernelGGL((k_bwd_dq<128, 2>), grid, dim3(128), 0, stream, a);
+    hipLaunchKernelGGL((k_bwd_dkdv<128, 2>), grid, dim3(128), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((k_bwd_dq<64, 2>), grid, dim3(128), 0, stream, a);
+    hipLaunchKernelGGL((k_bwd_dkdv<64, 2>), grid, dim3(128), 0, stream, a);
+  }
+  return fva_after_launch(stream, "fva_attention_backward");
+}

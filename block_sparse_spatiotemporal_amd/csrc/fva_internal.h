@@ -45,6 +45,8 @@ struct fva_plan_s {
   uint32_t* slack_hist;// [B*H][256] digit histogram of the slack radix select (kept zero between calls)
   int32_t* slack_need; // [B*H] pairs still to place below the current prefix
   double2* rope_tab;  // [(T+H+W) * D/2] rotary (cos, sin) of the last fva_permute_rope call
+  float* bwd_delta;   // [B*H*n_pad] backward: rowsum(dO * O) per query token
+  uint64_t* bits_t;   // [n_rows][nw] backward: transposed per-head block bitmap (key block -> query blocks)
   int32_t* worklist;  // [n_rows] attention rows in schedule order
   int32_t* counters;  // [64] work-queue cursor and misc counters
 
@@ -64,3 +66,7 @@ int fva_debug_enabled();
 struct SelectArgs {
   float p[FVA_MAX_PHEAD];
 };
+
+// Per-row id masks -> CSR (ascending ids) using the plan's selection
+// workspace (row counts, head totals and offsets).
+int fva_bits_to_csr(fva_plan_t plan, const uint64_t* bits, int32_t* row_ptr, int32_t* col_idx, hipStream_t stream);

@@ -6,9 +6,12 @@
 
 #include <algorithm>
 
+#include "attn_common.h"
 #include "fva_internal.h"
 
 namespace {
+
+using fva_attn::vt_slot_key;
 
 constexpr int kThreads = 256;
 
@@ -96,16 +99,6 @@ __global__ __launch_bounds__(kThreads) void k_unpermute_rows(const uint4* __rest
       dst[(((int64_t)b * n_tok + tok[u]) * heads + h) * cpr + ch] = v[u];
     }
   }
-}
-
-// Key slot order inside one 32-key half of the VT layout: slot s holds key
-// 16*c + 8*(j/4) + 4*g + j%4 with c = s/16, g = (s%16)/8, j = s%8.  This is
-// the key order in which a 32x32x16 bf16 matrix-core instruction's B-operand
-// lanes receive P^T when P^T comes straight from the S^T accumulators, so the
-// matching A operand (V^T) is one contiguous 16-byte load per lane.
-__device__ __forceinline__ int vt_slot_key(int s) {
-  const int c = s >> 4, g = (s >> 3) & 1, j = s & 7;
-  return 16 * c + 8 * (j >> 2) + 4 * g + (j & 3);
 }
 
 // One workgroup per (b, h, block).  The block's 64 rows come in as 16-byte

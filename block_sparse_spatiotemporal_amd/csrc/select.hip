@@ -922,3 +922,30 @@ extern "C" int fva_mask_overlap(fva_plan_t plan, const int32_t* row_ptr_a, const
                      col_idx_a, row_ptr_b, col_idx_b, (int)in.n_blk, in.n_rows, (unsigned long long*)counts);
   return fva_after_launch(stream, "fva_mask_overlap");
 }
+
+// Per-row 64-bit id masks ([n_rows][nw]) -> CSR with ascending ids, through
+// the selection's row-count, two-level scan and emit kernels.
+namespace {
+__global__ __launch_bounds__(256) void k_bits_rowcnt(const uint64_t* __restrict__ bits, int nw, int64_t n_rows,
+                                                     int32_t* __restrict__ cnt) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r >= n_rows) return;
+  int c = 0;
+  for (int i = 0; i < nw; ++i) c += __popcll(bits[r * nw + i]);
+  cnt[r] = c;
+}
+}  // namespace
+
+int fva_bits_to_csr(fva_plan_t plan, const uint64_t* bits, int32_t* row_ptr, int32_t* col_idx, hipStream_t stream) {
+  const fva_plan_info& in = plan->info;
+  const int n_bh = plan->desc.batch * plan->desc.heads;
+  hipLaunchKernelGGL(k_bits_rowcnt, dim3((unsigned)((in.n_rows + 255) / 256)), dim3(256), 0, stream, bits, plan->nw,
+                     in.n_rows, plan->rowcnt);
+  hipLaunchKernelGGL(k_scan_rows, dim3(n_bh), dim3(1024), 0, stream, plan->rowcnt, (int)in.n_blk, row_ptr,
+                     plan->headcnt);
+  hipLaunchKernelGGL(k_scan_heads, dim3(1), dim3(1024), 0, stream, plan->headcnt, n_bh, plan->headoff,
+                     (int32_t*)nullptr, row_ptr, in.n_rows);
+  hipLaunchKernelGGL(k_emit, dim3((unsigned)((in.n_rows + 3) / 4)), dim3(256), 0, stream, bits, row_ptr,
+                     plan->headoff, col_idx, plan->nw, (int)in.n_blk, in.n_rows);
+  return FVA_OK;
+}

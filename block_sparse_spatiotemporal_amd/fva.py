@@ -8,6 +8,7 @@ module raises: there is no fallback path.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import re
 
@@ -70,6 +71,9 @@ def lib() -> ctypes.CDLL:
             "fva_mask_overlap": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
             "fva_mask_accumulate": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp]),
             "fva_mask_from_counts": (c_i32, [c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp]),
+            "fva_attention_lse": (c_i32, [c_vp] * 10),
+            "fva_attention_backward": (c_i32, [c_vp] * 16),
+            "fva_mask_transpose": (c_i32, [c_vp] * 6),
             "fva_last_error": (ctypes.c_char_p, []),
         }
         for name, (res, args) in sig.items():
@@ -280,6 +284,46 @@ def fva_attention(plan: Plan, q_perm, k_perm, vt_perm, row_ptr, col_idx, o_perm,
                                _ptr(wg_times), _stream(stream)))
 
 
+def fva_attention_lse(plan: Plan, q_perm, k_perm, vt_perm, row_ptr, col_idx, o_perm, o32, lse, stream=None):
+    for t, n in ((q_perm, "q_perm"), (k_perm, "k_perm"), (o_perm, "o_perm")):
+        _expect(t, plan.perm_shape(), plan.torch_dtype, n)
+    if vt_perm.numel() != o_perm.numel() or vt_perm.dtype != plan.torch_dtype:
+        raise ValueError("vt_perm has the wrong size or dtype")
+    _expect(row_ptr, (plan.n_rows + 1,), torch.int32, "row_ptr")
+    _expect(lse, plan.perm_shape()[:3], torch.float32, "lse")
+    _expect(o32, plan.perm_shape(), torch.float32, "o32")
+    _check(lib().fva_attention_lse(plan.handle, _ptr(q_perm), _ptr(k_perm), _ptr(vt_perm), _ptr(row_ptr),
+                                   _ptr(col_idx), _ptr(o_perm), _ptr(o32), _ptr(lse), _stream(stream)))
+
+
+def fva_attention_backward(plan: Plan, q_perm, q_vt, k_perm, k_vt, v_perm, o32, lse, do_perm, do_vt,
+                           row_ptr, col_idx, dq_perm, dk_perm, dv_perm, stream=None):
+    shp = plan.perm_shape()
+    for t, n in ((q_perm, "q_perm"), (q_vt, "q_vt"), (k_perm, "k_perm"), (k_vt, "k_vt"), (v_perm, "v_perm"),
+                 (do_perm, "do_perm"), (do_vt, "do_vt"), (dq_perm, "dq_perm"),
+                 (dk_perm, "dk_perm"), (dv_perm, "dv_perm")):
+        if t.numel() != math.prod(shp) or t.dtype != plan.torch_dtype or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous {plan.torch_dtype} tensor of {math.prod(shp)} elements")
+    _expect(o32, shp, torch.float32, "o32")
+    _expect(lse, shp[:3], torch.float32, "lse")
+    _expect(row_ptr, (plan.n_rows + 1,), torch.int32, "row_ptr")
+    if col_idx.dtype != torch.int32:
+        raise ValueError("col_idx must be int32")
+    _check(lib().fva_attention_backward(plan.handle, _ptr(q_perm), _ptr(q_vt), _ptr(k_perm), _ptr(k_vt),
+                                        _ptr(v_perm), _ptr(o32), _ptr(lse), _ptr(do_perm), _ptr(do_vt),
+                                        _ptr(row_ptr), _ptr(col_idx), _ptr(dq_perm), _ptr(dk_perm), _ptr(dv_perm),
+                                        _stream(stream)))
+
+
+def fva_mask_transpose(plan: Plan, row_ptr, col_idx, t_row_ptr, t_col_idx, stream=None):
+    _expect(row_ptr, (plan.n_rows + 1,), torch.int32, "row_ptr")
+    _expect(t_row_ptr, (plan.n_rows + 1,), torch.int32, "t_row_ptr")
+    if col_idx.dtype != torch.int32 or t_col_idx.dtype != torch.int32:
+        raise ValueError("col_idx / t_col_idx must be int32")
+    _check(lib().fva_mask_transpose(plan.handle, _ptr(row_ptr), _ptr(col_idx), _ptr(t_row_ptr), _ptr(t_col_idx),
+                                    _stream(stream)))
+
+
 class Buffers:
     """Device buffers for one full call on a plan (block-order Q/K/V^T/O,
     CSR lists, per-head counts), allocated once and reused."""
@@ -308,3 +352,46 @@ def attention_call(plan: Plan, q, k, v, out, p, k_min, bufs: Buffers, slack="non
     fva_attention(plan, bufs.q, bufs.k, bufs.vt, bufs.row_ptr, bufs.col_idx, bufs.o, sched=sched,
                   wg_times=wg_times, stream=stream)
     fva_unpermute(plan, bufs.o, out, stream)
+
+
+class TrainBuffers:
+    """Extra block-order buffers of a training call: the VT layouts of Q, K
+    and dO, V and dO in rows, the fp32 output and per-query log-sum-exp of
+    the forward pass, the gradients."""
+
+    def __init__(self, plan: Plan):
+        dev = torch.device("cuda")
+        shp = plan.perm_shape()
+        mk = lambda: torch.empty(shp, dtype=plan.torch_dtype, device=dev)
+        self.q_vt, self.k_vt, self.v, self.do, self.do_vt = mk(), mk(), mk(), mk(), mk()
+        self.dq, self.dk, self.dv = mk(), mk(), mk()
+        self.lse = torch.empty(shp[:3], dtype=torch.float32, device=dev)
+        self.o32 = torch.empty(shp, dtype=torch.float32, device=dev)
+
+
+def attention_forward_train(plan: Plan, q, k, v, out, p, k_min, bufs: Buffers, tb: TrainBuffers, slack="none",
+                            stream=None):
+    """Forward pass of a training step: permute, select, attention with the
+    per-query log-sum-exp kept for the backward pass, unpermute."""
+    fva_permute(plan, q, bufs.q, LAYOUT_ROWS, stream)
+    fva_permute(plan, k, bufs.k, LAYOUT_ROWS, stream)
+    fva_permute(plan, v, bufs.vt, LAYOUT_VT, stream)
+    fva_select(plan, bufs.q, bufs.k, p, k_min, bufs.row_ptr, bufs.col_idx, slack=slack, head_nnz=bufs.head_nnz,
+               stream=stream)
+    fva_attention_lse(plan, bufs.q, bufs.k, bufs.vt, bufs.row_ptr, bufs.col_idx, bufs.o, tb.o32, tb.lse, stream)
+    fva_unpermute(plan, bufs.o, out, stream)
+
+
+def attention_backward_call(plan: Plan, q, k, v, dout, dq, dk, dv, bufs: Buffers, tb: TrainBuffers, stream=None):
+    """Backward pass after attention_forward_train on the same buffers:
+    raster dO in, raster dQ, dK, dV out (same lists as the forward pass)."""
+    fva_permute(plan, q, tb.q_vt, LAYOUT_VT, stream)
+    fva_permute(plan, k, tb.k_vt, LAYOUT_VT, stream)
+    fva_permute(plan, v, tb.v, LAYOUT_ROWS, stream)
+    fva_permute(plan, dout, tb.do, LAYOUT_ROWS, stream)
+    fva_permute(plan, dout, tb.do_vt, LAYOUT_VT, stream)
+    fva_attention_backward(plan, bufs.q, tb.q_vt, bufs.k, tb.k_vt, tb.v, tb.o32, tb.lse, tb.do, tb.do_vt,
+                           bufs.row_ptr, bufs.col_idx, tb.dq, tb.dk, tb.dv, stream)
+    fva_unpermute(plan, tb.dq, dq, stream)
+    fva_unpermute(plan, tb.dk, dk, stream)
+    fva_unpermute(plan, tb.dv, dv, stream)

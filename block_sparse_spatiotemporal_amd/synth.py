@@ -41,7 +41,7 @@ import numpy as np
 from scipy.ndimage import gaussian_filter1d
 
 # tensor ids inside a spawn key
-_T_FIELD, _T_Q, _T_K, _T_V, _T_FIELD_K = 0, 1, 2, 3, 4
+_T_FIELD, _T_Q, _T_K, _T_V, _T_FIELD_K, _T_DO = 0, 1, 2, 3, 4, 5
 _HEAD_PARAMS = 1000  # spawn-key slot for per-head parameters
 
 
@@ -224,3 +224,22 @@ def make(w: Workload, threads: int | None = None, heads=None):
         list(ex.map(work, pairs))
     meta = {"p_head": p, "sigma_head": sig, "near_dense": dense}
     return q, k, v, meta
+
+
+def make_dout(w: Workload, threads: int | None = None, heads=None, scale: float = 1.0):
+    """Seeded output gradient dO of shape [B, N, H, D] for the backward
+    pass: N(0, scale^2) per element, one independent stream per (b, h), in
+    the workload's storage type (``heads`` as for ``make``)."""
+    st = np.uint16 if w.dtype == "bf16" else np.float32
+    out = np.zeros((w.B, w.n_tokens, w.H, w.D), dtype=st)
+    pairs = heads if heads is not None else [(b, h) for b in range(w.B) for h in range(w.H)]
+
+    def work(bh):
+        b, h = bh
+        x = scale * _rng(w.seed, b, h, _T_DO).standard_normal((w.n_tokens, w.D), dtype=np.float32)
+        out[b, :, h, :] = f32_to_bf16_bits(x) if w.dtype == "bf16" else x
+
+    nthr = threads or min(16, len(os.sched_getaffinity(0)))
+    with ThreadPoolExecutor(max_workers=nthr) as ex:
+        list(ex.map(work, pairs))
+    return out

@@ -227,6 +227,56 @@ int fva_attention(fva_plan_t plan, const void* q_perm, const void* k_perm, const
                   const int32_t* row_ptr, const int32_t* col_idx, void* o_perm,
                   int32_t sched_mode, uint64_t* wg_times, hipStream_t stream);
 
+/* Forward pass of a training step: fva_attention that also keeps what the
+ * backward pass needs.
+ *   lse   device fp32 [B, H, N_pad], overwritten: per query token the
+ *         log2-sum-exp2 of its scaled scores over the listed keys,
+ *           lse[(b*H + h)*N_pad + t] = log2 sum_j exp(q_t . k_j / sqrt(D)),
+ *         for valid tokens with a non-empty row, 0 otherwise (the softmax
+ *         normaliser P is recomputed from);
+ *   o32   device fp32 [B, H, N_pad, D], overwritten: o_perm before its
+ *         rounding to bf16 (delta = rowsum(dO * O) is taken from it: the
+ *         bf16 rounding of O would enter every dQ row multiplied by the
+ *         mean of its listed keys).
+ * Persistent schedule; bf16 plans only (FVA_EUNSUPPORTED otherwise).
+ * Errors: FVA_EINVAL for NULL pointers. */
+int fva_attention_lse(fva_plan_t plan, const void* q_perm, const void* k_perm, const void* vt_perm,
+                      const int32_t* row_ptr, const int32_t* col_idx, void* o_perm, float* o32, float* lse,
+                      hipStream_t stream);
+
+/* Gradients of fva_attention for training ("Video Sparse Attention"
+ * explainer, section 3: the same block lists drive the forward and the
+ * backward kernels).  With s_ij = q_i . k_j / sqrt(D) and P the softmax of
+ * row i over the valid keys of its listed blocks:
+ *   dP = dO V^T,  delta_i = sum_d dO_id O_id,  dS = P * (dP - delta)
+ *   dQ = dS K / sqrt(D),  dK = dS^T Q / sqrt(D),  dV = P^T dO
+ * Arguments (block order, bf16, B*H heads of N_pad tokens):
+ *   q_perm, k_perm, v_perm, do_perm   FVA_LAYOUT_ROWS (fva_permute);
+ *   q_vt, k_vt, do_vt                 the same tensors in FVA_LAYOUT_VT;
+ *   o32, lse                          outputs of fva_attention_lse on the
+ *                                     same Q, K, V and lists;
+ *   row_ptr, col_idx                  the forward pass's CSR (set semantics);
+ *   dq_perm, dk_perm, dv_perm         FVA_LAYOUT_ROWS, overwritten; pad
+ *                                     tokens and tokens no list reaches get 0.
+ * All products on bf16 matrix cores with fp32 accumulation; P and dS are
+ * rounded to bf16 as operands, the gradients to bf16 at the end.  Uses the
+ * plan's workspace (not safe to overlap with other calls on the plan).
+ * Errors: FVA_EINVAL for NULL pointers, FVA_EUNSUPPORTED for fp32 plans. */
+int fva_attention_backward(fva_plan_t plan, const void* q_perm, const void* q_vt, const void* k_perm,
+                           const void* k_vt, const void* v_perm, const float* o32, const float* lse,
+                           const void* do_perm, const void* do_vt, const int32_t* row_ptr,
+                           const int32_t* col_idx, void* dq_perm, void* dk_perm, void* dv_perm,
+                           hipStream_t stream);
+
+/* Transposed block lists: row (b, h, J) of the output lists, ascending, the
+ * query blocks I whose row (b, h, I) of the input lists holds J (input rows
+ * read as sets).  These are the lists the backward pass walks for dK, dV.
+ *   t_row_ptr   device int32 [n_rows + 1];
+ *   t_col_idx   device int32, capacity >= the input's distinct in-range ids.
+ * Errors: FVA_EINVAL for NULL pointers. */
+int fva_mask_transpose(fva_plan_t plan, const int32_t* row_ptr, const int32_t* col_idx,
+                       int32_t* t_row_ptr, int32_t* t_col_idx, hipStream_t stream);
+
 /* Agreement of two block selections, for reusing a cached selection across
  * denoising steps ("DFSAttn" explainer, trick 3: blocks that mattered at an
  * earlier step are remembered instead of re-evaluated; fva_attention accepts

@@ -505,3 +505,44 @@ def attention_backward(q_perm, k_perm, v_perm, do_perm, row_ptr, col_idx, pl: Pl
                 np.add.at(dk[b, h], krows, dS.T @ Q * scale)
                 np.add.at(dv[b, h], krows, P.T @ dO)
     return dq, dk, dv
+
+
+# --------------------------------------------------------------------------
+# Softmax normaliser of each query row, the value the backward pass rebuilds
+# P from (same lists and scale as ``attention``): in base-2 units,
+#   lse_i = log2 sum_j exp(q_i . k_j / sqrt(D))
+# over the valid key tokens j of the listed blocks; 0 for pad queries and
+# rows with no listed block.  Result [B, H, n_pad].
+def attention_lse(q_perm, k_perm, row_ptr, col_idx, pl: Plan) -> np.ndarray:
+    B, H, n_pad, D = q_perm.shape
+    n, bs = pl.n_blk, pl.blk_size
+    out = np.zeros((B, H, n_pad), dtype=np.float64)
+    valid = pl.perm >= 0
+    scale = 1.0 / math.sqrt(D)
+    for b in range(B):
+        for h in range(H):
+            for i in range(n):
+                r = (b * H + h) * n + i
+                blocks = col_idx[row_ptr[r]:row_ptr[r + 1]]
+                qrows = np.nonzero(valid[i * bs:(i + 1) * bs])[0] + i * bs
+                if len(blocks) == 0 or len(qrows) == 0:
+                    continue
+                krows = np.concatenate([np.nonzero(valid[j * bs:(j + 1) * bs])[0] + j * bs for j in blocks])
+                z = q_perm[b, h, qrows] @ k_perm[b, h, krows].T * scale
+                m = z.max(axis=1)
+                out[b, h, qrows] = (m + np.log(np.exp(z - m[:, None]).sum(axis=1))) / math.log(2.0)
+    return out
+
+
+# Transposed lists: row (b, h, J) holds, ascending, every query block I whose
+# row (b, h, I) lists J (rows read as sets, ids outside [0, n_blk) ignored) --
+# the key-block-major view the dK / dV gradients are gathered over.
+def mask_transpose(row_ptr, col_idx, B: int, H: int, n_blk: int):
+    rows = [[] for _ in range(B * H * n_blk)]
+    for bh in range(B * H):
+        for i in range(n_blk):
+            r = bh * n_blk + i
+            for j in sorted(set(int(x) for x in col_idx[row_ptr[r]:row_ptr[r + 1]])):
+                if 0 <= j < n_blk:
+                    rows[bh * n_blk + j].append(i)
+    return to_csr([np.array(x, dtype=np.int64) for x in rows])

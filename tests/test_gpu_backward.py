@@ -1,0 +1,252 @@
+"""Backward pass of the block-sparse attention (fva_attention_backward, with
+fva_attention_lse and fva_mask_transpose) against the fp64 oracle.
+
+* transposed lists: bit-exact;
+* log-sum-exp: within 2e-3 (base-2 units) of the oracle's;
+* dQ, dK, dV: per head and tensor, max |GPU - oracle| <= 2e-2 * max |oracle|
+  (bf16 operands P and dS, bf16 gradients; the oracle runs in fp64 on the
+  same bf16 inputs), and exact zeros where the pages' definition gives zero
+  (pad tokens, key blocks no row lists, query blocks with empty rows).
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_spatiotemporal_amd import fva, synth
+from oracle import fva_oracle as O
+from tests._helpers import to_dev
+
+pytestmark = pytest.mark.gpu
+
+GRAD_TOL = 2e-2
+LSE_TOL = 2e-3
+
+
+def _dev_i32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+
+def _rand_lists(rng, n_rows, n, density, junk=False, empty_frac=0.1):
+    lists = []
+    for _ in range(n_rows):
+        if rng.random() < empty_frac:
+            lists.append(np.zeros(0, np.int64))
+            continue
+        m = max(1, int(rng.binomial(n, density)))
+        ids = rng.choice(n, size=m, replace=False)
+        if junk:   # repeats and ids outside the plan: rows are read as sets
+            ids = np.concatenate([ids, ids[:2], [n + 5, -2]])
+        lists.append(ids.astype(np.int64))
+    return lists
+
+
+def _clean(lists, n):
+    return [np.array(sorted({int(x) for x in r if 0 <= x < n}), dtype=np.int64) for r in lists]
+
+
+def _csr(lists):
+    rp, ci = O.to_csr(lists)
+    return rp, ci
+
+
+# ---------------------------------------------------------------- transpose
+@pytest.mark.parametrize("grid,junk", [((8, 16, 16), False), ((8, 40, 44), True), ((5, 7, 9), True)])
+def test_mask_transpose_bit_exact(grid, junk):
+    B, H = 1, 3
+    plan = fva.Plan(B, H, 64, grid, dtype="f32")
+    n = plan.n_blk
+    rng = np.random.default_rng(11)
+    rp, ci = _csr(_rand_lists(rng, plan.n_rows, n, 0.2, junk))
+    t_rp = torch.empty(plan.n_rows + 1, dtype=torch.int32, device="cuda")
+    t_ci = torch.full((max(1, len(ci)),), -7, dtype=torch.int32, device="cuda")
+    fva.fva_mask_transpose(plan, _dev_i32(rp), _dev_i32(ci if len(ci) else np.zeros(1)), t_rp, t_ci)
+    torch.cuda.synchronize()
+    w_rp, w_ci = O.mask_transpose(rp, ci, B, H, n)
+    got_rp = t_rp.cpu().numpy()
+    assert np.array_equal(got_rp, w_rp)
+    assert np.array_equal(t_ci[: got_rp[-1]].cpu().numpy(), w_ci)
+
+
+# ---------------------------------------------------------------- training run
+def _train(w, lists, dout_scale=1.0):
+    """Forward (with lse) and backward on the given lists; returns GPU
+    results in block order and the oracle's fp64 inputs."""
+    plan = fva.Plan(w.B, w.H, w.D, w.grid, tile=w.tile, order=w.order, sub=w.sub, dtype=w.dtype)
+    opl = O.plan(w.grid, tile=w.tile, order=w.order, sub=w.sub)
+    q, k, v, _ = synth.make(w)
+    do = synth.make_dout(w, scale=dout_scale)
+    shp = plan.perm_shape()
+    mk = lambda: torch.empty(shp, dtype=plan.torch_dtype, device="cuda")
+    qd, kd, vd, dod = (to_dev(x, w.dtype) for x in (q, k, v, do))
+    qp, kp, vt, o, qvt, kvt, vp, dop, dovt, dq, dk, dv = (mk() for _ in range(12))
+    for src, dst, lay in ((qd, qp, fva.LAYOUT_ROWS), (kd, kp, fva.LAYOUT_ROWS), (vd, vt, fva.LAYOUT_VT),
+                          (qd, qvt, fva.LAYOUT_VT), (kd, kvt, fva.LAYOUT_VT), (vd, vp, fva.LAYOUT_ROWS),
+                          (dod, dop, fva.LAYOUT_ROWS), (dod, dovt, fva.LAYOUT_VT)):
+        fva.fva_permute(plan, src, dst, lay)
+    rp, ci = _csr(lists)
+    rpd, cid = _dev_i32(rp), _dev_i32(ci if len(ci) else np.zeros(1))
+    lse = torch.empty(shp[:3], dtype=torch.float32, device="cuda")
+    o32 = torch.empty(shp, dtype=torch.float32, device="cuda")
+    fva.fva_attention_lse(plan, qp, kp, vt, rpd, cid, o, o32, lse)
+    for g in (dq, dk, dv):
+        g.fill_(float("nan"))   # every element must be written
+    fva.fva_attention_backward(plan, qp, qvt, kp, kvt, vp, o32, lse, dop, dovt, rpd, cid, dq, dk, dv)
+    torch.cuda.synchronize()
+    f64 = lambda t: t.float().cpu().numpy().astype(np.float64)
+    ref_in = [O.permute(synth.to_f64(x, w.dtype), opl) for x in (q, k, v, do)]
+    res = dict(plan=plan, opl=opl, o=f64(o), o32=f64(o32), lse=lse.cpu().numpy().astype(np.float64),
+               dq=f64(dq), dk=f64(dk), dv=f64(dv), ref_in=ref_in)
+    plan.destroy()
+    return res
+
+
+def _check_grads(got, ref, what):
+    for b in range(ref.shape[0]):
+        for h in range(ref.shape[1]):
+            scale = np.abs(ref[b, h]).max()
+            err = np.abs(got[b, h] - ref[b, h]).max()
+            assert np.isfinite(got[b, h]).all(), f"{what} head {(b, h)} not finite"
+            print(f"{what} head {(b, h)}: max err / max |ref| = {err / max(scale, 1e-300):.2e}")
+            assert err <= GRAD_TOL * scale + 1e-6, f"{what} head {(b, h)}: {err} vs max {scale}"
+
+
+CASES = [
+    ("d128_ragged", synth.scaled(synth.WORKLOADS["wan1.3b_480p"], H=2, grid=(9, 10, 13)), 0.3, False),
+    ("d128_junk", synth.scaled(synth.WORKLOADS["wan1.3b_480p"], B=2, H=1, grid=(8, 12, 16)), 0.2, True),
+    ("d64_ragged", synth.scaled(synth.WORKLOADS["wan1.3b_480p"], H=2, D=64, grid=(5, 12, 11)), 0.4, True),
+    ("d128_hilbert", synth.scaled(synth.WORKLOADS["wan_720p_hilbert_sub"], H=2, grid=(7, 9, 14)), 0.3, False),
+    ("d128_dense", synth.scaled(synth.WORKLOADS["wan1.3b_480p"], H=1, grid=(6, 8, 10)), 1.0, False),
+]
+
+
+@pytest.mark.parametrize("name,w,density,junk", CASES, ids=[c[0] for c in CASES])
+def test_backward_matches_oracle(name, w, density, junk):
+    n = O.plan(w.grid, tile=w.tile, order=w.order, sub=w.sub).n_blk
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    lists = _rand_lists(rng, w.B * w.H * n, n, density, junk, empty_frac=0.0 if density >= 1 else 0.1)
+    if density >= 1:
+        lists = [np.arange(n)] * (w.B * w.H * n)
+    r = _train(w, lists)
+    clean = _clean(lists, n)
+    rp, ci = _csr(clean)
+    qp, kp, vp, dop = r["ref_in"]
+    opl = r["opl"]
+    # forward output and log-sum-exp
+    o_ref = O.attention(qp, kp, vp, rp, ci, opl)
+    assert np.abs(r["o"] - o_ref).max() < 2e-2
+    # the fp32 copy is the output before its rounding: bf16(o32) == o
+    assert np.array_equal(synth.to_f64(synth.f32_to_bf16_bits(r["o32"].astype(np.float32)), "bf16"), r["o"])
+    assert np.abs(r["o32"] - o_ref).max() < 2e-2
+    lse_ref = O.attention_lse(qp, kp, rp, ci, opl)
+    print(f"lse max abs err {np.abs(r['lse'] - lse_ref).max():.2e}")
+    assert np.abs(r["lse"] - lse_ref).max() < LSE_TOL
+    # gradients
+    dq, dk, dv = O.attention_backward(qp, kp, vp, dop, rp, ci, opl)
+    _check_grads(r["dq"], dq, "dq")
+    _check_grads(r["dk"], dk, "dk")
+    _check_grads(r["dv"], dv, "dv")
+    # exact zeros: pad tokens, unlisted key blocks, query blocks with empty rows
+    pad = opl.perm < 0
+    for g in ("dq", "dk", "dv"):
+        assert np.all(r[g][:, :, pad, :] == 0)
+    for bh in range(w.B * w.H):
+        b, h = divmod(bh, w.H)
+        rows = clean[bh * n:(bh + 1) * n]
+        listed = set(int(x) for row in rows for x in row)
+        for J in range(n):
+            if J not in listed:
+                assert np.all(r["dk"][b, h, J * 64:(J + 1) * 64] == 0)
+                assert np.all(r["dv"][b, h, J * 64:(J + 1) * 64] == 0)
+        for I, row in enumerate(rows):
+            if len(row) == 0:
+                assert np.all(r["dq"][b, h, I * 64:(I + 1) * 64] == 0)
+
+
+def test_backward_raster_helpers_match_block_order():
+    """attention_forward_train / attention_backward_call (raster in and out)
+    return the block-order gradients scattered back to raster."""
+    w = synth.scaled(synth.WORKLOADS["wan1.3b_480p"], H=2, grid=(9, 10, 13))
+    plan = fva.Plan(w.B, w.H, w.D, w.grid)
+    q, k, v, meta = synth.make(w)
+    do = synth.make_dout(w)
+    qd, kd, vd, dod = (to_dev(x, w.dtype) for x in (q, k, v, do))
+    bufs, tb = fva.Buffers(plan), fva.TrainBuffers(plan)
+    out = torch.empty_like(qd)
+    fva.attention_forward_train(plan, qd, kd, vd, out, float(meta["p_head"][0]), w.k_min, bufs, tb)
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    fva.attention_backward_call(plan, qd, kd, vd, dod, dq, dk, dv, bufs, tb)
+    torch.cuda.synchronize()
+    opl = O.plan(w.grid)
+    for got, blk in ((dq, tb.dq), (dk, tb.dk), (dv, tb.dv)):
+        ref = O.unpermute(blk.float().cpu().numpy().astype(np.float64), opl)
+        assert np.array_equal(got.float().cpu().numpy().astype(np.float64), ref)
+    # and the gradients are the oracle's on the GPU's lists
+    rp = bufs.row_ptr.cpu().numpy().astype(np.int64)
+    ci = bufs.col_idx[: rp[-1]].cpu().numpy().astype(np.int64)
+    qp, kp, vp, dop = (O.permute(synth.to_f64(x, w.dtype), opl) for x in (q, k, v, do))
+    ref = O.attention_backward(qp, kp, vp, dop, rp, ci, opl)
+    for got, r, nm in zip((tb.dq, tb.dk, tb.dv), ref, ("dq", "dk", "dv")):
+        _check_grads(got.float().cpu().numpy().astype(np.float64), r, nm)
+
+
+def test_backward_rejects_fp32_plans_and_null():
+    plan = fva.Plan(1, 1, 64, (4, 4, 4), dtype="f32")
+    t = torch.zeros(plan.perm_shape(), dtype=torch.float32, device="cuda")
+    lse = torch.zeros(plan.perm_shape()[:3], dtype=torch.float32, device="cuda")
+    rp = torch.zeros(plan.n_rows + 1, dtype=torch.int32, device="cuda")
+    ci = torch.zeros(1, dtype=torch.int32, device="cuda")
+    with pytest.raises(fva.FvaError):
+        fva.fva_attention_backward(plan, t, t, t, t, t, t, lse, t, t, rp, ci, t, t, t)
+    with pytest.raises(fva.FvaError):
+        fva.fva_attention_lse(plan, t, t, t, rp, ci, t, t, lse)
+    rc = fva.lib().fva_attention_backward(plan.handle, *([None] * 15))
+    assert rc == fva.FVA_EINVAL
+
+
+# ---------------------------------------------------------------- full size
+def test_backward_full_size_sampled():
+    """Full Wan 14B 480p shape (B=2, H=40, 21x30x52, D=128) on the GPU's own
+    selection: dQ of sampled query blocks and dK, dV of sampled key blocks of
+    two heads against the oracle on the rows that reach them."""
+    w = synth.WORKLOADS["wan14b_480p_cfg"]
+    plan = fva.Plan(w.B, w.H, w.D, w.grid)
+    q, k, v, meta = synth.make(w)
+    do = synth.make_dout(w)
+    qd, kd, vd, dod = (to_dev(x, w.dtype) for x in (q, k, v, do))
+    bufs, tb = fva.Buffers(plan), fva.TrainBuffers(plan)
+    out = torch.empty_like(qd)
+    p = float(meta["p_head"][0])    # one p for every head of this workload
+    fva.attention_forward_train(plan, qd, kd, vd, out, p, w.k_min, bufs, tb)
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    fva.attention_backward_call(plan, qd, kd, vd, dod, dq, dk, dv, bufs, tb)
+    torch.cuda.synchronize()
+    n = plan.n_blk
+    rp = bufs.row_ptr.cpu().numpy().astype(np.int64)
+    ci = bufs.col_idx[: rp[-1]].cpu().numpy().astype(np.int64)
+    del qd, kd, vd, dod, out, dq, dk, dv
+    opl = O.plan(w.grid)
+    rng = np.random.default_rng(21)
+    for b, h in [(0, 5), (1, 33)]:
+        base = (b * w.H + h) * n
+        rows = [ci[rp[base + I]:rp[base + I + 1]] for I in range(n)]
+        qI = rng.choice(n, size=3, replace=False)
+        J = int(rng.choice(rows[qI[0]]))   # a key block some row lists
+        keep = [r if (I in qI or np.any(r == J)) else np.zeros(0, np.int64) for I, r in enumerate(rows)]
+        hrp, hci = O.to_csr(keep)
+        sl = lambda a: O.permute(synth.to_f64(a[b:b + 1, :, h:h + 1, :], w.dtype), opl)
+        ref_q, ref_k, ref_v = O.attention_backward(sl(q), sl(k), sl(v), sl(do), hrp, hci, opl)
+        got = {nm: t[b, h].float().cpu().numpy().astype(np.float64) for nm, t in
+               (("dq", tb.dq), ("dk", tb.dk), ("dv", tb.dv))}
+        for I in qI:
+            seg = slice(I * 64, (I + 1) * 64)
+            s = np.abs(ref_q[0, 0, seg]).max()
+            print(f"dq {(b, h, I)}: {np.abs(got['dq'][seg] - ref_q[0, 0, seg]).max() / s:.2e}")
+            assert np.abs(got["dq"][seg] - ref_q[0, 0, seg]).max() <= GRAD_TOL * s + 1e-6, (b, h, I)
+        seg = slice(J * 64, (J + 1) * 64)
+        for nm, ref in (("dk", ref_k), ("dv", ref_v)):
+            s = np.abs(ref[0, 0, seg]).max()
+            print(f"{nm} {(b, h, J)}: {np.abs(got[nm][seg] - ref[0, 0, seg]).max() / s:.2e}")
+            assert np.abs(got[nm][seg] - ref[0, 0, seg]).max() <= GRAD_TOL * s + 1e-6, (nm, b, h, J)
+    plan.destroy()
