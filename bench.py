@@ -43,6 +43,7 @@ def parse():
     ap.add_argument("--workload", default="wan14b_480p_cfg")
     ap.add_argument("--sched", default="persistent", choices=["persistent", "plain"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-backward", action="store_true", help="skip the training-step (backward) timing")
     ap.add_argument("--cpu-heads", type=int, default=4, help="(b,h) pairs in the CPU oracle sample")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (counter calibration)")
@@ -208,6 +209,42 @@ def main():
     torch.cuda.synchronize()
     balance = cu_idle(wg.cpu().numpy().view(np.uint64)) if args.sched == "persistent" else None
 
+    # training step on the same inputs and lists: the forward pass that keeps
+    # lse and the fp32 output, then the backward kernels alone and the whole
+    # raster-in / raster-out backward call
+    backward = None
+    if w.dtype == "bf16" and not args.no_backward:
+        dod = dev(synth.make_dout(w))
+        tb = fva.TrainBuffers(plan)
+        dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+        fva.attention_forward_train(plan, qd, kd, vd, out, p, w.k_min, bufs, tb, slack=w.slack)
+        fva.attention_backward_call(plan, qd, kd, vd, dod, dq, dk, dv, bufs, tb)
+        torch.cuda.synchronize()
+        e_b = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e_b[0].record()
+        for _ in range(args.steps):
+            fva.fva_attention_lse(plan, bufs.q, bufs.k, bufs.vt, bufs.row_ptr, bufs.col_idx, bufs.o, tb.o32, tb.lse)
+        e_b[1].record()
+        for _ in range(args.steps):
+            fva.fva_attention_backward(plan, bufs.q, tb.q_vt, bufs.k, tb.k_vt, tb.v, tb.o32, tb.lse, tb.do,
+                                       tb.do_vt, bufs.row_ptr, bufs.col_idx, tb.dq, tb.dk, tb.dv)
+        e_b[2].record()
+        for _ in range(args.steps):
+            fva.attention_backward_call(plan, qd, kd, vd, dod, dq, dk, dv, bufs, tb)
+        e_b[3].record()
+        torch.cuda.synchronize()
+        lse_ms, bwd_ms, bwd_call_ms = (e_b[i].elapsed_time(e_b[i + 1]) / args.steps for i in range(3))
+        nnz_b = int(bufs.row_ptr[-1].item())
+        # standard count: S recomputed, dP, dQ, dK, dV (five 64x64xD products per block pair)
+        bflop = nnz_b * 5 * 2.0 * 64 * 64 * w.D
+        backward = {"attention_lse_ms": round(lse_ms, 4), "backward_kernels_ms": round(bwd_ms, 4),
+                    "backward_call_ms": round(bwd_call_ms, 4),
+                    "backward_tflops": round(bflop / (bwd_ms * 1e-3) / 1e12, 2),
+                    "frac_bf16_peak": round(bflop / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                    "flop_count": "5 products of 64x64xD per listed block pair"}
+        del dod, tb, dq, dk, dv
+        torch.cuda.empty_cache()
+
     nnz = int(bufs.row_ptr[-1].item())
     head_nnz = bufs.head_nnz.cpu().numpy()
     n_blk = plan.n_blk
@@ -264,6 +301,7 @@ def main():
         "permute_rope_ms": round(rope_ms, 4),
         "reuse": {"ms_per_call_cached_selection": round(reuse_ms, 4), "mask_overlap_ms": round(overlap_ms, 4)},
         "permute_rope_gbs": round(perm_bytes / (rope_ms * 1e-3) / 1e9, 1),
+        "training": backward,
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "kernel": "k_attn_bf16 (fva_attention)",

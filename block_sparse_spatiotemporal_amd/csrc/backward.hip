@@ -89,13 +89,13 @@ struct BwdArgs {
   int64_t n_pad;
   int n_blk;
   int nw;
-  int n_items;              // B*H*n_blk
+  int n_items;              // B*H*ceil(n_blk / G) groups
   int chunk;
   float scale;              // 1/sqrt(D)
 };
 
-// Block handled by this workgroup, dealt XCD-aware (neighbouring blocks of
-// one head share an L2), or -1 past the end.  Wave-uniform.
+// Group of G consecutive blocks of one head handled by this workgroup, dealt
+// XCD-aware (neighbouring groups share an L2), or -1 past the end.
 __device__ __forceinline__ int bwd_item(const BwdArgs& a) {
   const int64_t it = xcd_item(blockIdx.x % kXcds, blockIdx.x / kXcds, a.chunk);
   return it < a.n_items ? (int)it : -1;
@@ -105,8 +105,9 @@ __device__ __forceinline__ int bwd_item(const BwdArgs& a) {
 // still in flight.
 template <int PW, int NST>
 __device__ __forceinline__ void wait_steps(int ahead) {
-  static_assert(NST >= 2 && NST <= 3 && (NST - 1) * PW < 64, "vmcnt range");
-  if (NST == 3 && ahead >= 2) wait_vm<(NST == 3 ? 2 * PW : 0)>();
+  static_assert(NST >= 2 && NST <= 4 && (NST - 1) * PW < 64, "vmcnt range");
+  if (NST >= 4 && ahead >= 3) wait_vm<(NST >= 4 ? 3 * PW : 0)>();
+  else if (NST >= 3 && ahead >= 2) wait_vm<(NST >= 3 ? 2 * PW : 0)>();
   else if (ahead >= 1) wait_vm<PW>();
   else wait_vm<0>();
 }
@@ -122,13 +123,13 @@ __device__ __forceinline__ void store4(uint16_t* dst, const f32x16& acc, int g4,
 
 // Source offsets (bytes within one 32-row half) of a wave's direct loads of
 // a row tile (K-like: XOR swizzle kswz by row) and of a VT tile (vswz by d).
-// Load j of wave w fills LDS bytes [1024 (2j + w), +1024) of the half.
-template <int D, int LPW>
+// Load j of wave w (of NW) fills LDS bytes [1024 (NW j + w), +1024) of the half.
+template <int D, int LPW, int NW>
 __device__ __forceinline__ void tile_offsets(int w, int lane, uint32_t* roff, uint32_t* toff) {
   constexpr int KCH = D / 8;
 #pragma unroll
   for (int j = 0; j < LPW; ++j) {
-    const int off = (2 * j + w) * 1024 + lane * 16;
+    const int off = (NW * j + w) * 1024 + lane * 16;
     const int row = off / (KCH * 16), pc = (off / 16) % KCH;
     roff[j] = row * (D * 2) + ((pc ^ kswz<D>(row)) * 16);
     const int d = off / 64, pv = (off / 16) & 3;
@@ -136,38 +137,65 @@ __device__ __forceinline__ void tile_offsets(int w, int lane, uint32_t* roff, ui
   }
 }
 
-// dQ and delta.  Workgroup = 2 waves = one 64-query block; wave w owns
-// queries 32w..32w+31, one per lane pair (lanes l and l+32 split D).  A step
-// is one 32-key half of a listed block:
+// The G bitmaps of a group (rows of `bits` starting at row0; rows past the
+// head's last block are empty): this wave's own one (block g) and their
+// union, one 64-bit word per lane.
+template <int G>
+__device__ __forceinline__ void group_bits(const uint64_t* bits, int64_t row0, int nvalid, int nw, int lane, int g,
+                                           uint32_t* own_lo, uint32_t* own_hi, uint32_t* un_lo, uint32_t* un_hi) {
+  uint64_t own = 0, un = 0;
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    const uint64_t x = (lane < nw && i < nvalid) ? bits[(row0 + i) * nw + lane] : 0;
+    un |= x;
+    if (i == g) own = x;
+  }
+  *own_lo = (uint32_t)own;
+  *own_hi = (uint32_t)(own >> 32);
+  *un_lo = (uint32_t)un;
+  *un_hi = (uint32_t)(un >> 32);
+}
+
+// dQ and delta.  Workgroup = G query blocks, 2 waves each; wave w serves
+// block w/2, queries 32 (w%2)..+31, one per lane pair (lanes l and l+32
+// split D).  Steps walk the union of the G rows of the selection, one
+// 32-key half of a block per step, loaded once into the LDS ring for every
+// wave pair whose row holds it:
 //   S^T  (32 keys x 32 queries) = K_half . Q^T      (Q in registers)
 //   dP^T (32 keys x 32 queries) = V_half . dO^T     (dO in registers)
 //   dS^T = P^T * (dP^T - delta),  P^T = exp2(S^T * scale * log2 e - lse)
 //   dQ^T (D x 32 queries) += K^T_half . dS^T        (dS^T straight from the accumulators)
 // K rows, V rows and K^T (VT layout) of each half stream through an
-// NST-stage LDS ring of direct loads, published by one barrier per step.
-template <int D, int NST>
-__global__ __launch_bounds__(128) void k_bwd_dq(BwdArgs a) {
+// NST-stage ring of direct loads, published by one barrier per step.
+template <int D, int NST, int G>
+__global__ __launch_bounds__(128 * G, 2) void k_bwd_dq(BwdArgs a) {
+  constexpr int NW = 2 * G;
   constexpr int KS = D / 16, DT = D / 32, KCH = D / 8;
   constexpr int HALF = 32 * D * 2;
   constexpr int STAGE = 3 * HALF;
-  constexpr int LPW = HALF / 1024 / 2;  // direct loads per wave per tile
-  constexpr int PW = 3 * LPW;           // per wave per step
+  constexpr int LPW = HALF / 1024 / NW;  // direct loads per wave per tile
+  constexpr int PW = 3 * LPW;            // per wave per step
+  static_assert(LPW >= 1 && (HALF / 1024) % NW == 0, "tile loads split evenly over the waves");
   __shared__ __attribute__((aligned(1024))) uint4 ring[NST * STAGE / 16];
   const int item = bwd_item(a);
   if (item < 0) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qg = w >> 1, w2 = w & 1;
   const int h = lane >> 5, l32 = lane & 31;
-  const int bh = item / a.n_blk, I = item - bh * a.n_blk;
+  const int ngh = (a.n_blk + G - 1) / G;
+  const int bh = item / ngh, I0 = (item - bh * ngh) * G;
+  const bool has_row = I0 + qg < a.n_blk;
+  const int I = has_row ? I0 + qg : I0;
   const int64_t head = (int64_t)bh * a.n_pad;
-  const int64_t tok = head + (int64_t)I * 64 + 32 * w + l32;
+  const int64_t tok = head + (int64_t)I * 64 + 32 * w2 + l32;
   const float sl2 = a.scale * 1.44269504088896340736f;
-  const bool qvalid = sload(a.blk_mask, I) >> (32 * w + l32) & 1;
+  const bool qvalid = has_row && (sload(a.blk_mask, I) >> (32 * w2 + l32) & 1);
 
   uint32_t roff[LPW], toff[LPW];
-  tile_offsets<D, LPW>(w, lane, roff, toff);
-  const uint64_t rw = lane < a.nw ? a.bits[(int64_t)item * a.nw + lane] : 0;
-  const uint32_t row_lo = (uint32_t)rw, row_hi = (uint32_t)(rw >> 32);
+  tile_offsets<D, LPW, NW>(w, lane, roff, toff);
+  uint32_t own_lo, own_hi, un_lo, un_hi;
+  group_bits<G>(a.bits, (int64_t)bh * a.n_blk + I0, a.n_blk - I0, a.nw, lane, qg, &own_lo, &own_hi, &un_lo, &un_hi);
   const uint64_t fw = lane < a.nw ? a.blk_full[lane] : 0;
   const uint32_t full_lo = (uint32_t)fw, full_hi = (uint32_t)(fw >> 32);
 
@@ -192,7 +220,7 @@ __global__ __launch_bounds__(128) void k_bwd_dq(BwdArgs a) {
     lse2 = qvalid ? a.lse[tok] : INFINITY;   // pad queries: P = 0
     // settle these loads before the ring's direct loads are counted
     wait_vm<0>();
-    if (h == 0) a.delta[tok] = delta;
+    if (h == 0 && has_row) a.delta[tok] = delta;
   }
 
   BitWalk iw, cw;
@@ -203,7 +231,7 @@ __global__ __launch_bounds__(128) void k_bwd_dq(BwdArgs a) {
   bool more = true;
   auto issue_next = [&]() __attribute__((always_inline)) {
     if ((issued & 1) == 0) {
-      more = iw.next(row_lo, row_hi, a.nw, &curJ);
+      more = iw.next(un_lo, un_hi, a.nw, &curJ);
       if (!more) return;
     }
     const int u = issued & 1;
@@ -212,7 +240,7 @@ __global__ __launch_bounds__(128) void k_bwd_dq(BwdArgs a) {
     const uint32_t dst = lds_addr(ring) + (issued % NST) * STAGE;
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
-      const uint32_t o1 = (2 * j + w) * 1024;
+      const uint32_t o1 = (NW * j + w) * 1024;
       dma16(kbase + roff0, roff[j], dst + o1);
       dma16(vbase + roff0, roff[j], dst + HALF + o1);
       dma16(tbase + toff0, toff[j], dst + 2 * HALF + o1);
@@ -228,10 +256,11 @@ __global__ __launch_bounds__(128) void k_bwd_dq(BwdArgs a) {
     if (more) issue_next();
 
   int J = 0;
-  bool full = false;
+  bool mine = false, full = false;
   for (int st = 0; st < issued; ++st) {
     if ((st & 1) == 0) {
-      cw.next(row_lo, row_hi, a.nw, &J);
+      cw.next(un_lo, un_hi, a.nw, &J);
+      mine = lane_word(own_lo, own_hi, J >> 6) >> (J & 63) & 1;
       full = lane_word(full_lo, full_hi, J >> 6) >> (J & 63) & 1;
     }
     wait_steps<PW, NST>(issued - 1 - st);
@@ -239,8 +268,9 @@ __global__ __launch_bounds__(128) void k_bwd_dq(BwdArgs a) {
     if (more) issue_next();
 
     const int u = st & 1;
-    const uint32_t mh = full ? 0xFFFFFFFFu : (uint32_t)(sload(a.blk_mask, J) >> (32 * u));
-    if (mh == 0) continue;   // a half of pad keys
+    uint32_t mh = 0;
+    if (mine) mh = full ? 0xFFFFFFFFu : (uint32_t)(sload(a.blk_mask, J) >> (32 * u));
+    if (mh == 0) continue;   // not in this row, or a half of pad keys
     const uint4* kst = ring + (st % NST) * (STAGE / 16);
     const uint4* vst = kst + HALF / 16;
     const uint4* tst = kst + 2 * HALF / 16;
@@ -257,7 +287,7 @@ __global__ __launch_bounds__(128) void k_bwd_dq(BwdArgs a) {
     for (int i = 0; i < 16; ++i) {
       const int key = 8 * (i >> 2) + 4 * h + (i & 3);
       float p = __builtin_amdgcn_exp2f(fmaf(s[i], sl2, -lse2));
-      if (!(mh >> key & 1)) p = 0.0f;
+      if (mh != 0xFFFFFFFFu && !(mh >> key & 1)) p = 0.0f;
       const float ds = p * (dp[i] - delta);
       if (i < 8) d0[i] = ds;
       else d1[i - 8] = ds;
@@ -272,6 +302,7 @@ __global__ __launch_bounds__(128) void k_bwd_dq(BwdArgs a) {
       acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(tst[d * 4 + ((2 + h) ^ sw)]), db1, acc[dt], 0, 0, 0);
     }
   }
+  if (!has_row) return;
   // acc[dt][r]: dQ^T[32 dt + 8 (r/4) + 4 h + r%4][query l32]
   uint16_t* out = a.dq + tok * D;
 #pragma unroll
@@ -280,38 +311,48 @@ __global__ __launch_bounds__(128) void k_bwd_dq(BwdArgs a) {
     for (int g4 = 0; g4 < 4; ++g4) store4(out + 32 * dt + 8 * g4 + 4 * h, acc[dt], g4, a.scale, qvalid);
 }
 
-// dK and dV.  Workgroup = 2 waves = one 64-key block; wave w owns keys
-// 32w..32w+31 (K and V rows in registers).  A step is one 32-query half of
-// a query block that listed this key block:
+// dK and dV.  Workgroup = G key blocks, 2 waves each; wave w owns keys
+// 32 (w%2)..+31 of block w/2 (K and V rows in registers).  Steps walk the
+// union of the G columns (the query blocks whose rows list the key
+// blocks), one 32-query half per step:
 //   S  (32 queries x 32 keys) = Q_half . K^T,   dP = dO_half . V^T
 //   P = exp2(S * scale * log2 e - lse),  dS = P * (dP - delta)
 //   dV^T (D x 32 keys) += dO^T_half . P,   dK^T += Q^T_half . dS
 // The ring stage holds Q rows, dO rows, Q^T and dO^T (VT layout) of the
-// half, and the half's 32 lse and 32 delta values.
-template <int D, int NST>
-__global__ __launch_bounds__(128) void k_bwd_dkdv(BwdArgs a) {
+// half, and the half's 32 lse then 32 delta values (each wave brings
+// 256/NW bytes of those).
+template <int D, int NST, int G>
+__global__ __launch_bounds__(128 * G, G) void k_bwd_dkdv(BwdArgs a) {
+  constexpr int NW = 2 * G;
   constexpr int KS = D / 16, DT = D / 32, KCH = D / 8;
   constexpr int HALF = 32 * D * 2;
   constexpr int STAGE = 4 * HALF + 256;
-  constexpr int LPW = HALF / 1024 / 2;
+  constexpr int LPW = HALF / 1024 / NW;
   constexpr int PW = 4 * LPW + 1;
+  constexpr int LDW = 64 / NW;           // lse/delta floats each wave brings
+  static_assert(LPW >= 1 && (HALF / 1024) % NW == 0, "tile loads split evenly over the waves");
   __shared__ __attribute__((aligned(1024))) uint4 ring[NST * STAGE / 16];
   const int item = bwd_item(a);
   if (item < 0) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = w >> 1, w2 = w & 1;
   const int h = lane >> 5, l32 = lane & 31;
-  const int bh = item / a.n_blk, J = item - bh * a.n_blk;
+  const int ngh = (a.n_blk + G - 1) / G;
+  const int bh = item / ngh, J0 = (item - bh * ngh) * G;
+  const bool has_blk = J0 + kg < a.n_blk;
+  const int J = has_blk ? J0 + kg : J0;
   const int64_t head = (int64_t)bh * a.n_pad;
-  const int64_t tok = head + (int64_t)J * 64 + 32 * w + l32;   // this lane's key token
+  const int64_t tok = head + (int64_t)J * 64 + 32 * w2 + l32;   // this lane's key token
   const float sl2 = a.scale * 1.44269504088896340736f;
-  const uint32_t kmask = (uint32_t)(sload(a.blk_mask, J) >> (32 * w));
+  const uint32_t kmask = has_blk ? (uint32_t)(sload(a.blk_mask, J) >> (32 * w2)) : 0u;
   const bool kvalid = kmask >> l32 & 1;
 
   uint32_t roff[LPW], toff[LPW];
-  tile_offsets<D, LPW>(w, lane, roff, toff);
-  const uint64_t cwd = lane < a.nw ? a.bits_t[(int64_t)item * a.nw + lane] : 0;
-  const uint32_t col_lo = (uint32_t)cwd, col_hi = (uint32_t)(cwd >> 32);
+  tile_offsets<D, LPW, NW>(w, lane, roff, toff);
+  uint32_t own_lo, own_hi, un_lo, un_hi;
+  group_bits<G>(a.bits_t, (int64_t)bh * a.n_blk + J0, a.n_blk - J0, a.nw, lane, kg, &own_lo, &own_hi, &un_lo,
+                &un_hi);
 
   bf16x8 kreg[KS], vreg[KS];
   {
@@ -330,13 +371,13 @@ __global__ __launch_bounds__(128) void k_bwd_dkdv(BwdArgs a) {
   const char* dbase = (const char*)(a.dout + head * D);
   const char* qtbase = (const char*)(a.qt + head * D);
   const char* dtbase = (const char*)(a.dot + head * D);
-  // wave 0 brings the half's lse values, wave 1 its delta values
-  const float* lbase = (w == 0 ? a.lse : (const float*)a.delta) + head;
+  // floats [LDW w, LDW (w+1)) of the stage's [32 lse | 32 delta]
+  const float* lbase = (LDW * w < 32 ? a.lse + LDW * w : (const float*)a.delta + (LDW * w - 32)) + head;
   int issued = 0, curI = 0;
   bool more = true;
   auto issue_next = [&]() __attribute__((always_inline)) {
     if ((issued & 1) == 0) {
-      more = iw.next(col_lo, col_hi, a.nw, &curI);
+      more = iw.next(un_lo, un_hi, a.nw, &curI);
       if (!more) return;
     }
     const int u = issued & 1;
@@ -345,13 +386,13 @@ __global__ __launch_bounds__(128) void k_bwd_dkdv(BwdArgs a) {
     const uint32_t dst = lds_addr(ring) + (issued % NST) * STAGE;
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
-      const uint32_t o1 = (2 * j + w) * 1024;
+      const uint32_t o1 = (NW * j + w) * 1024;
       dma16(qbase + roff0, roff[j], dst + o1);
       dma16(dbase + roff0, roff[j], dst + HALF + o1);
       dma16(qtbase + toff0, toff[j], dst + 2 * HALF + o1);
       dma16(dtbase + toff0, toff[j], dst + 3 * HALF + o1);
     }
-    if (lane < 8) dma16(lbase + (int64_t)curI * 64 + 32 * u, lane * 16, dst + 4 * HALF + 128 * w);
+    if (lane < LDW / 4) dma16(lbase + (int64_t)curI * 64 + 32 * u, lane * 16, dst + 4 * HALF + 4 * LDW * w);
     ++issued;
   };
 
@@ -364,9 +405,11 @@ __global__ __launch_bounds__(128) void k_bwd_dkdv(BwdArgs a) {
 
   int I = 0;
   uint64_t qm64 = 0;
+  bool mine = false;
   for (int st = 0; st < issued; ++st) {
     if ((st & 1) == 0) {
-      cw.next(col_lo, col_hi, a.nw, &I);
+      cw.next(un_lo, un_hi, a.nw, &I);
+      mine = lane_word(own_lo, own_hi, I >> 6) >> (I & 63) & 1;
       qm64 = sload(a.blk_mask, I);
     }
     wait_steps<PW, NST>(issued - 1 - st);
@@ -374,50 +417,68 @@ __global__ __launch_bounds__(128) void k_bwd_dkdv(BwdArgs a) {
     if (more) issue_next();
 
     const int u = st & 1;
-    const uint32_t qm = (uint32_t)(qm64 >> (32 * u));
-    if (qm == 0 || kmask == 0) continue;   // a half of pad queries, or a wave of pad keys
+    const uint32_t qm = mine ? (uint32_t)(qm64 >> (32 * u)) : 0u;
+    if (qm == 0 || kmask == 0) continue;   // not in this column, pad queries, or a wave of pad keys
     const uint4* qst = ring + (st % NST) * (STAGE / 16);
     const uint4* dst_ = qst + HALF / 16;
     const uint4* qtst = qst + 2 * HALF / 16;
     const uint4* dtst = qst + 3 * HALF / 16;
     const float* lds_l = (const float*)(qst + 4 * HALF / 16);
-    f32x16 s = {}, dp = {};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int c = l32 * KCH + ((2 * ks + h) ^ kswz<D>(l32));
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qst[c]), kreg[ks], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(dst_[c]), vreg[ks], dp, 0, 0, 0);
-    }
-    // element r: query 8*(r/4) + 4*h + r%4 of this half, key l32
+    // Two phases keep the live registers low enough for two waves per
+    // SIMD: S -> P -> dV, then dP -> dS -> dK (P kept in fp32 between).
+    // element r of S, dP: query 8*(r/4) + 4*h + r%4 of this half, key l32
     typedef float f32x4 __attribute__((ext_vector_type(4)));
-    f32x8 p0, p1, d0, d1;
+    f32x16 s = {};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qst[l32 * KCH + ((2 * ks + h) ^ kswz<D>(l32))]),
+                                                  kreg[ks], s, 0, 0, 0);
+    f32x16 p;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const f32x4 L = *(const f32x4*)(lds_l + 8 * c + 4 * h);
-      const f32x4 Dl = *(const f32x4*)(lds_l + 32 + 8 * c + 4 * h);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = 4 * c + j, qi = 8 * c + 4 * h + j;
-        float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -L[j]));
-        if (!(qm >> qi & 1) || !kvalid) p = 0.0f;
-        const float ds = p * (dp[r] - Dl[j]);
-        if (r < 8) { p0[r] = p; d0[r] = ds; }
-        else { p1[r - 8] = p; d1[r - 8] = ds; }
+        const float e = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -L[j]));
+        p[r] = (qm >> qi & 1) && kvalid ? e : 0.0f;
       }
     }
-    const bf16x8 pb0 = __builtin_convertvector(p0, bf16x8), pb1 = __builtin_convertvector(p1, bf16x8);
-    const bf16x8 db0 = __builtin_convertvector(d0, bf16x8), db1 = __builtin_convertvector(d1, bf16x8);
+    {
+      const bf16x8 pb0 = __builtin_convertvector(p.lo, bf16x8), pb1 = __builtin_convertvector(p.hi, bf16x8);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int d = 32 * dt + l32;
-      const int sw = vswz(d);
-      const int c0 = d * 4 + ((0 + h) ^ sw), c1 = d * 4 + ((2 + h) ^ sw);
-      dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(dtst[c0]), pb0, dv[dt], 0, 0, 0);
-      dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(dtst[c1]), pb1, dv[dt], 0, 0, 0);
-      dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qtst[c0]), db0, dk[dt], 0, 0, 0);
-      dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qtst[c1]), db1, dk[dt], 0, 0, 0);
+      for (int dt = 0; dt < DT; ++dt) {
+        const int d = 32 * dt + l32;
+        const int sw = vswz(d);
+        dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(dtst[d * 4 + ((0 + h) ^ sw)]), pb0, dv[dt], 0, 0, 0);
+        dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(dtst[d * 4 + ((2 + h) ^ sw)]), pb1, dv[dt], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 dp = {};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(dst_[l32 * KCH + ((2 * ks + h) ^ kswz<D>(l32))]),
+                                                   vreg[ks], dp, 0, 0, 0);
+    f32x16 ds;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const f32x4 Dl = *(const f32x4*)(lds_l + 32 + 8 * c + 4 * h);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ds[4 * c + j] = p[4 * c + j] * (dp[4 * c + j] - Dl[j]);
+    }
+    {
+      const bf16x8 db0 = __builtin_convertvector(ds.lo, bf16x8), db1 = __builtin_convertvector(ds.hi, bf16x8);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int d = 32 * dt + l32;
+        const int sw = vswz(d);
+        dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qtst[d * 4 + ((0 + h) ^ sw)]), db0, dk[dt], 0, 0, 0);
+        dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qtst[d * 4 + ((2 + h) ^ sw)]), db1, dk[dt], 0, 0, 0);
+      }
     }
   }
+  if (!has_blk) return;
   // dk[dt][r], dv[dt][r]: [32 dt + 8 (r/4) + 4 h + r%4][key l32]
   uint16_t* ok = a.dk + tok * D;
   uint16_t* ov = a.dv + tok * D;
@@ -428,6 +489,14 @@ __global__ __launch_bounds__(128) void k_bwd_dkdv(BwdArgs a) {
       store4(ok + 32 * dt + 8 * g4 + 4 * h, dk[dt], g4, a.scale, kvalid);
       store4(ov + 32 * dt + 8 * g4 + 4 * h, dv[dt], g4, 1.0f, kvalid);
     }
+}
+
+// Key blocks per workgroup of the dK/dV kernel (1 or 2); FVA_BWD_KGROUP
+// overrides it.
+int bwd_kgroup() {
+  const char* v = getenv("FVA_BWD_KGROUP");
+  const int n = v ? atoi(v) : 1;
+  return n == 2 ? 2 : 1;
 }
 
 // Blocks per XCD chunk of the backward grids; FVA_BWD_CHUNK overrides it.
@@ -496,17 +565,25 @@ extern "C" int fva_attention_backward(fva_plan_t plan, const void* q_perm, const
   a.n_pad = in.n_pad;
   a.n_blk = (int)in.n_blk;
   a.nw = plan->nw;
-  a.n_items = (int)in.n_rows;
   a.chunk = bwd_chunk();
   a.scale = 1.0f / sqrtf((float)d.head_dim);
   const int deal = kXcds * a.chunk;
-  const dim3 grid((unsigned)((a.n_items + deal - 1) / deal * deal));
+  const int n_bh = d.batch * d.heads;
+  constexpr int GQ = 2;   // query blocks per workgroup of the dQ kernel
+  const int GK = bwd_kgroup();
+  BwdArgs aq = a, ak = a;
+  aq.n_items = n_bh * (int)((in.n_blk + GQ - 1) / GQ);
+  ak.n_items = n_bh * (int)((in.n_blk + GK - 1) / GK);
+  const dim3 gq((unsigned)((aq.n_items + deal - 1) / deal * deal));
+  const dim3 gk((unsigned)((ak.n_items + deal - 1) / deal * deal));
   if (d.head_dim == 128) {
-    hipLaunchKernelGGL((k_bwd_dq<128, 2>), grid, dim3(128), 0, stream, a);
-    hipLaunchKernelGGL((k_bwd_dkdv<128, 2>), grid, dim3(128), 0, stream, a);
+    hipLaunchKernelGGL((k_bwd_dq<128, 3, GQ>), gq, dim3(128 * GQ), 0, stream, aq);
+    if (GK == 2) hipLaunchKernelGGL((k_bwd_dkdv<128, 2, 2>), gk, dim3(256), 0, stream, ak);
+    else hipLaunchKernelGGL((k_bwd_dkdv<128, 2, 1>), gk, dim3(128), 0, stream, ak);
   } else {
-    hipLaunchKernelGGL((k_bwd_dq<64, 2>), grid, dim3(128), 0, stream, a);
-    hipLaunchKernelGGL((k_bwd_dkdv<64, 2>), grid, dim3(128), 0, stream, a);
+    hipLaunchKernelGGL((k_bwd_dq<64, 3, GQ>), gq, dim3(128 * GQ), 0, stream, aq);
+    if (GK == 2) hipLaunchKernelGGL((k_bwd_dkdv<64, 2, 2>), gk, dim3(256), 0, stream, ak);
+    else hipLaunchKernelGGL((k_bwd_dkdv<64, 2, 1>), gk, dim3(128), 0, stream, ak);
   }
   return fva_after_launch(stream, "fva_attention_backward");
 }
