@@ -48,6 +48,12 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t l
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds_addr) : "memory", "m0");
 }
 
+// dma16 for call sites where the compiler cannot prove the (wave-uniform)
+// LDS address scalar, e.g. a ring index modulo 3: readfirstlane states it.
+__device__ __forceinline__ void dma16u(const void* base, uint32_t off, uint32_t lds_addr) {
+  dma16(base, off, __builtin_amdgcn_readfirstlane(lds_addr));
+}
+
 // LDS byte address of a shared-memory object.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;

@@ -241,9 +241,9 @@ __global__ __launch_bounds__(128 * G, 2) void k_bwd_dq(BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
       const uint32_t o1 = (NW * j + w) * 1024;
-      dma16(kbase + roff0, roff[j], dst + o1);
-      dma16(vbase + roff0, roff[j], dst + HALF + o1);
-      dma16(tbase + toff0, toff[j], dst + 2 * HALF + o1);
+      dma16u(kbase + roff0, roff[j], dst + o1);
+      dma16u(vbase + roff0, roff[j], dst + HALF + o1);
+      dma16u(tbase + toff0, toff[j], dst + 2 * HALF + o1);
     }
     ++issued;
   };
@@ -387,12 +387,12 @@ __global__ __launch_bounds__(128 * G, G) void k_bwd_dkdv(BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
       const uint32_t o1 = (NW * j + w) * 1024;
-      dma16(qbase + roff0, roff[j], dst + o1);
-      dma16(dbase + roff0, roff[j], dst + HALF + o1);
-      dma16(qtbase + toff0, toff[j], dst + 2 * HALF + o1);
-      dma16(dtbase + toff0, toff[j], dst + 3 * HALF + o1);
+      dma16u(qbase + roff0, roff[j], dst + o1);
+      dma16u(dbase + roff0, roff[j], dst + HALF + o1);
+      dma16u(qtbase + toff0, toff[j], dst + 2 * HALF + o1);
+      dma16u(dtbase + toff0, toff[j], dst + 3 * HALF + o1);
     }
-    if (lane < LDW / 4) dma16(lbase + (int64_t)curI * 64 + 32 * u, lane * 16, dst + 4 * HALF + 4 * LDW * w);
+    if (lane < LDW / 4) dma16u(lbase + (int64_t)curI * 64 + 32 * u, lane * 16, dst + 4 * HALF + 4 * LDW * w);
     ++issued;
   };
 
@@ -491,12 +491,180 @@ __global__ __launch_bounds__(128 * G, G) void k_bwd_dkdv(BwdArgs a) {
     }
 }
 
-// Key blocks per workgroup of the dK/dV kernel (1 or 2); FVA_BWD_KGROUP
-// overrides it.
+// dV or dK alone (DK selects), for two waves per SIMD: the fused kernel
+// above needs both accumulators and K, V in registers at once.  Workgroup =
+// G key blocks, 2 waves each, wave w owning keys 32 (w%2)..+31 of block
+// w/2; steps walk the union of the G columns, one 32-query half per step.
+//   dV:  S = Q_half . K^T,  P,  dV^T += dO^T_half . P
+//        stage: Q rows, dO^T (VT layout), 32 lse
+//   dK:  S = Q_half . K^T,  dP = dO_half . V^T,  P,  dS = P (dP - delta),
+//        dK^T += Q^T_half . dS
+//        stage: Q rows, dO rows, Q^T (VT layout), 32 lse, 32 delta
+template <int D, int NST, int G, bool DK, int OCC>
+__global__ __launch_bounds__(128 * G, OCC) void k_bwd_dkv(BwdArgs a) {
+  constexpr int NW = 2 * G;
+  constexpr int KS = D / 16, DT = D / 32, KCH = D / 8;
+  constexpr int HALF = 32 * D * 2;
+  constexpr int NT = DK ? 3 : 2;          // 32-row tiles per stage
+  constexpr int LDB = DK ? 256 : 128;     // lse (and delta) bytes per stage
+  constexpr int STAGE = NT * HALF + LDB;
+  constexpr int LPW = HALF / 1024 / NW;
+  constexpr int PW = NT * LPW + 1;
+  constexpr int LDW = LDB / 4 / NW;       // lse / delta floats each wave brings
+  static_assert(LPW >= 1 && (HALF / 1024) % NW == 0 && LDW % 4 == 0, "loads split evenly over the waves");
+  __shared__ __attribute__((aligned(1024))) uint4 ring[NST * STAGE / 16];
+  const int item = bwd_item(a);
+  if (item < 0) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = w >> 1, w2 = w & 1;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int ngh = (a.n_blk + G - 1) / G;
+  const int bh = item / ngh, J0 = (item - bh * ngh) * G;
+  const bool has_blk = J0 + kg < a.n_blk;
+  const int J = has_blk ? J0 + kg : J0;
+  const int64_t head = (int64_t)bh * a.n_pad;
+  const int64_t tok = head + (int64_t)J * 64 + 32 * w2 + l32;   // this lane's key token
+  const float sl2 = a.scale * 1.44269504088896340736f;
+  const uint32_t kmask = has_blk ? (uint32_t)(sload(a.blk_mask, J) >> (32 * w2)) : 0u;
+  const bool kvalid = kmask >> l32 & 1;
+
+  uint32_t roff[LPW], toff[LPW];
+  tile_offsets<D, LPW, NW>(w, lane, roff, toff);
+  uint32_t own_lo, own_hi, un_lo, un_hi;
+  group_bits<G>(a.bits_t, (int64_t)bh * a.n_blk + J0, a.n_blk - J0, a.nw, lane, kg, &own_lo, &own_hi, &un_lo,
+                &un_hi);
+
+  bf16x8 kreg[KS], vreg[DK ? KS : 1];
+  {
+    const uint4* krow = (const uint4*)(a.k + tok * D);
+    const uint4* vrow = (const uint4*)(a.v + tok * D);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kreg[ks] = as_bf16x8(krow[2 * ks + h]);
+      if (DK) vreg[DK ? ks : 0] = as_bf16x8(vrow[2 * ks + h]);
+    }
+    wait_vm<0>();
+  }
+
+  BitWalk iw, cw;
+  const char* qbase = (const char*)(a.q + head * D);
+  const char* dbase = (const char*)(a.dout + head * D);
+  const char* qtbase = (const char*)(a.qt + head * D);
+  const char* dtbase = (const char*)(a.dot + head * D);
+  // floats [LDW w, LDW (w+1)) of the stage's [32 lse | 32 delta]
+  const float* lbase = (LDW * w < 32 ? a.lse + LDW * w : (const float*)a.delta + (LDW * w - 32)) + head;
+  int issued = 0, curI = 0;
+  bool more = true;
+  auto issue_next = [&]() __attribute__((always_inline)) {
+    if ((issued & 1) == 0) {
+      more = iw.next(un_lo, un_hi, a.nw, &curI);
+      if (!more) return;
+    }
+    const int u = issued & 1;
+    const int64_t roff0 = ((int64_t)curI * 64 + 32 * u) * D * 2;
+    const int64_t toff0 = (int64_t)curI * 64 * D * 2 + u * HALF;
+    const uint32_t dst = lds_addr(ring) + (issued % NST) * STAGE;
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+      const uint32_t o1 = (NW * j + w) * 1024;
+      dma16u(qbase + roff0, roff[j], dst + o1);
+      if (DK) {
+        dma16u(dbase + roff0, roff[j], dst + HALF + o1);
+        dma16u(qtbase + toff0, toff[j], dst + 2 * HALF + o1);
+      } else {
+        dma16u(dtbase + toff0, toff[j], dst + HALF + o1);
+      }
+    }
+    if (lane < LDW / 4) dma16u(lbase + (int64_t)curI * 64 + 32 * u, lane * 16, dst + NT * HALF + 4 * LDW * w);
+    ++issued;
+  };
+
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+#pragma unroll
+  for (int st = 0; st < NST - 1; ++st)
+    if (more) issue_next();
+
+  int I = 0;
+  uint64_t qm64 = 0;
+  bool mine = false;
+  for (int st = 0; st < issued; ++st) {
+    if ((st & 1) == 0) {
+      cw.next(un_lo, un_hi, a.nw, &I);
+      mine = lane_word(own_lo, own_hi, I >> 6) >> (I & 63) & 1;
+      qm64 = sload(a.blk_mask, I);
+    }
+    wait_steps<PW, NST>(issued - 1 - st);
+    barrier_no_fence();
+    if (more) issue_next();
+
+    const int u = st & 1;
+    const uint32_t qm = mine ? (uint32_t)(qm64 >> (32 * u)) : 0u;
+    if (qm == 0 || kmask == 0) continue;   // not in this column, pad queries, or a wave of pad keys
+    const uint4* qst = ring + (st % NST) * (STAGE / 16);
+    const uint4* t1 = qst + HALF / 16;       // dO rows (dK) or dO^T (dV)
+    const uint4* t2 = qst + 2 * HALF / 16;   // Q^T (dK)
+    const float* lds_l = (const float*)(qst + NT * HALF / 16);
+    // element r: query 8*(r/4) + 4*h + r%4 of this half, key l32
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    f32x16 s = {}, dp = {};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int c = l32 * KCH + ((2 * ks + h) ^ kswz<D>(l32));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qst[c]), kreg[ks], s, 0, 0, 0);
+      if (DK) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(t1[c]), vreg[DK ? ks : 0], dp, 0, 0, 0);
+    }
+    f32x16 x;   // P (dV) or dS (dK)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const f32x4 L = *(const f32x4*)(lds_l + 8 * c + 4 * h);
+      f32x4 Dl = {};
+      if (DK) Dl = *(const f32x4*)(lds_l + 32 + 8 * c + 4 * h);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 4 * c + j, qi = 8 * c + 4 * h + j;
+        float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -L[j]));
+        if (!(qm >> qi & 1) || !kvalid) p = 0.0f;
+        x[r] = DK ? p * (dp[r] - Dl[j]) : p;
+      }
+    }
+    const bf16x8 xb0 = __builtin_convertvector(x.lo, bf16x8), xb1 = __builtin_convertvector(x.hi, bf16x8);
+    const uint4* at = DK ? t2 : t1;   // Q^T (dK) or dO^T (dV)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int d = 32 * dt + l32;
+      const int sw = vswz(d);
+      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(at[d * 4 + ((0 + h) ^ sw)]), xb0, acc[dt], 0, 0, 0);
+      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(at[d * 4 + ((2 + h) ^ sw)]), xb1, acc[dt], 0, 0, 0);
+    }
+  }
+  if (!has_blk) return;
+  // acc[dt][r]: [32 dt + 8 (r/4) + 4 h + r%4][key l32]
+  uint16_t* out = (DK ? a.dk : a.dv) + tok * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) store4(out + 32 * dt + 8 * g4 + 4 * h, acc[dt], g4, DK ? a.scale : 1.0f, kvalid);
+}
+
+// dK/dV kernels: 0 = dK and dV in separate kernels of two key blocks per
+// workgroup (default); 1 or 2 = the fused kernel with that many key blocks
+// per workgroup.  FVA_BWD_KGROUP overrides it.
 int bwd_kgroup() {
   const char* v = getenv("FVA_BWD_KGROUP");
-  const int n = v ? atoi(v) : 1;
-  return n == 2 ? 2 : 1;
+  const int n = v ? atoi(v) : 0;
+  return n == 1 || n == 2 ? n : 0;
+}
+
+// Tuning switches of the split dK / dV kernels: FVA_BWD_DV_OCC = 2|3
+// (waves per SIMD the dV kernel is compiled for), FVA_BWD_DK_NST = 2|3
+// (ring depth of the dK kernel).
+int env_pick(const char* name, int a, int b, int dflt) {
+  const char* v = getenv(name);
+  const int n = v ? atoi(v) : dflt;
+  return n == a || n == b ? n : dflt;
 }
 
 // Blocks per XCD chunk of the backward grids; FVA_BWD_CHUNK overrides it.
@@ -570,7 +738,10 @@ extern "C" int fva_attention_backward(fva_plan_t plan, const void* q_perm, const
   const int deal = kXcds * a.chunk;
   const int n_bh = d.batch * d.heads;
   constexpr int GQ = 2;   // query blocks per workgroup of the dQ kernel
-  const int GK = bwd_kgroup();
+  const int kmode = bwd_kgroup();
+  const int dv_occ = env_pick("FVA_BWD_DV_OCC", 2, 3, 3);
+  const int dk_nst = env_pick("FVA_BWD_DK_NST", 2, 3, 2);
+  const int GK = kmode == 1 ? 1 : 2;
   BwdArgs aq = a, ak = a;
   aq.n_items = n_bh * (int)((in.n_blk + GQ - 1) / GQ);
   ak.n_items = n_bh * (int)((in.n_blk + GK - 1) / GK);
@@ -578,12 +749,28 @@ extern "C" int fva_attention_backward(fva_plan_t plan, const void* q_perm, const
   const dim3 gk((unsigned)((ak.n_items + deal - 1) / deal * deal));
   if (d.head_dim == 128) {
     hipLaunchKernelGGL((k_bwd_dq<128, 3, GQ>), gq, dim3(128 * GQ), 0, stream, aq);
-    if (GK == 2) hipLaunchKernelGGL((k_bwd_dkdv<128, 2, 2>), gk, dim3(256), 0, stream, ak);
-    else hipLaunchKernelGGL((k_bwd_dkdv<128, 2, 1>), gk, dim3(128), 0, stream, ak);
+    if (kmode == 0) {
+      if (dv_occ == 3) hipLaunchKernelGGL((k_bwd_dkv<128, 3, 2, false, 3>), gk, dim3(256), 0, stream, ak);
+      else hipLaunchKernelGGL((k_bwd_dkv<128, 3, 2, false, 2>), gk, dim3(256), 0, stream, ak);
+      if (dk_nst == 3) hipLaunchKernelGGL((k_bwd_dkv<128, 3, 2, true, 2>), gk, dim3(256), 0, stream, ak);
+      else hipLaunchKernelGGL((k_bwd_dkv<128, 2, 2, true, 2>), gk, dim3(256), 0, stream, ak);
+    } else if (kmode == 2) {
+      hipLaunchKernelGGL((k_bwd_dkdv<128, 2, 2>), gk, dim3(256), 0, stream, ak);
+    } else {
+      hipLaunchKernelGGL((k_bwd_dkdv<128, 2, 1>), gk, dim3(128), 0, stream, ak);
+    }
   } else {
     hipLaunchKernelGGL((k_bwd_dq<64, 3, GQ>), gq, dim3(128 * GQ), 0, stream, aq);
-    if (GK == 2) hipLaunchKernelGGL((k_bwd_dkdv<64, 2, 2>), gk, dim3(256), 0, stream, ak);
-    else hipLaunchKernelGGL((k_bwd_dkdv<64, 2, 1>), gk, dim3(128), 0, stream, ak);
+    if (kmode == 0) {
+      if (dv_occ == 3) hipLaunchKernelGGL((k_bwd_dkv<64, 3, 2, false, 3>), gk, dim3(256), 0, stream, ak);
+      else hipLaunchKernelGGL((k_bwd_dkv<64, 3, 2, false, 2>), gk, dim3(256), 0, stream, ak);
+      if (dk_nst == 3) hipLaunchKernelGGL((k_bwd_dkv<64, 3, 2, true, 2>), gk, dim3(256), 0, stream, ak);
+      else hipLaunchKernelGGL((k_bwd_dkv<64, 2, 2, true, 2>), gk, dim3(256), 0, stream, ak);
+    } else if (kmode == 2) {
+      hipLaunchKernelGGL((k_bwd_dkdv<64, 2, 2>), gk, dim3(256), 0, stream, ak);
+    } else {
+      hipLaunchKernelGGL((k_bwd_dkdv<64, 2, 1>), gk, dim3(128), 0, stream, ak);
+    }
   }
   return fva_after_launch(stream, "fva_attention_backward");
 }
