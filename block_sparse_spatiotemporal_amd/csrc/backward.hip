@@ -5,11 +5,14 @@
 // query, and dO the gradient of the output:
 //   dP = dO V^T,  delta_i = sum_d dO_id O_id,  dS = P * (dP - delta)
 //   dQ = dS K / sqrt(D),  dK = dS^T Q / sqrt(D),  dV = P^T dO
-// Two kernels, each owning its outputs outright (no atomics):
-//   k_bwd_dq    one workgroup per query block, walking the block's row of
-//               the selection (like the forward pass);
-//   k_bwd_dkdv  one workgroup per key block, walking the transposed
-//               selection (the query blocks that listed it).
+// Each kernel owns its outputs outright (no atomics, so the gradients are
+// bitwise reproducible):
+//   k_bwd_dq    groups of query blocks, walking their rows of the selection
+//               (like the forward pass); also writes delta;
+//   k_bwd_dkv   groups of key blocks, walking the transposed selection (the
+//               query blocks that listed them), once for dV and once for dK;
+//   k_bwd_dkdv  dK and dV in one kernel (a selectable variant: holding both
+//               accumulators costs it half the waves per SIMD).
 // P is recomputed from the forward pass's per-query log-sum-exp.
 #include <hip/hip_runtime.h>
 
