@@ -464,13 +464,18 @@ int attn_order() {
   return v && atoi(v) == 0 ? 0 : 1;
 }
 
-// LDS ring depth of the bf16 attention kernel (stages of 2*32*D*2 bytes);
-// FVA_ATTN_STAGES=2|3|4 overrides it for tuning.
-// Rows per XCD chunk of the work list; FVA_ATTN_CHUNK overrides it.
-int attn_chunk() {
+// Groups per XCD chunk of the work list.  Persistent grid: one head's
+// groups, so each XCD works through whole heads and a head's K/V is fetched
+// into one L2, not eight (3.6% faster at the Wan-14B 480P shape and 10% at
+// the Wan-1.3B one than chunks of 32, measured; the per-XCD cursors and
+// stealing absorb heads of unequal cost).  Plain grid: 32, since in-order
+// dispatch would stall every XCD behind the one holding the heaviest head.
+// FVA_ATTN_CHUNK overrides it.
+int attn_chunk(int groups_per_head, bool persistent) {
+  const int dflt = persistent ? groups_per_head : 32;
   const char* v = getenv("FVA_ATTN_CHUNK");
-  int n = v ? atoi(v) : 32;
-  if (n < 1 || n > 4096) n = 32;
+  int n = v ? atoi(v) : dflt;
+  if (n < 1 || n > 65536) n = dflt;
   return n;
 }
 
@@ -483,6 +488,8 @@ int attn_group() {
   return n;
 }
 
+// LDS ring depth of the bf16 attention kernel (stages of 2*32*D*2 bytes);
+// FVA_ATTN_STAGES=2|3|4 overrides it for tuning.
 int attn_stages() {
   const char* v = getenv("FVA_ATTN_STAGES");
   int n = v ? atoi(v) : 4;
@@ -537,7 +544,7 @@ static int attention_launch(fva_plan_t plan, const void* q_perm, const void* k_p
   a.n_items = n_bh * ((in.n_blk + G - 1) / G);
   a.n_blk = in.n_blk;
   a.persistent = sched_mode == FVA_SCHED_PERSISTENT;
-  a.chunk = attn_chunk();
+  a.chunk = attn_chunk((in.n_blk + G - 1) / G, sched_mode == FVA_SCHED_PERSISTENT);
   a.scale = 1.0f / sqrtf((float)d.head_dim);
 
 #define FVA_LAUNCH(KERNEL, THREADS)                                                              \
