@@ -16,8 +16,10 @@
 // P is recomputed from the forward pass's per-query log-sum-exp.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
+#include <cstring>
 
 #include "attn_common.h"
 #include "fva_internal.h"
@@ -94,14 +96,68 @@ struct BwdArgs {
   int nw;
   int n_items;              // B*H*ceil(n_blk / G) groups
   int chunk;
+  int persistent;           // 1: resident grid popping groups from per-XCD cursors
+  int32_t* cursor;          // [16] per-XCD cursors, then per-XCD exhausted flags (zeroed before launch)
+  const int32_t* order;     // persistent: groups in schedule order (list position -> group)
   float scale;              // 1/sqrt(D)
 };
 
-// Group of G consecutive blocks of one head handled by this workgroup, dealt
-// XCD-aware (neighbouring groups share an L2), or -1 past the end.
-__device__ __forceinline__ int bwd_item(const BwdArgs& a) {
-  const int64_t it = xcd_item(blockIdx.x % kXcds, blockIdx.x / kXcds, a.chunk);
-  return it < a.n_items ? (int)it : -1;
+// Next group of G consecutive blocks of one head for this workgroup, or -1
+// when none is left.  Plain grid: workgroup b is on XCD b % 8 and takes its
+// XCD's (b / 8)-th group.  Persistent grid: one cursor per XCD over the
+// XCD's chunks of the group list; an XCD whose share is done steals from the
+// others.  Uniform across the workgroup (an LDS broadcast).
+__device__ __forceinline__ int bwd_next(const BwdArgs& a, int* s_item, bool first) {
+  if (!a.persistent) {
+    if (!first) return -1;
+    const int64_t it = xcd_item(blockIdx.x % kXcds, blockIdx.x / kXcds, a.chunk);
+    return it < a.n_items ? (int)it : -1;
+  }
+  __syncthreads();   // the previous group's ring reads are done
+  if (threadIdx.x == 0) {
+    const int x0 = blockIdx.x % kXcds;
+    int found = -1;
+    for (int t = 0; t < kXcds && found < 0; ++t) {
+      const int x = (x0 + t) % kXcds;
+      if (__hip_atomic_load(&a.cursor[kXcds + x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) continue;
+      const int64_t it = xcd_item(x, atomicAdd(&a.cursor[x], 1), a.chunk);
+      if (it < a.n_items) found = a.order[it];
+      else __hip_atomic_store(&a.cursor[kXcds + x], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    *s_item = found;
+  }
+  __syncthreads();
+  return *s_item;
+}
+
+// Schedule order of one head's groups of G blocks (one workgroup per head):
+// decreasing cost, the number of set bits of the group's bitmap rows (ties
+// by group id), so each XCD runs a head's long groups first and its short
+// ones last.
+__global__ __launch_bounds__(1024) void k_bwd_order(const uint64_t* __restrict__ bits, int n_blk, int nw, int G,
+                                                    int32_t* __restrict__ order) {
+  __shared__ int cost[4096];
+  const int ngh = (n_blk + G - 1) / G;
+  const int bh = blockIdx.x;
+  for (int g = threadIdx.x; g < ngh; g += 1024) {
+    int c = 0;
+    for (int i = 0; i < G && g * G + i < n_blk; ++i) {
+      const uint64_t* row = bits + ((int64_t)bh * n_blk + g * G + i) * nw;
+      for (int wd = 0; wd < nw; ++wd) c += __popcll(row[wd]);
+    }
+    cost[g] = c;
+  }
+  __syncthreads();
+  for (int g = threadIdx.x; g < ngh; g += 1024) {
+    int rk = 0;
+    const int c = cost[g];
+    for (int o = 0; o < ngh; ++o) rk += (cost[o] > c) || (cost[o] == c && o < g);
+    order[(int64_t)bh * ngh + rk] = bh * ngh + g;
+  }
+}
+
+__global__ __launch_bounds__(64) void k_zero_i32(int32_t* __restrict__ p, int n) {
+  for (int i = threadIdx.x; i < n; i += 64) p[i] = 0;
 }
 
 // Wait until at most `ahead` steps of this wave's direct loads (PW each) are
@@ -180,8 +236,8 @@ __global__ __launch_bounds__(128 * G, 2) void k_bwd_dq(BwdArgs a) {
   constexpr int PW = 3 * LPW;            // per wave per step
   static_assert(LPW >= 1 && (HALF / 1024) % NW == 0, "tile loads split evenly over the waves");
   __shared__ __attribute__((aligned(1024))) uint4 ring[NST * STAGE / 16];
-  const int item = bwd_item(a);
-  if (item < 0) return;
+  __shared__ int s_item;
+  for (int item = bwd_next(a, &s_item, true); item >= 0; item = bwd_next(a, &s_item, false)) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qg = w >> 1, w2 = w & 1;
@@ -305,13 +361,14 @@ __global__ __launch_bounds__(128 * G, 2) void k_bwd_dq(BwdArgs a) {
       acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(tst[d * 4 + ((2 + h) ^ sw)]), db1, acc[dt], 0, 0, 0);
     }
   }
-  if (!has_row) return;
+  if (!has_row) continue;
   // acc[dt][r]: dQ^T[32 dt + 8 (r/4) + 4 h + r%4][query l32]
   uint16_t* out = a.dq + tok * D;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) store4(out + 32 * dt + 8 * g4 + 4 * h, acc[dt], g4, a.scale, qvalid);
+  }
 }
 
 // dK and dV.  Workgroup = G key blocks, 2 waves each; wave w owns keys
@@ -335,8 +392,8 @@ __global__ __launch_bounds__(128 * G, G) void k_bwd_dkdv(BwdArgs a) {
   constexpr int LDW = 64 / NW;           // lse/delta floats each wave brings
   static_assert(LPW >= 1 && (HALF / 1024) % NW == 0, "tile loads split evenly over the waves");
   __shared__ __attribute__((aligned(1024))) uint4 ring[NST * STAGE / 16];
-  const int item = bwd_item(a);
-  if (item < 0) return;
+  __shared__ int s_item;
+  for (int item = bwd_next(a, &s_item, true); item >= 0; item = bwd_next(a, &s_item, false)) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kg = w >> 1, w2 = w & 1;
@@ -481,7 +538,7 @@ __global__ __launch_bounds__(128 * G, G) void k_bwd_dkdv(BwdArgs a) {
       }
     }
   }
-  if (!has_blk) return;
+  if (!has_blk) continue;
   // dk[dt][r], dv[dt][r]: [32 dt + 8 (r/4) + 4 h + r%4][key l32]
   uint16_t* ok = a.dk + tok * D;
   uint16_t* ov = a.dv + tok * D;
@@ -492,6 +549,7 @@ __global__ __launch_bounds__(128 * G, G) void k_bwd_dkdv(BwdArgs a) {
       store4(ok + 32 * dt + 8 * g4 + 4 * h, dk[dt], g4, a.scale, kvalid);
       store4(ov + 32 * dt + 8 * g4 + 4 * h, dv[dt], g4, 1.0f, kvalid);
     }
+  }
 }
 
 // dV or dK alone (DK selects), for two waves per SIMD: the fused kernel
@@ -516,8 +574,8 @@ __global__ __launch_bounds__(128 * G, OCC) void k_bwd_dkv(BwdArgs a) {
   constexpr int LDW = LDB / 4 / NW;       // lse / delta floats each wave brings
   static_assert(LPW >= 1 && (HALF / 1024) % NW == 0 && LDW % 4 == 0, "loads split evenly over the waves");
   __shared__ __attribute__((aligned(1024))) uint4 ring[NST * STAGE / 16];
-  const int item = bwd_item(a);
-  if (item < 0) return;
+  __shared__ int s_item;
+  for (int item = bwd_next(a, &s_item, true); item >= 0; item = bwd_next(a, &s_item, false)) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kg = w >> 1, w2 = w & 1;
@@ -643,13 +701,14 @@ __global__ __launch_bounds__(128 * G, OCC) void k_bwd_dkv(BwdArgs a) {
       acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(at[d * 4 + ((2 + h) ^ sw)]), xb1, acc[dt], 0, 0, 0);
     }
   }
-  if (!has_blk) return;
+  if (!has_blk) continue;
   // acc[dt][r]: [32 dt + 8 (r/4) + 4 h + r%4][key l32]
   uint16_t* out = (DK ? a.dk : a.dv) + tok * D;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) store4(out + 32 * dt + 8 * g4 + 4 * h, acc[dt], g4, DK ? a.scale : 1.0f, kvalid);
+  }
 }
 
 // dK/dV kernels: 0 = dK and dV in separate kernels of two key blocks per
@@ -670,12 +729,51 @@ int env_pick(const char* name, int a, int b, int dflt) {
   return n == a || n == b ? n : dflt;
 }
 
-// Blocks per XCD chunk of the backward grids; FVA_BWD_CHUNK overrides it.
-int bwd_chunk() {
+// Schedule of the backward grids.  Persistent (default): a resident grid
+// pops groups from per-XCD cursors, one head's groups per XCD chunk, so a
+// head's Q, dO (or K, V) is fetched into one XCD's L2.  Plain
+// (FVA_BWD_SCHED=plain): one workgroup per group in chunks of 16 groups per
+// XCD (in-order dispatch cannot take head-sized chunks).  FVA_BWD_CHUNK
+// overrides the chunk of either.
+bool bwd_persistent() {
+  const char* v = getenv("FVA_BWD_SCHED");
+  return !(v && strcmp(v, "plain") == 0);
+}
+
+int bwd_chunk(int dflt) {
   const char* v = getenv("FVA_BWD_CHUNK");
-  int n = v ? atoi(v) : 16;
-  if (n < 1 || n > 4096) n = 16;
+  int n = v ? atoi(v) : dflt;
+  if (n < 1 || n > 65536) n = dflt;
   return n;
+}
+
+template <typename K>
+int bwd_occupancy(K kernel, int threads) {
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, threads, 0) != hipSuccess || nb < 1) nb = 1;
+  return nb;
+}
+
+// Launch one backward kernel over the groups of G blocks of every head, with
+// its own cursor set (16 counters, zeroed by the caller).
+template <typename K>
+void bwd_launch(K kernel, int threads, int G, BwdArgs a, fva_plan_t plan, int32_t* cursor, const int32_t* order,
+                hipStream_t stream) {
+  const int n_bh = plan->desc.batch * plan->desc.heads;
+  const int ngh = (int)((plan->info.n_blk + G - 1) / G);
+  a.n_items = n_bh * ngh;
+  a.persistent = bwd_persistent() ? 1 : 0;
+  a.cursor = cursor;
+  a.order = order;
+  a.chunk = bwd_chunk(a.persistent ? ngh : 16);
+  int64_t grid;
+  if (a.persistent) {
+    grid = std::min<int64_t>(a.n_items, (int64_t)plan->num_cu * bwd_occupancy(kernel, threads));
+  } else {
+    const int64_t deal = (int64_t)kXcds * a.chunk;
+    grid = (a.n_items + deal - 1) / deal * deal;
+  }
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(threads), 0, stream, a);
 }
 
 // Row bitmaps of a CSR and their per-head transpose into the plan's workspace.
@@ -736,43 +834,49 @@ extern "C" int fva_attention_backward(fva_plan_t plan, const void* q_perm, const
   a.n_pad = in.n_pad;
   a.n_blk = (int)in.n_blk;
   a.nw = plan->nw;
-  a.chunk = bwd_chunk();
   a.scale = 1.0f / sqrtf((float)d.head_dim);
-  const int deal = kXcds * a.chunk;
-  const int n_bh = d.batch * d.heads;
   constexpr int GQ = 2;   // query blocks per workgroup of the dQ kernel
   const int kmode = bwd_kgroup();
   const int dv_occ = env_pick("FVA_BWD_DV_OCC", 2, 3, 3);
   const int dk_nst = env_pick("FVA_BWD_DK_NST", 2, 3, 2);
+  // cursor sets: dQ, dV (or fused dK/dV), dK
+  int32_t* cq = plan->counters + 16;
+  int32_t* cv = plan->counters + 32;
+  int32_t* ck = plan->counters + 48;
+  hipLaunchKernelGGL(k_zero_i32, dim3(1), dim3(64), 0, stream, cq, 48);
+  // longest-first order inside each head: query-block groups by row lengths
+  // (dQ), key-block groups by column lengths (dK, dV)
+  const int n_bh = d.batch * d.heads;
   const int GK = kmode == 1 ? 1 : 2;
-  BwdArgs aq = a, ak = a;
-  aq.n_items = n_bh * (int)((in.n_blk + GQ - 1) / GQ);
-  ak.n_items = n_bh * (int)((in.n_blk + GK - 1) / GK);
-  const dim3 gq((unsigned)((aq.n_items + deal - 1) / deal * deal));
-  const dim3 gk((unsigned)((ak.n_items + deal - 1) / deal * deal));
+  int32_t* oq = plan->worklist;
+  int32_t* ok = plan->worklist_t;
+  if (bwd_persistent()) {
+    hipLaunchKernelGGL(k_bwd_order, dim3(n_bh), dim3(1024), 0, stream, plan->rowmask, (int)in.n_blk, plan->nw, GQ, oq);
+    hipLaunchKernelGGL(k_bwd_order, dim3(n_bh), dim3(1024), 0, stream, plan->bits_t, (int)in.n_blk, plan->nw, GK, ok);
+  }
   if (d.head_dim == 128) {
-    hipLaunchKernelGGL((k_bwd_dq<128, 3, GQ>), gq, dim3(128 * GQ), 0, stream, aq);
+    bwd_launch(k_bwd_dq<128, 3, GQ>, 128 * GQ, GQ, a, plan, cq, oq, stream);
     if (kmode == 0) {
-      if (dv_occ == 3) hipLaunchKernelGGL((k_bwd_dkv<128, 3, 2, false, 3>), gk, dim3(256), 0, stream, ak);
-      else hipLaunchKernelGGL((k_bwd_dkv<128, 3, 2, false, 2>), gk, dim3(256), 0, stream, ak);
-      if (dk_nst == 3) hipLaunchKernelGGL((k_bwd_dkv<128, 3, 2, true, 2>), gk, dim3(256), 0, stream, ak);
-      else hipLaunchKernelGGL((k_bwd_dkv<128, 2, 2, true, 2>), gk, dim3(256), 0, stream, ak);
+      if (dv_occ == 3) bwd_launch(k_bwd_dkv<128, 3, 2, false, 3>, 256, 2, a, plan, cv, ok, stream);
+      else bwd_launch(k_bwd_dkv<128, 3, 2, false, 2>, 256, 2, a, plan, cv, ok, stream);
+      if (dk_nst == 3) bwd_launch(k_bwd_dkv<128, 3, 2, true, 2>, 256, 2, a, plan, ck, ok, stream);
+      else bwd_launch(k_bwd_dkv<128, 2, 2, true, 2>, 256, 2, a, plan, ck, ok, stream);
     } else if (kmode == 2) {
-      hipLaunchKernelGGL((k_bwd_dkdv<128, 2, 2>), gk, dim3(256), 0, stream, ak);
+      bwd_launch(k_bwd_dkdv<128, 2, 2>, 256, 2, a, plan, cv, ok, stream);
     } else {
-      hipLaunchKernelGGL((k_bwd_dkdv<128, 2, 1>), gk, dim3(128), 0, stream, ak);
+      bwd_launch(k_bwd_dkdv<128, 2, 1>, 128, 1, a, plan, cv, ok, stream);
     }
   } else {
-    hipLaunchKernelGGL((k_bwd_dq<64, 3, GQ>), gq, dim3(128 * GQ), 0, stream, aq);
+    bwd_launch(k_bwd_dq<64, 3, GQ>, 128 * GQ, GQ, a, plan, cq, oq, stream);
     if (kmode == 0) {
-      if (dv_occ == 3) hipLaunchKernelGGL((k_bwd_dkv<64, 3, 2, false, 3>), gk, dim3(256), 0, stream, ak);
-      else hipLaunchKernelGGL((k_bwd_dkv<64, 3, 2, false, 2>), gk, dim3(256), 0, stream, ak);
-      if (dk_nst == 3) hipLaunchKernelGGL((k_bwd_dkv<64, 3, 2, true, 2>), gk, dim3(256), 0, stream, ak);
-      else hipLaunchKernelGGL((k_bwd_dkv<64, 2, 2, true, 2>), gk, dim3(256), 0, stream, ak);
+      if (dv_occ == 3) bwd_launch(k_bwd_dkv<64, 3, 2, false, 3>, 256, 2, a, plan, cv, ok, stream);
+      else bwd_launch(k_bwd_dkv<64, 3, 2, false, 2>, 256, 2, a, plan, cv, ok, stream);
+      if (dk_nst == 3) bwd_launch(k_bwd_dkv<64, 3, 2, true, 2>, 256, 2, a, plan, ck, ok, stream);
+      else bwd_launch(k_bwd_dkv<64, 2, 2, true, 2>, 256, 2, a, plan, ck, ok, stream);
     } else if (kmode == 2) {
-      hipLaunchKernelGGL((k_bwd_dkdv<64, 2, 2>), gk, dim3(256), 0, stream, ak);
+      bwd_launch(k_bwd_dkdv<64, 2, 2>, 256, 2, a, plan, cv, ok, stream);
     } else {
-      hipLaunchKernelGGL((k_bwd_dkdv<64, 2, 1>), gk, dim3(128), 0, stream, ak);
+      bwd_launch(k_bwd_dkdv<64, 2, 1>, 128, 1, a, plan, cv, ok, stream);
     }
   }
   return fva_after_launch(stream, "fva_attention_backward");

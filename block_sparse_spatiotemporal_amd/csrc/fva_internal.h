@@ -48,6 +48,7 @@ struct fva_plan_s {
   float* bwd_delta;   // [B*H*n_pad] backward: rowsum(dO * O) per query token
   uint64_t* bits_t;   // [n_rows][nw] backward: transposed per-head block bitmap (key block -> query blocks)
   int32_t* worklist;  // [n_rows] attention rows in schedule order
+  int32_t* worklist_t;// [n_rows] backward: key-block groups in schedule order
   int32_t* counters;  // [64] work-queue cursor and misc counters
 
   void* dev_base;     // single device allocation holding everything above

@@ -250,3 +250,28 @@ def test_backward_full_size_sampled():
             print(f"{nm} {(b, h, J)}: {np.abs(got[nm][seg] - ref[0, 0, seg]).max() / s:.2e}")
             assert np.abs(got[nm][seg] - ref[0, 0, seg]).max() <= GRAD_TOL * s + 1e-6, (nm, b, h, J)
     plan.destroy()
+
+
+def test_backward_schedules_and_variants_bitwise_equal(monkeypatch):
+    """Persistent or plain grids, XCD chunk, split or fused dK/dV kernels and
+    their tuning switches change only which workgroup computes a block, never
+    its arithmetic: the gradients are bitwise equal."""
+    w = synth.scaled(synth.WORKLOADS["wan1.3b_480p"], H=3, grid=(9, 10, 13))
+    n = O.plan(w.grid).n_blk
+    rng = np.random.default_rng(3)
+    lists = _rand_lists(rng, w.B * w.H * n, n, 0.3)
+    ref = None
+    for env in [{}, {"FVA_BWD_SCHED": "plain"}, {"FVA_BWD_CHUNK": "3"}, {"FVA_BWD_SCHED": "plain", "FVA_BWD_CHUNK": "5"},
+                {"FVA_BWD_KGROUP": "1"}, {"FVA_BWD_KGROUP": "2", "FVA_BWD_SCHED": "plain"},
+                {"FVA_BWD_DV_OCC": "2", "FVA_BWD_DK_NST": "3"}]:
+        for k in ("FVA_BWD_SCHED", "FVA_BWD_CHUNK", "FVA_BWD_KGROUP", "FVA_BWD_DV_OCC", "FVA_BWD_DK_NST"):
+            monkeypatch.delenv(k, raising=False)
+        for k, v in env.items():
+            monkeypatch.setenv(k, v)
+        r = _train(w, lists)
+        got = (r["dq"], r["dk"], r["dv"])
+        if ref is None:
+            ref = got
+        else:
+            for a, b, nm in zip(ref, got, ("dq", "dk", "dv")):
+                assert np.array_equal(a, b), (nm, env)
