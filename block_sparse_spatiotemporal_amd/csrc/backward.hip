@@ -730,7 +730,8 @@ int env_pick(const char* name, int a, int b, int dflt) {
 }
 
 // Schedule of the backward grids.  Persistent (default): a resident grid
-// pops groups from per-XCD cursors, one head's groups per XCD chunk, so a
+// pops groups from per-XCD cursors, one head's groups per XCD chunk (or an
+// equal part of a head when the head count is not a multiple of 8), so a
 // head's Q, dO (or K, V) is fetched into one XCD's L2.  Plain
 // (FVA_BWD_SCHED=plain): one workgroup per group in chunks of 16 groups per
 // XCD (in-order dispatch cannot take head-sized chunks).  FVA_BWD_CHUNK
@@ -765,7 +766,12 @@ void bwd_launch(K kernel, int threads, int G, BwdArgs a, fva_plan_t plan, int32_
   a.persistent = bwd_persistent() ? 1 : 0;
   a.cursor = cursor;
   a.order = order;
-  a.chunk = bwd_chunk(a.persistent ? ngh : 16);
+  // whole heads per XCD chunk, cut into 8 / gcd(heads, 8) parts so every
+  // XCD gets the same number of chunks
+  int gc = n_bh, bb = kXcds;
+  while (bb) { const int t = gc % bb; gc = bb; bb = t; }
+  const int parts = kXcds / gc;
+  a.chunk = bwd_chunk(a.persistent ? (ngh + parts - 1) / parts : 16);
   int64_t grid;
   if (a.persistent) {
     grid = std::min<int64_t>(a.n_items, (int64_t)plan->num_cu * bwd_occupancy(kernel, threads));
