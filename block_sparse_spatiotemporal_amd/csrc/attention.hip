@@ -91,7 +91,13 @@ __device__ __forceinline__ int next_item(const AttnArgs& a, int* s_item, bool fi
 // G query blocks per workgroup (2G waves; wave w serves block w/2, queries
 // 32*(w%2)..+31).  Steps walk the union of the G block lists half by half;
 // a stage is loaded once and used by every wave pair whose list holds it.
-template <int D, int NST, int G>
+// LSE: the training-forward form.  It sums the row in fp32 over the
+// unrounded weights (the per-query log-sum-exp it writes is what the
+// backward pass rebuilds P from, so it must be the softmax normaliser to
+// fp32 accuracy), and writes lse and the fp32 output.  The inference form
+// sums the bf16 weights PV uses, with dot instructions: half the adds, and
+// O normalised by exactly the weights applied to V.
+template <int D, int NST, int G, bool LSE>
 __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
   constexpr int NW = 2 * G;             // waves per workgroup
   constexpr int KS = D / 16;            // k-steps of S^T
@@ -212,8 +218,16 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
 
     int J = 0;
     bool mine = false, full = false;
-    for (int st = 0; st < issued; ++st) {
-      if ((st & 1) == 0) {
+    // Unrolled by the ring depth so each copy of the step reads a fixed
+    // stage: the stage offset then folds into the LDS reads' immediate
+    // offsets instead of costing address arithmetic every step.
+    for (int st0 = 0; st0 < issued; st0 += NST) {
+#pragma unroll
+    for (int kk = 0; kk < NST; ++kk) {
+      const int st = st0 + kk;
+      if (st >= issued) break;
+      const int u = NST % 2 == 0 ? (kk & 1) : (st & 1);   // half of the block
+      if (u == 0) {
         cw.next(un_lo, un_hi, nw, &J);
         mine = lane_word(own_lo, own_hi, J >> 6) >> (J & 63) & 1;
         full = lane_word(full_lo, full_hi, J >> 6) >> (J & 63) & 1;
@@ -227,11 +241,10 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
       barrier_no_fence();
       if (more) issue_next();   // into the stage retired by the barrier
 
-      const int u = st & 1;
       uint32_t mh = 0;
       if (mine) mh = full ? 0xFFFFFFFFu : (uint32_t)(sload(a.blk_mask, J) >> (32 * u));
       if (mh == 0) continue;   // not in this row's list, or a half of pad keys (uniform per wave)
-      const uint4* kst = ring + (st % NST) * (STAGE / 16);
+      const uint4* kst = ring + kk * (STAGE / 16);
       const uint4* vst = kst + HALF / 16;
 
       f32x16 s = {};
@@ -268,10 +281,21 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
         p0[i] = __builtin_amdgcn_exp2f(fmaf(s[i], sl2, nm));
         p1[i] = __builtin_amdgcn_exp2f(fmaf(s[8 + i], sl2, nm));
       }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) l_run += p0[i] + p1[i];
       const bf16x8 pb0 = __builtin_convertvector(p0, bf16x8);
       const bf16x8 pb1 = __builtin_convertvector(p1, bf16x8);
+      if constexpr (LSE) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) l_run += p0[i] + p1[i];
+      } else {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bf16x2 a0 = {pb0[2 * i], pb0[2 * i + 1]}, a1 = {pb1[2 * i], pb1[2 * i + 1]};
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(a0, one2, l_run, false);
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(a1, one2, l_run, false);
+        }
+      }
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const int d = 32 * dt + l32;
@@ -280,12 +304,13 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vst[d * 4 + ((2 + h) ^ sw)]), pb1, o[dt], 0, 0, 0);
       }
     }
+    }
     if (has_row) {
       const float l_tot = xhalf_sum(l_run);
       const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
       const bool qvalid = sload(a.blk_mask, I) >> (32 * w2 + l32) & 1;
       uint16_t* orow = (uint16_t*)a.o + (head + (int64_t)I * 64 + 32 * w2 + l32) * D;
-      if (a.lse && h == 0)   // P_ij = exp2(s_ij * scale * log2(e) - lse_i) for the backward pass
+      if (LSE && h == 0)   // P_ij = exp2(s_ij * scale * log2(e) - lse_i) for the backward pass
         a.lse[head + (int64_t)I * 64 + 32 * w2 + l32] = qvalid && l_tot > 0.0f ? m_run + __log2f(l_tot) : 0.0f;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
@@ -297,7 +322,7 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
           if (!qvalid) v = f32x4{0.f, 0.f, 0.f, 0.f};
           const bf16x4 b = __builtin_convertvector(v, bf16x4);
           *(uint2*)(orow + 32 * dt + 8 * g4 + 4 * h) = __builtin_bit_cast(uint2, b);
-          if (a.o32)
+          if (LSE)
             *(f32x4*)(a.o32 + (head + (int64_t)I * 64 + 32 * w2 + l32) * D + 32 * dt + 8 * g4 + 4 * h) = v;
         }
       }
@@ -522,7 +547,7 @@ static int attention_launch(fva_plan_t plan, const void* q_perm, const void* k_p
   const fva_plan_desc& d = plan->desc;
   const fva_plan_info& in = plan->info;
   const int n_bh = d.batch * d.heads;
-  int G = d.dtype == FVA_DTYPE_BF16 ? attn_group() : 1;
+  int G = d.dtype == FVA_DTYPE_BF16 ? (lse ? 2 : attn_group()) : 1;   // the training form is G = 2 only
   if (d.head_dim == 64 && G > 2) G = 2;   // a 4 KB half splits over at most 4 waves
   hipLaunchKernelGGL(k_sched, dim3(1), dim3(1024), 0, stream, row_ptr, in.n_blk, n_bh, G, plan->worklist,
                      plan->counters);
@@ -564,13 +589,16 @@ static int attention_launch(fva_plan_t plan, const void* q_perm, const void* k_p
   if (d.dtype == FVA_DTYPE_BF16) {
     const int ns = attn_stages();
 #define FVA_BF16_128(NS)                                                      \
-    if (G == 1) FVA_LAUNCH((k_attn_bf16<128, NS, 1>), 128);                   \
-    else if (G == 2) FVA_LAUNCH((k_attn_bf16<128, NS, 2>), 256);              \
-    else FVA_LAUNCH((k_attn_bf16<128, NS, 4>), 512);
+    if (G == 1) FVA_LAUNCH((k_attn_bf16<128, NS, 1, false>), 128);            \
+    else if (G == 2) FVA_LAUNCH((k_attn_bf16<128, NS, 2, false>), 256);       \
+    else FVA_LAUNCH((k_attn_bf16<128, NS, 4, false>), 512);
 #define FVA_BF16_64(NS)                                                       \
-    if (G == 1) FVA_LAUNCH((k_attn_bf16<64, NS, 1>), 128);                    \
-    else FVA_LAUNCH((k_attn_bf16<64, NS, 2>), 256);
-    if (d.head_dim == 128) {
+    if (G == 1) FVA_LAUNCH((k_attn_bf16<64, NS, 1, false>), 128);             \
+    else FVA_LAUNCH((k_attn_bf16<64, NS, 2, false>), 256);
+    if (lse) {   // training forward: the default shape only
+      if (d.head_dim == 128) FVA_LAUNCH((k_attn_bf16<128, 4, 2, true>), 256);
+      else FVA_LAUNCH((k_attn_bf16<64, 4, 2, true>), 256);
+    } else if (d.head_dim == 128) {
       if (ns == 2) { FVA_BF16_128(2) }
       else if (ns == 3) { FVA_BF16_128(3) }
       else { FVA_BF16_128(4) }
