@@ -30,6 +30,7 @@ struct AttnArgs {
   const uint64_t* blk_full; // [64] bitmap of blocks with every position valid
   void* o;
   const int32_t* worklist;
+  const int2* pairs;        // optional (G = 2): the two query blocks of each group
   int32_t* cursor;
   uint64_t* wg_times;
   float* lse;               // optional [B*H, n_pad]: log2 sum exp2 of the scaled scores
@@ -142,6 +143,15 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
     const int gid = sload(a.worklist, __builtin_amdgcn_readfirstlane(item));
     const int bh = gid / ngh;
     const int I0 = (gid - bh * ngh) * G;
+    // this wave pair's query block, or -1: consecutive ids, or the pair
+    // table (G = 2, groups paired by list overlap)
+    int Iq = I0 + qg < a.n_blk ? I0 + qg : -1, Ifirst = I0;
+    if (G == 2 && a.pairs) {
+      const uint64_t pr = sload((const uint64_t*)a.pairs, gid);   // (x, y) of an int2
+      const int px = (int)(uint32_t)pr, py = (int)(uint32_t)(pr >> 32);
+      Iq = qg == 0 ? px : py;
+      Ifirst = px;
+    }
     const int64_t head = (int64_t)bh * a.n_pad;
     // The G rows' block sets as bitmaps: LDS words filled from the CSR
     // lists (ids outside the plan are dropped), then one 64-bit word per
@@ -149,8 +159,8 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
     s_bits[tid] = 0;
     __syncthreads();
     {
-      const int64_t rr = (int64_t)bh * a.n_blk + I0 + qg;
-      if (I0 + qg < a.n_blk) {
+      const int64_t rr = (int64_t)bh * a.n_blk + Iq;
+      if (Iq >= 0) {
         const int beg = sload(a.row_ptr, rr), end = sload(a.row_ptr, rr + 1);
         for (int j = beg + (tid & 127); j < end; j += 128) {
           const int J = a.col_idx[j];
@@ -195,8 +205,8 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
       return true;
     };
 
-    const bool has_row = I0 + qg < a.n_blk;
-    const int I = has_row ? I0 + qg : I0;
+    const bool has_row = Iq >= 0;
+    const int I = has_row ? Iq : Ifirst;
     bf16x8 qreg[KS];
     {
       const uint4* qrow = (const uint4*)(a.q + (head + (int64_t)I * 64 + 32 * w2 + l32) * D);
@@ -456,7 +466,7 @@ __global__ __launch_bounds__(1024) void k_sched(const int32_t* __restrict__ row_
 // id), so the persistent grid's last items are the short ones.  One
 // workgroup per segment.
 __global__ __launch_bounds__(1024) void k_sched_lpt(const int32_t* __restrict__ row_ptr, int n_blk, int G,
-                                                    int32_t* __restrict__ worklist) {
+                                                    const int2* __restrict__ pairs, int32_t* __restrict__ worklist) {
   __shared__ int item[4096];
   __shared__ int cost[4096];
   const int ngh = (n_blk + G - 1) / G;
@@ -464,10 +474,19 @@ __global__ __launch_bounds__(1024) void k_sched_lpt(const int32_t* __restrict__ 
   for (int k = threadIdx.x; k < ngh; k += 1024) {
     const int r = seg[k];
     const int bh = r / ngh, g = r - bh * ngh;
-    const int64_t r0 = (int64_t)bh * n_blk + (int64_t)g * G;
-    const int r1 = min((g + 1) * G, n_blk) - g * G;
+    const int64_t hb = (int64_t)bh * n_blk;
+    int c;
+    if (pairs) {
+      const int2 pr = pairs[r];
+      c = row_ptr[hb + pr.x + 1] - row_ptr[hb + pr.x];
+      if (pr.y >= 0) c += row_ptr[hb + pr.y + 1] - row_ptr[hb + pr.y];
+    } else {
+      const int64_t r0 = hb + (int64_t)g * G;
+      const int r1 = min((g + 1) * G, n_blk) - g * G;
+      c = row_ptr[r0 + r1] - row_ptr[r0];
+    }
     item[k] = r;
-    cost[k] = row_ptr[r0 + r1] - row_ptr[r0];
+    cost[k] = c;
   }
   __syncthreads();
   int pos[4];
@@ -479,6 +498,91 @@ __global__ __launch_bounds__(1024) void k_sched_lpt(const int32_t* __restrict__ 
   }
   __syncthreads();
   for (int k = threadIdx.x, i = 0; k < ngh; k += 1024, ++i) seg[pos[i]] = item[k];
+}
+
+// Query-block pairs for groups of two (one workgroup per head).  Candidate
+// pairs join spatial neighbours: in tile order the next block along w, h
+// and t; in Hilbert order the next three blocks along the curve.  They are
+// taken greedily in decreasing overlap of the two rows' block sets (the
+// keys a group's shared stages serve twice), then the blocks left over are
+// paired in id order.  Every head gets exactly ceil(n_blk / 2) groups.
+__global__ __launch_bounds__(1024) void k_pair(const uint64_t* __restrict__ bits, int n_blk, int nw, int nbw,
+                                               int nbh, int hilbert, int2* __restrict__ pairs) {
+  __shared__ uint32_t key[16384];   // (overlap + 1) << 18 | edge, 0 for no edge
+  __shared__ uint8_t used[4096];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const uint64_t* hb = bits + (int64_t)bh * n_blk * nw;
+  const int ne = 3 * n_blk;
+  int np2 = 1;
+  while (np2 < ne) np2 <<= 1;
+  auto partner = [&](int I, int c) -> int {
+    if (hilbert) return I + c + 1 < n_blk ? I + c + 1 : -1;
+    const int bw = I % nbw, bhh = (I / nbw) % nbh;
+    if (c == 0) return bw + 1 < nbw ? I + 1 : -1;
+    if (c == 1) return bhh + 1 < nbh ? I + nbw : -1;
+    return I + nbw * nbh < n_blk ? I + nbw * nbh : -1;
+  };
+  for (int e = tid; e < np2; e += 1024) {
+    uint32_t k = 0;
+    if (e < ne) {
+      const int I = e / 3, J = partner(I, e % 3);
+      if (J >= 0) {
+        int ov = 0;
+        for (int w = 0; w < nw; ++w) ov += __popcll(hb[(int64_t)I * nw + w] & hb[(int64_t)J * nw + w]);
+        k = ((uint32_t)(ov + 1) << 18) | (uint32_t)e;
+      }
+    }
+    key[e] = k;
+  }
+  for (int i = tid; i < n_blk; i += 1024) used[i] = 0;
+  // bitonic sort, descending
+  for (int size = 2; size <= np2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      __syncthreads();
+      for (int i = tid; i < np2; i += 1024) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const bool desc = (i & size) == 0;
+          const uint32_t x = key[i], y = key[j];
+          if (desc ? x < y : x > y) { key[i] = y; key[j] = x; }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int2* out = pairs + (int64_t)bh * ((n_blk + 1) / 2);
+    int g = 0;
+    for (int i = 0; i < ne && key[i] != 0; ++i) {
+      const int e = (int)(key[i] & 0x3FFFFu), I = e / 3, J = partner(I, e % 3);
+      if (!used[I] && !used[J]) {
+        used[I] = used[J] = 1;
+        out[g++] = make_int2(I, J);
+      }
+    }
+    int pend = -1;
+    for (int I = 0; I < n_blk; ++I) {
+      if (used[I]) continue;
+      if (pend < 0) {
+        pend = I;
+      } else {
+        out[g++] = make_int2(pend, I);
+        pend = -1;
+      }
+    }
+    if (pend >= 0) out[g++] = make_int2(pend, -1);
+  }
+}
+
+// Groups of two: pair query blocks by list overlap (1) or take consecutive
+// ids (0).  Default: pairing for Hilbert-order plans only (1.6% faster at
+// 720P, where curve neighbours 2g, 2g+1 overlap less; 3% slower in tile
+// order, whose consecutive ids are w-neighbours), measured.
+// FVA_ATTN_PAIR overrides it.
+int attn_pair(bool hilbert) {
+  const char* v = getenv("FVA_ATTN_PAIR");
+  if (v) return atoi(v) == 1 ? 1 : 0;
+  return hilbert ? 1 : 0;
 }
 
 // Work-list order inside a head: 1 = decreasing cost (default; 2% faster
@@ -549,10 +653,18 @@ static int attention_launch(fva_plan_t plan, const void* q_perm, const void* k_p
   const int n_bh = d.batch * d.heads;
   int G = d.dtype == FVA_DTYPE_BF16 ? (lse ? 2 : attn_group()) : 1;   // the training form is G = 2 only
   if (d.head_dim == 64 && G > 2) G = 2;   // a 4 KB half splits over at most 4 waves
+  const bool paired = G == 2 && attn_pair(d.order == FVA_ORDER_HILBERT) == 1;
+  if (paired) {
+    const int nbw = in.padded[2] / d.tile[2], nbh = in.padded[1] / d.tile[1];
+    fva_csr_bits(plan, row_ptr, col_idx, plan->rowmask, stream);
+    hipLaunchKernelGGL(k_pair, dim3(n_bh), dim3(1024), 0, stream, plan->rowmask, (int)in.n_blk, plan->nw, nbw, nbh,
+                       d.order == FVA_ORDER_HILBERT ? 1 : 0, plan->pairs);
+  }
   hipLaunchKernelGGL(k_sched, dim3(1), dim3(1024), 0, stream, row_ptr, in.n_blk, n_bh, G, plan->worklist,
                      plan->counters);
   if (attn_order() == 1)
-    hipLaunchKernelGGL(k_sched_lpt, dim3(n_bh), dim3(1024), 0, stream, row_ptr, (int)in.n_blk, G, plan->worklist);
+    hipLaunchKernelGGL(k_sched_lpt, dim3(n_bh), dim3(1024), 0, stream, row_ptr, (int)in.n_blk, G,
+                       paired ? (const int2*)plan->pairs : nullptr, plan->worklist);
   AttnArgs a{};
   a.q = (const uint16_t*)q_perm;
   a.k = (const uint16_t*)k_perm;
@@ -566,6 +678,7 @@ static int attention_launch(fva_plan_t plan, const void* q_perm, const void* k_p
   a.blk_full = plan->blk_full;
   a.o = o_perm;
   a.worklist = plan->worklist;
+  a.pairs = paired ? plan->pairs : nullptr;
   a.cursor = plan->counters;
   a.wg_times = wg_times;
   a.lse = lse;

@@ -794,6 +794,13 @@ void launch_lists(fva_plan_t plan, const int32_t* row_ptr, const int32_t* col_id
 
 }  // namespace
 
+void fva_csr_bits(fva_plan_t plan, const int32_t* row_ptr, const int32_t* col_idx, uint64_t* bits,
+                  hipStream_t stream) {
+  const fva_plan_info& in = plan->info;
+  hipLaunchKernelGGL(k_csr_bits, dim3((unsigned)((in.n_rows + 3) / 4)), dim3(256), 0, stream, row_ptr, col_idx,
+                     (int)in.n_blk, plan->nw, in.n_rows, bits);
+}
+
 extern "C" int fva_mask_transpose(fva_plan_t plan, const int32_t* row_ptr, const int32_t* col_idx,
                                   int32_t* t_row_ptr, int32_t* t_col_idx, hipStream_t stream) {
   if (!plan) return fva_fail(FVA_EINVAL, "plan is NULL");

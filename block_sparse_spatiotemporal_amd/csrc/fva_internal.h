@@ -49,6 +49,7 @@ struct fva_plan_s {
   uint64_t* bits_t;   // [n_rows][nw] backward: transposed per-head block bitmap (key block -> query blocks)
   int32_t* worklist;  // [n_rows] attention rows in schedule order
   int32_t* worklist_t;// [n_rows] backward: key-block groups in schedule order
+  int2* pairs;        // [n_rows] attention: the two query blocks of each group of a head (second -1 if none)
   int32_t* counters;  // [64] work-queue cursor and misc counters
 
   void* dev_base;     // single device allocation holding everything above
@@ -71,3 +72,7 @@ struct SelectArgs {
 // Per-row id masks -> CSR (ascending ids) using the plan's selection
 // workspace (row counts, head totals and offsets).
 int fva_bits_to_csr(fva_plan_t plan, const uint64_t* bits, int32_t* row_ptr, int32_t* col_idx, hipStream_t stream);
+
+// CSR -> per-row 64-bit-word bitmaps (rows as sets, out-of-range ids dropped).
+void fva_csr_bits(fva_plan_t plan, const int32_t* row_ptr, const int32_t* col_idx, uint64_t* bits,
+                  hipStream_t stream);

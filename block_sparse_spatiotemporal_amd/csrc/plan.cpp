@@ -182,6 +182,7 @@ static void layout_workspace(const fva_plan_desc* d, const fva_plan_info& in, si
   offs[22] = c.take(sizeof(float) * bh * in.n_pad);                      // bwd_delta
   offs[23] = c.take(sizeof(uint64_t) * in.n_rows * nw);                 // bits_t
   offs[24] = c.take(sizeof(int32_t) * in.n_rows);                        // worklist_t
+  offs[25] = c.take(sizeof(int2) * in.n_rows);                           // pairs
   *total = c.off;
 }
 
@@ -260,7 +261,7 @@ extern "C" int fva_plan_dims(const fva_plan_desc* desc, fva_plan_info* info) {
   if (!info) return fva_fail(FVA_EINVAL, "info is NULL");
   int rc = validate(desc, info);
   if (rc) return rc;
-  size_t offs[25], total;
+  size_t offs[26], total;
   layout_workspace(desc, *info, offs, &total);
   info->workspace_bytes = (int64_t)total;
   return FVA_OK;
@@ -285,7 +286,7 @@ extern "C" int fva_plan_create(fva_plan_t* out, const fva_plan_desc* desc, hipSt
   fva_plan_info in;
   int rc = validate(desc, &in);
   if (rc) return rc;
-  size_t offs[25], total;
+  size_t offs[26], total;
   layout_workspace(desc, in, offs, &total);
   in.workspace_bytes = (int64_t)total;
 
@@ -338,6 +339,7 @@ extern "C" int fva_plan_create(fva_plan_t* out, const fva_plan_desc* desc, hipSt
   p->bwd_delta = (float*)(b + offs[22]);
   p->bits_t = (uint64_t*)(b + offs[23]);
   p->worklist_t = (int32_t*)(b + offs[24]);
+  p->pairs = (int2*)(b + offs[25]);
 
   // Synchronous upload from pageable memory: the tables are small and this
   // happens once per plan, outside any timed path.

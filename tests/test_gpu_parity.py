@@ -234,20 +234,24 @@ def test_wg_times_recorded():
 
 
 def test_launch_shapes_bitwise_equal(monkeypatch):
-    """Group size, LDS ring depth, XCD chunk, work-list order and schedule
-    change only the order rows are taken in, never a row's arithmetic:
-    outputs are bitwise equal."""
+    """Group size, query-block pairing, LDS ring depth, XCD chunk, work-list
+    order and schedule change only which rows share a workgroup and the
+    order they are taken in, never a row's arithmetic: outputs are bitwise
+    equal."""
     w = synth.scaled(synth.WORKLOADS["wan1.3b_480p"], H=3, grid=(9, 10, 13))
     plan, opl, (q, k, v), _, meta = _plan_and_inputs(w)
     ref = None
-    for group, stages, chunk, sched, order in [("1", "3", "32", "persistent", "0"), ("2", "2", "16", "plain", "1"),
-                                               ("4", "4", "1", "persistent", "1"), ("2", "3", "32", "persistent", "0"),
-                                               ("4", "2", "64", "plain", "0"), ("2", "4", "8", "plain", "1"),
-                                               ("2", "4", "32", "persistent", "1"), ("1", "4", "8", "persistent", "1")]:
+    for group, stages, chunk, sched, order, pair in [
+            ("1", "3", "32", "persistent", "0", "0"), ("2", "2", "16", "plain", "1", "1"),
+            ("4", "4", "1", "persistent", "1", "1"), ("2", "3", "32", "persistent", "0", "1"),
+            ("4", "2", "64", "plain", "0", "0"), ("2", "4", "8", "plain", "1", "0"),
+            ("2", "4", "32", "persistent", "1", "1"), ("1", "4", "8", "persistent", "1", "0"),
+            ("2", "4", "1000", "persistent", "1", "0")]:
         monkeypatch.setenv("FVA_ATTN_GROUP", group)
         monkeypatch.setenv("FVA_ATTN_STAGES", stages)
         monkeypatch.setenv("FVA_ATTN_CHUNK", chunk)
         monkeypatch.setenv("FVA_ATTN_ORDER", order)
+        monkeypatch.setenv("FVA_ATTN_PAIR", pair)
         b = fva.Buffers(plan)
         out = torch.empty_like(q)
         fva.attention_call(plan, q, k, v, out, 0.9, 16, b, sched=sched)
@@ -255,4 +259,4 @@ def test_launch_shapes_bitwise_equal(monkeypatch):
         if ref is None:
             ref = out
         else:
-            assert torch.equal(out, ref), (group, stages, chunk, sched, order)
+            assert torch.equal(out, ref), (group, stages, chunk, sched, order, pair)
