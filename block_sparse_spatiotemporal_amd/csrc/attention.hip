@@ -675,6 +675,14 @@ int occupancy(K kernel, int threads) {
 
 }  // namespace
 
+void fva_pair_blocks(fva_plan_t plan, const uint64_t* bits, int2* pairs, hipStream_t stream) {
+  const fva_plan_desc& d = plan->desc;
+  const fva_plan_info& in = plan->info;
+  const int nbw = in.padded[2] / d.tile[2], nbh = in.padded[1] / d.tile[1];
+  hipLaunchKernelGGL(k_pair, dim3(d.batch * d.heads), dim3(1024), 0, stream, bits, (int)in.n_blk, plan->nw, nbw, nbh,
+                     d.order == FVA_ORDER_HILBERT ? 1 : 0, pairs);
+}
+
 static int attention_launch(fva_plan_t plan, const void* q_perm, const void* k_perm, const void* vt_perm,
                             const int32_t* row_ptr, const int32_t* col_idx, void* o_perm, int32_t sched_mode,
                             uint64_t* wg_times, float* lse, float* o32, hipStream_t stream) {
@@ -690,10 +698,8 @@ static int attention_launch(fva_plan_t plan, const void* q_perm, const void* k_p
   if (d.head_dim == 64 && G > 2) G = 2;   // a 4 KB half splits over at most 4 waves
   const bool paired = G == 2 && attn_pair() == 1;
   if (paired) {
-    const int nbw = in.padded[2] / d.tile[2], nbh = in.padded[1] / d.tile[1];
     fva_csr_bits(plan, row_ptr, col_idx, plan->rowmask, stream);
-    hipLaunchKernelGGL(k_pair, dim3(n_bh), dim3(1024), 0, stream, plan->rowmask, (int)in.n_blk, plan->nw, nbw, nbh,
-                       d.order == FVA_ORDER_HILBERT ? 1 : 0, plan->pairs);
+    fva_pair_blocks(plan, plan->rowmask, plan->pairs, stream);
   }
   hipLaunchKernelGGL(k_sched, dim3(1), dim3(1024), 0, stream, row_ptr, in.n_blk, n_bh, G, plan->worklist,
                      plan->counters);

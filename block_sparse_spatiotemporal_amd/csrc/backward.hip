@@ -99,6 +99,7 @@ struct BwdArgs {
   int persistent;           // 1: resident grid popping groups from per-XCD cursors
   int32_t* cursor;          // [16] per-XCD cursors, then per-XCD exhausted flags (zeroed before launch)
   const int32_t* order;     // persistent: groups in schedule order (list position -> group)
+  const int2* pairs;        // optional (G = 2): the two blocks of each group, second -1 if none
   float scale;              // 1/sqrt(D)
 };
 
@@ -135,14 +136,17 @@ __device__ __forceinline__ int bwd_next(const BwdArgs& a, int* s_item, bool firs
 // by group id), so each XCD runs a head's long groups first and its short
 // ones last.
 __global__ __launch_bounds__(1024) void k_bwd_order(const uint64_t* __restrict__ bits, int n_blk, int nw, int G,
-                                                    int32_t* __restrict__ order) {
+                                                    const int2* __restrict__ pairs, int32_t* __restrict__ order) {
   __shared__ int cost[4096];
   const int ngh = (n_blk + G - 1) / G;
   const int bh = blockIdx.x;
   for (int g = threadIdx.x; g < ngh; g += 1024) {
     int c = 0;
-    for (int i = 0; i < G && g * G + i < n_blk; ++i) {
-      const uint64_t* row = bits + ((int64_t)bh * n_blk + g * G + i) * nw;
+    for (int i = 0; i < G; ++i) {
+      const int b = pairs ? (i == 0 ? pairs[(int64_t)bh * ngh + g].x : pairs[(int64_t)bh * ngh + g].y)
+                          : (g * G + i < n_blk ? g * G + i : -1);
+      if (b < 0) continue;
+      const uint64_t* row = bits + ((int64_t)bh * n_blk + b) * nw;
       for (int wd = 0; wd < nw; ++wd) c += __popcll(row[wd]);
     }
     cost[g] = c;
@@ -196,16 +200,31 @@ __device__ __forceinline__ void tile_offsets(int w, int lane, uint32_t* roff, ui
   }
 }
 
-// The G bitmaps of a group (rows of `bits` starting at row0; rows past the
-// head's last block are empty): this wave's own one (block g) and their
-// union, one 64-bit word per lane.
+// The blocks of group `item` (G consecutive ids from I0, or a pair from the
+// pair table), -1 past the head's last block.  Wave-uniform.
 template <int G>
-__device__ __forceinline__ void group_bits(const uint64_t* bits, int64_t row0, int nvalid, int nw, int lane, int g,
-                                           uint32_t* own_lo, uint32_t* own_hi, uint32_t* un_lo, uint32_t* un_hi) {
+__device__ __forceinline__ void group_blocks(const int2* pairs, int item, int I0, int n_blk, int* blk) {
+  if (G == 2 && pairs) {
+    const uint64_t v = sload((const uint64_t*)pairs, item);   // (x, y) of an int2
+    blk[0] = (int)(uint32_t)v;
+    blk[G - 1] = (int)(uint32_t)(v >> 32);
+  } else {
+#pragma unroll
+    for (int i = 0; i < G; ++i) blk[i] = I0 + i < n_blk ? I0 + i : -1;
+  }
+}
+
+// The G bitmaps of a group (rows head_row0 + blk[i] of `bits`; a -1 block
+// is empty): this wave's own one (member g) and their union, one 64-bit
+// word per lane.
+template <int G>
+__device__ __forceinline__ void group_bits(const uint64_t* bits, int64_t head_row0, const int* blk, int nw, int lane,
+                                           int g, uint32_t* own_lo, uint32_t* own_hi, uint32_t* un_lo,
+                                           uint32_t* un_hi) {
   uint64_t own = 0, un = 0;
 #pragma unroll
   for (int i = 0; i < G; ++i) {
-    const uint64_t x = (lane < nw && i < nvalid) ? bits[(row0 + i) * nw + lane] : 0;
+    const uint64_t x = (lane < nw && blk[i] >= 0) ? bits[(head_row0 + blk[i]) * nw + lane] : 0;
     un |= x;
     if (i == g) own = x;
   }
@@ -244,8 +263,10 @@ __global__ __launch_bounds__(128 * G, 2) void k_bwd_dq(BwdArgs a) {
   const int h = lane >> 5, l32 = lane & 31;
   const int ngh = (a.n_blk + G - 1) / G;
   const int bh = item / ngh, I0 = (item - bh * ngh) * G;
-  const bool has_row = I0 + qg < a.n_blk;
-  const int I = has_row ? I0 + qg : I0;
+  int blk[G];
+  group_blocks<G>(a.pairs, item, I0, a.n_blk, blk);
+  const bool has_row = blk[qg] >= 0;
+  const int I = has_row ? blk[qg] : blk[0];
   const int64_t head = (int64_t)bh * a.n_pad;
   const int64_t tok = head + (int64_t)I * 64 + 32 * w2 + l32;
   const float sl2 = a.scale * 1.44269504088896340736f;
@@ -254,7 +275,7 @@ __global__ __launch_bounds__(128 * G, 2) void k_bwd_dq(BwdArgs a) {
   uint32_t roff[LPW], toff[LPW];
   tile_offsets<D, LPW, NW>(w, lane, roff, toff);
   uint32_t own_lo, own_hi, un_lo, un_hi;
-  group_bits<G>(a.bits, (int64_t)bh * a.n_blk + I0, a.n_blk - I0, a.nw, lane, qg, &own_lo, &own_hi, &un_lo, &un_hi);
+  group_bits<G>(a.bits, (int64_t)bh * a.n_blk, blk, a.nw, lane, qg, &own_lo, &own_hi, &un_lo, &un_hi);
   const uint64_t fw = lane < a.nw ? a.blk_full[lane] : 0;
   const uint32_t full_lo = (uint32_t)fw, full_hi = (uint32_t)(fw >> 32);
 
@@ -400,8 +421,10 @@ __global__ __launch_bounds__(128 * G, G) void k_bwd_dkdv(BwdArgs a) {
   const int h = lane >> 5, l32 = lane & 31;
   const int ngh = (a.n_blk + G - 1) / G;
   const int bh = item / ngh, J0 = (item - bh * ngh) * G;
-  const bool has_blk = J0 + kg < a.n_blk;
-  const int J = has_blk ? J0 + kg : J0;
+  int blk[G];
+  group_blocks<G>(a.pairs, item, J0, a.n_blk, blk);
+  const bool has_blk = blk[kg] >= 0;
+  const int J = has_blk ? blk[kg] : blk[0];
   const int64_t head = (int64_t)bh * a.n_pad;
   const int64_t tok = head + (int64_t)J * 64 + 32 * w2 + l32;   // this lane's key token
   const float sl2 = a.scale * 1.44269504088896340736f;
@@ -411,8 +434,7 @@ __global__ __launch_bounds__(128 * G, G) void k_bwd_dkdv(BwdArgs a) {
   uint32_t roff[LPW], toff[LPW];
   tile_offsets<D, LPW, NW>(w, lane, roff, toff);
   uint32_t own_lo, own_hi, un_lo, un_hi;
-  group_bits<G>(a.bits_t, (int64_t)bh * a.n_blk + J0, a.n_blk - J0, a.nw, lane, kg, &own_lo, &own_hi, &un_lo,
-                &un_hi);
+  group_bits<G>(a.bits_t, (int64_t)bh * a.n_blk, blk, a.nw, lane, kg, &own_lo, &own_hi, &un_lo, &un_hi);
 
   bf16x8 kreg[KS], vreg[KS];
   {
@@ -582,8 +604,10 @@ __global__ __launch_bounds__(128 * G, OCC) void k_bwd_dkv(BwdArgs a) {
   const int h = lane >> 5, l32 = lane & 31;
   const int ngh = (a.n_blk + G - 1) / G;
   const int bh = item / ngh, J0 = (item - bh * ngh) * G;
-  const bool has_blk = J0 + kg < a.n_blk;
-  const int J = has_blk ? J0 + kg : J0;
+  int blk[G];
+  group_blocks<G>(a.pairs, item, J0, a.n_blk, blk);
+  const bool has_blk = blk[kg] >= 0;
+  const int J = has_blk ? blk[kg] : blk[0];
   const int64_t head = (int64_t)bh * a.n_pad;
   const int64_t tok = head + (int64_t)J * 64 + 32 * w2 + l32;   // this lane's key token
   const float sl2 = a.scale * 1.44269504088896340736f;
@@ -593,8 +617,7 @@ __global__ __launch_bounds__(128 * G, OCC) void k_bwd_dkv(BwdArgs a) {
   uint32_t roff[LPW], toff[LPW];
   tile_offsets<D, LPW, NW>(w, lane, roff, toff);
   uint32_t own_lo, own_hi, un_lo, un_hi;
-  group_bits<G>(a.bits_t, (int64_t)bh * a.n_blk + J0, a.n_blk - J0, a.nw, lane, kg, &own_lo, &own_hi, &un_lo,
-                &un_hi);
+  group_bits<G>(a.bits_t, (int64_t)bh * a.n_blk, blk, a.nw, lane, kg, &own_lo, &own_hi, &un_lo, &un_hi);
 
   bf16x8 kreg[KS], vreg[DK ? KS : 1];
   {
@@ -759,13 +782,14 @@ int bwd_occupancy(K kernel, int threads) {
 // its own cursor set (16 counters, zeroed by the caller).
 template <typename K>
 void bwd_launch(K kernel, int threads, int G, BwdArgs a, fva_plan_t plan, int32_t* cursor, const int32_t* order,
-                hipStream_t stream) {
+                const int2* pairs, hipStream_t stream) {
   const int n_bh = plan->desc.batch * plan->desc.heads;
   const int ngh = (int)((plan->info.n_blk + G - 1) / G);
   a.n_items = n_bh * ngh;
   a.persistent = bwd_persistent() ? 1 : 0;
   a.cursor = cursor;
   a.order = order;
+  a.pairs = G == 2 ? pairs : nullptr;
   // whole heads per XCD chunk, cut into 8 / gcd(heads, 8) parts so every
   // XCD gets the same number of chunks
   int gc = n_bh, bb = kXcds;
@@ -863,33 +887,44 @@ extern "C" int fva_attention_backward(fva_plan_t plan, const void* q_perm, const
   const int GK = kmode == 1 ? 1 : 2;
   int32_t* oq = plan->worklist;
   int32_t* ok = plan->worklist_t;
+  // groups of two by list overlap: query blocks over rows, key blocks over
+  // columns (FVA_BWD_PAIR=0: consecutive ids)
+  const bool paired = env_pick("FVA_BWD_PAIR", 0, 1, 1) == 1;
+  const int2* pq = paired ? plan->pairs : nullptr;
+  const int2* pk = paired && GK == 2 ? plan->pairs_t : nullptr;
+  if (paired) {
+    fva_pair_blocks(plan, plan->rowmask, plan->pairs, stream);
+    if (GK == 2) fva_pair_blocks(plan, plan->bits_t, plan->pairs_t, stream);
+  }
   if (bwd_persistent()) {
-    hipLaunchKernelGGL(k_bwd_order, dim3(n_bh), dim3(1024), 0, stream, plan->rowmask, (int)in.n_blk, plan->nw, GQ, oq);
-    hipLaunchKernelGGL(k_bwd_order, dim3(n_bh), dim3(1024), 0, stream, plan->bits_t, (int)in.n_blk, plan->nw, GK, ok);
+    hipLaunchKernelGGL(k_bwd_order, dim3(n_bh), dim3(1024), 0, stream, plan->rowmask, (int)in.n_blk, plan->nw, GQ, pq,
+                       oq);
+    hipLaunchKernelGGL(k_bwd_order, dim3(n_bh), dim3(1024), 0, stream, plan->bits_t, (int)in.n_blk, plan->nw, GK, pk,
+                       ok);
   }
   if (d.head_dim == 128) {
-    bwd_launch(k_bwd_dq<128, 3, GQ>, 128 * GQ, GQ, a, plan, cq, oq, stream);
+    bwd_launch(k_bwd_dq<128, 3, GQ>, 128 * GQ, GQ, a, plan, cq, oq, pq, stream);
     if (kmode == 0) {
-      if (dv_occ == 3) bwd_launch(k_bwd_dkv<128, 3, 2, false, 3>, 256, 2, a, plan, cv, ok, stream);
-      else bwd_launch(k_bwd_dkv<128, 3, 2, false, 2>, 256, 2, a, plan, cv, ok, stream);
-      if (dk_nst == 3) bwd_launch(k_bwd_dkv<128, 3, 2, true, 2>, 256, 2, a, plan, ck, ok, stream);
-      else bwd_launch(k_bwd_dkv<128, 2, 2, true, 2>, 256, 2, a, plan, ck, ok, stream);
+      if (dv_occ == 3) bwd_launch(k_bwd_dkv<128, 3, 2, false, 3>, 256, 2, a, plan, cv, ok, pk, stream);
+      else bwd_launch(k_bwd_dkv<128, 3, 2, false, 2>, 256, 2, a, plan, cv, ok, pk, stream);
+      if (dk_nst == 3) bwd_launch(k_bwd_dkv<128, 3, 2, true, 2>, 256, 2, a, plan, ck, ok, pk, stream);
+      else bwd_launch(k_bwd_dkv<128, 2, 2, true, 2>, 256, 2, a, plan, ck, ok, pk, stream);
     } else if (kmode == 2) {
-      bwd_launch(k_bwd_dkdv<128, 2, 2>, 256, 2, a, plan, cv, ok, stream);
+      bwd_launch(k_bwd_dkdv<128, 2, 2>, 256, 2, a, plan, cv, ok, pk, stream);
     } else {
-      bwd_launch(k_bwd_dkdv<128, 2, 1>, 128, 1, a, plan, cv, ok, stream);
+      bwd_launch(k_bwd_dkdv<128, 2, 1>, 128, 1, a, plan, cv, ok, pk, stream);
     }
   } else {
-    bwd_launch(k_bwd_dq<64, 3, GQ>, 128 * GQ, GQ, a, plan, cq, oq, stream);
+    bwd_launch(k_bwd_dq<64, 3, GQ>, 128 * GQ, GQ, a, plan, cq, oq, pq, stream);
     if (kmode == 0) {
-      if (dv_occ == 3) bwd_launch(k_bwd_dkv<64, 3, 2, false, 3>, 256, 2, a, plan, cv, ok, stream);
-      else bwd_launch(k_bwd_dkv<64, 3, 2, false, 2>, 256, 2, a, plan, cv, ok, stream);
-      if (dk_nst == 3) bwd_launch(k_bwd_dkv<64, 3, 2, true, 2>, 256, 2, a, plan, ck, ok, stream);
-      else bwd_launch(k_bwd_dkv<64, 2, 2, true, 2>, 256, 2, a, plan, ck, ok, stream);
+      if (dv_occ == 3) bwd_launch(k_bwd_dkv<64, 3, 2, false, 3>, 256, 2, a, plan, cv, ok, pk, stream);
+      else bwd_launch(k_bwd_dkv<64, 3, 2, false, 2>, 256, 2, a, plan, cv, ok, pk, stream);
+      if (dk_nst == 3) bwd_launch(k_bwd_dkv<64, 3, 2, true, 2>, 256, 2, a, plan, ck, ok, pk, stream);
+      else bwd_launch(k_bwd_dkv<64, 2, 2, true, 2>, 256, 2, a, plan, ck, ok, pk, stream);
     } else if (kmode == 2) {
-      bwd_launch(k_bwd_dkdv<64, 2, 2>, 256, 2, a, plan, cv, ok, stream);
+      bwd_launch(k_bwd_dkdv<64, 2, 2>, 256, 2, a, plan, cv, ok, pk, stream);
     } else {
-      bwd_launch(k_bwd_dkdv<64, 2, 1>, 128, 1, a, plan, cv, ok, stream);
+      bwd_launch(k_bwd_dkdv<64, 2, 1>, 128, 1, a, plan, cv, ok, pk, stream);
     }
   }
   return fva_after_launch(stream, "fva_attention_backward");

@@ -50,6 +50,7 @@ struct fva_plan_s {
   int32_t* worklist;  // [n_rows] attention rows in schedule order
   int32_t* worklist_t;// [n_rows] backward: key-block groups in schedule order
   int2* pairs;        // [n_rows] attention: the two query blocks of each group of a head (second -1 if none)
+  int2* pairs_t;      // [n_rows] backward: the two key blocks of each group of a head
   int32_t* counters;  // [64] work-queue cursor and misc counters
 
   void* dev_base;     // single device allocation holding everything above
@@ -76,3 +77,7 @@ int fva_bits_to_csr(fva_plan_t plan, const uint64_t* bits, int32_t* row_ptr, int
 // CSR -> per-row 64-bit-word bitmaps (rows as sets, out-of-range ids dropped).
 void fva_csr_bits(fva_plan_t plan, const int32_t* row_ptr, const int32_t* col_idx, uint64_t* bits,
                   hipStream_t stream);
+
+// Pairs of neighbouring blocks with overlapping bitmap rows, per head
+// (ceil(n_blk / 2) entries per head; second -1 for a single block).
+void fva_pair_blocks(fva_plan_t plan, const uint64_t* bits, int2* pairs, hipStream_t stream);

@@ -183,6 +183,7 @@ static void layout_workspace(const fva_plan_desc* d, const fva_plan_info& in, si
   offs[23] = c.take(sizeof(uint64_t) * in.n_rows * nw);                 // bits_t
   offs[24] = c.take(sizeof(int32_t) * in.n_rows);                        // worklist_t
   offs[25] = c.take(sizeof(int2) * in.n_rows);                           // pairs
+  offs[26] = c.take(sizeof(int2) * in.n_rows);                           // pairs_t
   *total = c.off;
 }
 
@@ -261,7 +262,7 @@ extern "C" int fva_plan_dims(const fva_plan_desc* desc, fva_plan_info* info) {
   if (!info) return fva_fail(FVA_EINVAL, "info is NULL");
   int rc = validate(desc, info);
   if (rc) return rc;
-  size_t offs[26], total;
+  size_t offs[27], total;
   layout_workspace(desc, *info, offs, &total);
   info->workspace_bytes = (int64_t)total;
   return FVA_OK;
@@ -286,7 +287,7 @@ extern "C" int fva_plan_create(fva_plan_t* out, const fva_plan_desc* desc, hipSt
   fva_plan_info in;
   int rc = validate(desc, &in);
   if (rc) return rc;
-  size_t offs[26], total;
+  size_t offs[27], total;
   layout_workspace(desc, in, offs, &total);
   in.workspace_bytes = (int64_t)total;
 
@@ -340,6 +341,7 @@ extern "C" int fva_plan_create(fva_plan_t* out, const fva_plan_desc* desc, hipSt
   p->bits_t = (uint64_t*)(b + offs[23]);
   p->worklist_t = (int32_t*)(b + offs[24]);
   p->pairs = (int2*)(b + offs[25]);
+  p->pairs_t = (int2*)(b + offs[26]);
 
   // Synchronous upload from pageable memory: the tables are small and this
   // happens once per plan, outside any timed path.

@@ -253,9 +253,10 @@ def test_backward_full_size_sampled():
 
 
 def test_backward_schedules_and_variants_bitwise_equal(monkeypatch):
-    """Persistent or plain grids, XCD chunk, split or fused dK/dV kernels and
-    their tuning switches change only which workgroup computes a block, never
-    its arithmetic: the gradients are bitwise equal."""
+    """Persistent or plain grids, XCD chunk, block pairing, split or fused
+    dK/dV kernels and their tuning switches change only which workgroup
+    computes a block, never its arithmetic: the gradients are bitwise
+    equal."""
     w = synth.scaled(synth.WORKLOADS["wan1.3b_480p"], H=3, grid=(9, 10, 13))
     n = O.plan(w.grid).n_blk
     rng = np.random.default_rng(3)
@@ -263,8 +264,9 @@ def test_backward_schedules_and_variants_bitwise_equal(monkeypatch):
     ref = None
     for env in [{}, {"FVA_BWD_SCHED": "plain"}, {"FVA_BWD_CHUNK": "3"}, {"FVA_BWD_SCHED": "plain", "FVA_BWD_CHUNK": "5"},
                 {"FVA_BWD_KGROUP": "1"}, {"FVA_BWD_KGROUP": "2", "FVA_BWD_SCHED": "plain"},
-                {"FVA_BWD_DV_OCC": "2", "FVA_BWD_DK_NST": "3"}]:
-        for k in ("FVA_BWD_SCHED", "FVA_BWD_CHUNK", "FVA_BWD_KGROUP", "FVA_BWD_DV_OCC", "FVA_BWD_DK_NST"):
+                {"FVA_BWD_DV_OCC": "2", "FVA_BWD_DK_NST": "3"}, {"FVA_BWD_PAIR": "0"},
+                {"FVA_BWD_PAIR": "0", "FVA_BWD_SCHED": "plain"}]:
+        for k in ("FVA_BWD_SCHED", "FVA_BWD_CHUNK", "FVA_BWD_KGROUP", "FVA_BWD_DV_OCC", "FVA_BWD_DK_NST", "FVA_BWD_PAIR"):
             monkeypatch.delenv(k, raising=False)
         for k, v in env.items():
             monkeypatch.setenv(k, v)
