@@ -2,15 +2,20 @@
 one MI355X.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                  [--sched persistent|plain] [--no-cpu] [--cpu-heads N]
+                  [--sched persistent|plain] [--no-cpu] [--cpu-heads N] [--unfused]
   python bench.py --copy-probe MIB     # plain device copy of a known size,
                                        # the calibration run for HBM counters
 
 A step is one whole call: permute Q, K, V -> select (pool, score, Top-p with
 Top-k floor, CSR) -> block-sparse attention -> unpermute O, on one HIP stream
-with the inputs already resident in HBM.  Events recorded on that stream
-between the stages of every timed step give the per-stage times (the
-attention stage is a single kernel launch after a tiny scheduling kernel).
+with the inputs already resident in HBM.  By default the permutes of Q and K
+also pool (fva_permute_pool; fva_select_pooled then scores and selects) and
+the attention writes O straight to raster order (fva_attention_raster: the
+unpermute is its epilogue); with --unfused the same steps run as the six
+separate calls fva_permute x3, fva_select, fva_attention, fva_unpermute.  Events recorded
+on that stream between the stages of every timed step give the per-stage
+times (the attention stage is one kernel launch after the small pairing and
+scheduling kernels).
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -44,6 +49,8 @@ def parse():
     ap.add_argument("--sched", default="persistent", choices=["persistent", "plain"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-backward", action="store_true", help="skip the training-step (backward) timing")
+    ap.add_argument("--unfused", action="store_true",
+                    help="separate pool (inside fva_select) and unpermute calls")
     ap.add_argument("--cpu-heads", type=int, default=4, help="(b,h) pairs in the CPU oracle sample")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (counter calibration)")
@@ -141,32 +148,44 @@ def main():
     p_head = meta["p_head"]
     p = p_head.tolist() if isinstance(w.p, tuple) else float(p_head[0])
 
-    names = ["permute_q", "permute_k", "permute_v", "select", "attention", "unpermute"]
+    names = ["permute_q", "permute_k", "permute_v", "select", "attention"] + (["unpermute"] if args.unfused else [])
 
     def call(ev=None):
-        # the same six C-ABI calls as fva.attention_call, with events between them
+        # the C-ABI calls of fva.attention_call, with events between them
         rec = (lambda i: ev[i].record()) if ev else (lambda i: None)
         rec(0)
-        fva.fva_permute(plan, qd, bufs.q, fva.LAYOUT_ROWS); rec(1)
-        fva.fva_permute(plan, kd, bufs.k, fva.LAYOUT_ROWS); rec(2)
+        if args.unfused:
+            fva.fva_permute(plan, qd, bufs.q, fva.LAYOUT_ROWS); rec(1)
+            fva.fva_permute(plan, kd, bufs.k, fva.LAYOUT_ROWS); rec(2)
+        else:
+            fva.fva_permute_pool(plan, qd, bufs.q, "q"); rec(1)
+            fva.fva_permute_pool(plan, kd, bufs.k, "k"); rec(2)
         fva.fva_permute(plan, vd, bufs.vt, fva.LAYOUT_VT); rec(3)
-        fva.fva_select(plan, bufs.q, bufs.k, p, w.k_min, bufs.row_ptr, bufs.col_idx, slack=w.slack,
-                       head_nnz=bufs.head_nnz); rec(4)
-        fva.fva_attention(plan, bufs.q, bufs.k, bufs.vt, bufs.row_ptr, bufs.col_idx, bufs.o,
-                          sched=args.sched); rec(5)
-        fva.fva_unpermute(plan, bufs.o, out); rec(6)
+        if args.unfused:
+            fva.fva_select(plan, bufs.q, bufs.k, p, w.k_min, bufs.row_ptr, bufs.col_idx, slack=w.slack,
+                           head_nnz=bufs.head_nnz); rec(4)
+        else:
+            fva.fva_select_pooled(plan, p, w.k_min, bufs.row_ptr, bufs.col_idx, slack=w.slack,
+                                  head_nnz=bufs.head_nnz); rec(4)
+        if args.unfused:
+            fva.fva_attention(plan, bufs.q, bufs.k, bufs.vt, bufs.row_ptr, bufs.col_idx, bufs.o,
+                              sched=args.sched); rec(5)
+            fva.fva_unpermute(plan, bufs.o, out); rec(6)
+        else:
+            fva.fva_attention_raster(plan, bufs.q, bufs.k, bufs.vt, bufs.row_ptr, bufs.col_idx, out,
+                                     sched=args.sched); rec(5)
 
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
 
     # exactly `steps` timed calls; events on the launch stream between stages
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
         call(evs[i])
     torch.cuda.synchronize()
-    ms_call = evs[0][0].elapsed_time(evs[-1][6]) / args.steps
+    ms_call = evs[0][0].elapsed_time(evs[-1][len(names)]) / args.steps
     stage = {n: np.array([e[j].elapsed_time(e[j + 1]) for e in evs]) for j, n in enumerate(names)}
     st_mean = {n: float(x.mean()) for n, x in stage.items()}
     st_med = {n: float(np.median(x)) for n, x in stage.items()}
@@ -187,8 +206,7 @@ def main():
         fva.fva_permute(plan, qd, bufs.q, fva.LAYOUT_ROWS)
         fva.fva_permute(plan, kd, bufs.k, fva.LAYOUT_ROWS)
         fva.fva_permute(plan, vd, bufs.vt, fva.LAYOUT_VT)
-        fva.fva_attention(plan, bufs.q, bufs.k, bufs.vt, bufs.row_ptr, bufs.col_idx, bufs.o, sched=args.sched)
-        fva.fva_unpermute(plan, bufs.o, out)
+        fva.fva_attention_raster(plan, bufs.q, bufs.k, bufs.vt, bufs.row_ptr, bufs.col_idx, out, sched=args.sched)
     counts = torch.empty(w.B * w.H, 2, dtype=torch.int64, device="cuda")
     e_u0, e_u1, e_u2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
     e_u0.record()
@@ -259,7 +277,7 @@ def main():
     perm_bytes = BH * (N * row + plan.n_pad * row)        # read valid rows, write every padded row
     unperm_bytes = BH * 2 * N * row
     n_kbar = n_blk * (8 if w.sub[0] else 1)
-    sel_bytes = (2 * BH * N * row                           # pool reads Q and K once
+    sel_bytes = ((2 * BH * N * row if args.unfused else 0)  # pool reads Q and K once (unless fused)
                  + BH * (n_blk + n_kbar) * w.D * 8          # pooled Q, K written (fp64)
                  + BH * n_blk * n_blk * 4                   # fp32 scores, one pass
                  + 4 * nnz + 4 * (plan.n_rows + 1))         # CSR out
@@ -295,7 +313,8 @@ def main():
         "hbm_gbs": {"permute_rows": round(perm_bytes / (st_mean["permute_q"] * 1e-3) / 1e9, 1),
                     "permute_vt": round(perm_bytes / (st_mean["permute_v"] * 1e-3) / 1e9, 1),
                     "select": round(sel_bytes / (st_mean["select"] * 1e-3) / 1e9, 1),
-                    "unpermute": round(unperm_bytes / (st_mean["unpermute"] * 1e-3) / 1e9, 1),
+                    **({"unpermute": round(unperm_bytes / (st_mean["unpermute"] * 1e-3) / 1e9, 1)}
+                       if args.unfused else {}),
                     "peak": PEAK_HBM_GBS},
         "load_balance": balance,
         "permute_rope_ms": round(rope_ms, 4),
@@ -304,7 +323,7 @@ def main():
         "training": backward,
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "k_attn_bf16 (fva_attention)",
+                     "traffic": traffic, "kernel": "k_attn_bf16 (" + ("fva_attention" if args.unfused else "fva_attention_raster") + ")",
                      "launch_ms": round(st_mean["attention"], 4)},
     }
     if not args.no_cpu:

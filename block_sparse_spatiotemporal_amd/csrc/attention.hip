@@ -35,6 +35,9 @@ struct AttnArgs {
   uint64_t* wg_times;
   float* lse;               // optional [B*H, n_pad]: log2 sum exp2 of the scaled scores
   float* o32;               // optional [B*H, n_pad, D]: the output before rounding to bf16
+  const int32_t* perm;      // optional: write O in raster order [B, N, H, D] (position -> token)
+  int64_t n_tok;            // raster tokens per batch entry (with perm)
+  int heads;                // H (with perm)
   int64_t n_pad;
   int n_items;
   int n_blk;
@@ -69,6 +72,18 @@ __device__ __forceinline__ int next_item(const AttnArgs& a, int* s_item, bool fi
   }
   __syncthreads();
   return *s_item;
+}
+
+// Output row of query position `pos` of (b, h) = bh: block order
+// [B*H, n_pad, D], or with a.perm the raster row [b, perm[pos], h, :]; null
+// for a pad position in raster order (nothing is written there).
+template <typename T>
+__device__ __forceinline__ T* out_row(const AttnArgs& a, int bh, int64_t pos, int D) {
+  if (!a.perm) return (T*)a.o + ((int64_t)bh * a.n_pad + pos) * D;
+  const int tok = a.perm[pos];
+  if (tok < 0) return nullptr;
+  const int b = bh / a.heads, h = bh - b * a.heads;
+  return (T*)a.o + (((int64_t)b * a.n_tok + tok) * a.heads + h) * D;
 }
 
 // ------------------------------------------------------------------ bf16
@@ -319,7 +334,7 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
       const float l_tot = xhalf_sum(l_run);
       const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
       const bool qvalid = sload(a.blk_mask, I) >> (32 * w2 + l32) & 1;
-      uint16_t* orow = (uint16_t*)a.o + (head + (int64_t)I * 64 + 32 * w2 + l32) * D;
+      uint16_t* orow = out_row<uint16_t>(a, bh, (int64_t)I * 64 + 32 * w2 + l32, D);
       if (LSE && h == 0)   // P_ij = exp2(s_ij * scale * log2(e) - lse_i) for the backward pass
         a.lse[head + (int64_t)I * 64 + 32 * w2 + l32] = qvalid && l_tot > 0.0f ? m_run + __log2f(l_tot) : 0.0f;
 #pragma unroll
@@ -331,7 +346,7 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
           f32x4 v = {o[dt][4 * g4] * inv, o[dt][4 * g4 + 1] * inv, o[dt][4 * g4 + 2] * inv, o[dt][4 * g4 + 3] * inv};
           if (!qvalid) v = f32x4{0.f, 0.f, 0.f, 0.f};
           const bf16x4 b = __builtin_convertvector(v, bf16x4);
-          *(uint2*)(orow + 32 * dt + 8 * g4 + 4 * h) = __builtin_bit_cast(uint2, b);
+          if (orow) *(uint2*)(orow + 32 * dt + 8 * g4 + 4 * h) = __builtin_bit_cast(uint2, b);
           if (LSE)
             *(f32x4*)(a.o32 + (head + (int64_t)I * 64 + 32 * w2 + l32) * D + 32 * dt + 8 * g4 + 4 * h) = v;
         }
@@ -419,9 +434,11 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a) {
     }
     const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
     const bool qvalid = a.blk_mask[I] >> qi & 1;
-    float* orow = (float*)a.o + (head + (int64_t)I * 64 + qi) * D + part * DP;
+    float* orow = out_row<float>(a, bh, (int64_t)I * 64 + qi, D);
+    if (orow) {
 #pragma unroll
-    for (int d = 0; d < DP; ++d) orow[d] = qvalid ? o[d] * inv : 0.0f;
+      for (int d = 0; d < DP; ++d) orow[part * DP + d] = qvalid ? o[d] * inv : 0.0f;
+    }
   }
   if (a.wg_times && tid == 0) {
     a.wg_times[2 * blockIdx.x] = t0;
@@ -685,7 +702,7 @@ void fva_pair_blocks(fva_plan_t plan, const uint64_t* bits, int2* pairs, hipStre
 
 static int attention_launch(fva_plan_t plan, const void* q_perm, const void* k_perm, const void* vt_perm,
                             const int32_t* row_ptr, const int32_t* col_idx, void* o_perm, int32_t sched_mode,
-                            uint64_t* wg_times, float* lse, float* o32, hipStream_t stream) {
+                            uint64_t* wg_times, float* lse, float* o32, bool raster, hipStream_t stream) {
   if (!plan) return fva_fail(FVA_EINVAL, "plan is NULL");
   if (!q_perm || !k_perm || !vt_perm || !o_perm) return fva_fail(FVA_EINVAL, "tensor pointer is NULL");
   if (!row_ptr || !col_idx) return fva_fail(FVA_EINVAL, "row_ptr / col_idx is NULL");
@@ -724,6 +741,9 @@ static int attention_launch(fva_plan_t plan, const void* q_perm, const void* k_p
   a.wg_times = wg_times;
   a.lse = lse;
   a.o32 = o32;
+  a.perm = raster ? plan->perm : nullptr;
+  a.n_tok = in.n_tokens;
+  a.heads = d.heads;
   a.n_pad = in.n_pad;
   a.n_items = n_bh * ((in.n_blk + G - 1) / G);
   a.n_blk = in.n_blk;
@@ -776,7 +796,14 @@ extern "C" int fva_attention(fva_plan_t plan, const void* q_perm, const void* k_
                              const int32_t* row_ptr, const int32_t* col_idx, void* o_perm, int32_t sched_mode,
                              uint64_t* wg_times, hipStream_t stream) {
   return attention_launch(plan, q_perm, k_perm, vt_perm, row_ptr, col_idx, o_perm, sched_mode, wg_times, nullptr,
-                          nullptr, stream);
+                          nullptr, false, stream);
+}
+
+extern "C" int fva_attention_raster(fva_plan_t plan, const void* q_perm, const void* k_perm, const void* vt_perm,
+                                    const int32_t* row_ptr, const int32_t* col_idx, void* o_raster,
+                                    int32_t sched_mode, hipStream_t stream) {
+  return attention_launch(plan, q_perm, k_perm, vt_perm, row_ptr, col_idx, o_raster, sched_mode, nullptr, nullptr,
+                          nullptr, true, stream);
 }
 
 extern "C" int fva_attention_lse(fva_plan_t plan, const void* q_perm, const void* k_perm, const void* vt_perm,
@@ -786,5 +813,5 @@ extern "C" int fva_attention_lse(fva_plan_t plan, const void* q_perm, const void
   if (!lse || !o32) return fva_fail(FVA_EINVAL, "lse / o32 is NULL");
   if (plan->desc.dtype != FVA_DTYPE_BF16) return fva_fail(FVA_EUNSUPPORTED, "the training path is bf16 only");
   return attention_launch(plan, q_perm, k_perm, vt_perm, row_ptr, col_idx, o_perm, FVA_SCHED_PERSISTENT, nullptr,
-                          lse, o32, stream);
+                          lse, o32, false, stream);
 }

@@ -53,6 +53,11 @@ struct fva_plan_s {
   int2* pairs_t;      // [n_rows] backward: the two key blocks of each group of a head
   int32_t* counters;  // [64] work-queue cursor and misc counters
 
+  // host state: bit 0 / bit 1 set once fva_permute_pool has enqueued the
+  // pooled means of Q / K into qbar / kbar (cleared when fva_select pools
+  // its own inputs there)
+  int pooled;
+
   void* dev_base;     // single device allocation holding everything above
   size_t dev_bytes;
 };

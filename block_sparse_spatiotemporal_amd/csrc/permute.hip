@@ -224,6 +224,76 @@ __global__ __launch_bounds__(kThreads) void k_permute_rope(const uint4* __restri
   }
 }
 
+// fva_permute (rows) of one block plus its pooled means, so the selection
+// need not read the block-order tensor again ("Video Sparse Attention"
+// explainer, section 3: one mean per (4,4,4) cube; "DFSAttn" trick 2: one
+// per (2,2,2) sub-block for K when the plan has sub-blocks).  One workgroup
+// per (block, b*h): the rows move as in k_permute_rows and a copy stays in
+// LDS, from which the means are summed in fp64 in the order the separate
+// pooling kernels use (row groups g, g+RG, ... per column, then the groups
+// in order; sub-block members in table order), so the means are the same
+// bits.  Pad rows are zero, so the sums run over all 64 rows.
+template <typename T, int D, bool SUB>
+__global__ __launch_bounds__(kThreads) void k_permute_pool(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                           const int32_t* __restrict__ perm, int64_t n_tok,
+                                                           int heads, int64_t n_pad, int n_blk,
+                                                           const int32_t* __restrict__ blk_cnt,
+                                                           const uint8_t* __restrict__ sub_pos,
+                                                           const int32_t* __restrict__ sub_cnt,
+                                                           double* __restrict__ bar) {
+  constexpr int CPR = D * (int)sizeof(T) / 16;   // 16-byte chunks per row
+  constexpr int NCH = 64 * CPR;                  // chunks per block
+  constexpr int PER = NCH / kThreads;
+  constexpr int RG = 64 / CPR;                   // row groups of the column sums
+  constexpr int RPL = 64 / RG;
+  static_assert(NCH % kThreads == 0, "whole chunks per thread");
+  __shared__ uint4 tile[NCH];
+  __shared__ double part[SUB ? 1 : RG][D];
+  const int blk = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / heads, h = bh - b * heads;
+  const int t = threadIdx.x;
+  uint4* out = dst + ((int64_t)bh * n_pad + (int64_t)blk * 64) * CPR;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int c = t + kThreads * u;
+    const int row = c / CPR, ch = c - row * CPR;
+    const int tok = perm[blk * 64 + row];
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (tok >= 0) v = src[(((int64_t)b * n_tok + tok) * heads + h) * CPR + ch];
+    out[c] = v;
+    tile[c] = v;
+  }
+  __syncthreads();
+  const T* x = (const T*)tile;   // x[row * D + d]
+  if (!SUB) {
+    for (int e = t; e < RG * D; e += kThreads) {
+      const int g = e / D, d = e - g * D;
+      double acc = 0.0;
+#pragma unroll 8
+      for (int i = 0; i < RPL; ++i) acc += (double)ld_val(x + (g + RG * i) * D + d);
+      part[g][d] = acc;
+    }
+    __syncthreads();
+    if (t < D) {
+      double sum = 0.0;
+#pragma unroll
+      for (int g = 0; g < RG; ++g) sum += part[g][t];
+      bar[((int64_t)bh * n_blk + blk) * D + t] = sum / (double)blk_cnt[blk];
+    }
+  } else {
+    double* o = bar + ((int64_t)bh * n_blk + blk) * 8 * D;
+    for (int e = t; e < 8 * D; e += kThreads) {
+      const int sb = e / D, d = e - sb * D;
+      const uint8_t* pos = sub_pos + ((int64_t)blk * 8 + sb) * 8;
+      double acc = 0.0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc += (double)ld_val(x + (int)pos[i] * D + d);
+      const int cnt = sub_cnt[blk * 8 + sb];
+      o[e] = cnt ? acc / (double)cnt : 0.0;
+    }
+  }
+}
+
 int check_common(fva_plan_t plan, const void* a, const void* b) {
   if (!plan) return fva_fail(FVA_EINVAL, "plan is NULL");
   if (!a || !b) return fva_fail(FVA_EINVAL, "tensor pointer is NULL");
@@ -266,6 +336,32 @@ extern "C" int fva_permute(fva_plan_t plan, const void* x_raster, void* x_perm, 
     }
   }
   return fva_after_launch(stream, "fva_permute");
+}
+
+extern "C" int fva_permute_pool(fva_plan_t plan, const void* x_raster, void* x_perm, int32_t which,
+                                hipStream_t stream) {
+  int rc = check_common(plan, x_raster, x_perm);
+  if (rc) return rc;
+  if (which != FVA_POOL_Q && which != FVA_POOL_K) return fva_fail(FVA_EINVAL, "unknown pooled tensor %d", which);
+  const fva_plan_desc& d = plan->desc;
+  const fva_plan_info& in = plan->info;
+  const bool sub = which == FVA_POOL_K && in.n_sub != 0;
+  double* bar = which == FVA_POOL_Q ? plan->qbar : plan->kbar;
+  dim3 grid(in.n_blk, d.batch * d.heads);
+#define FVA_PP(T, DD, S)                                                                                        \
+  hipLaunchKernelGGL((k_permute_pool<T, DD, S>), grid, dim3(kThreads), 0, stream, (const uint4*)x_raster,        \
+                     (uint4*)x_perm, plan->perm, in.n_tokens, d.heads, in.n_pad, (int)in.n_blk, plan->blk_cnt,  \
+                     plan->sub_pos, plan->sub_cnt, bar)
+  if (d.dtype == FVA_DTYPE_BF16) {
+    if (d.head_dim == 128) { if (sub) FVA_PP(uint16_t, 128, true); else FVA_PP(uint16_t, 128, false); }
+    else { if (sub) FVA_PP(uint16_t, 64, true); else FVA_PP(uint16_t, 64, false); }
+  } else {
+    if (d.head_dim == 128) { if (sub) FVA_PP(float, 128, true); else FVA_PP(float, 128, false); }
+    else { if (sub) FVA_PP(float, 64, true); else FVA_PP(float, 64, false); }
+  }
+#undef FVA_PP
+  plan->pooled |= 1 << which;
+  return fva_after_launch(stream, "fva_permute_pool");
 }
 
 extern "C" int fva_unpermute(fva_plan_t plan, const void* x_perm, void* x_raster, hipStream_t stream) {

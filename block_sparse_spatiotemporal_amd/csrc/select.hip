@@ -718,12 +718,11 @@ void launch_score(fva_plan_t plan, hipStream_t s) {
                        plan->ybuf, plan->rowstat, in.n_blk, scale);
 }
 
-}  // namespace
-
-extern "C" int fva_select(fva_plan_t plan, const void* q_perm, const void* k_perm, const float* p,
-                          int32_t p_count, int32_t k_min, int32_t slack_mode, const float* scores_in,
-                          float* scores_out, int32_t* row_ptr, int32_t* col_idx, int32_t* head_nnz,
-                          hipStream_t stream) {
+// fva_select's body.  pooled: the means come from fva_permute_pool calls
+// (already in qbar / kbar), so q_perm / k_perm are not read.
+int select_impl(fva_plan_t plan, const void* q_perm, const void* k_perm, bool pooled, const float* p,
+                int32_t p_count, int32_t k_min, int32_t slack_mode, const float* scores_in, float* scores_out,
+                int32_t* row_ptr, int32_t* col_idx, int32_t* head_nnz, hipStream_t stream) {
   if (!plan) return fva_fail(FVA_EINVAL, "plan is NULL");
   const fva_plan_desc& d = plan->desc;
   const fva_plan_info& in = plan->info;
@@ -744,9 +743,12 @@ extern "C" int fva_select(fva_plan_t plan, const void* q_perm, const void* k_per
   if (slack_mode == FVA_SLACK_MEDIAN && n_bh > FVA_MAX_PHEAD)
     return fva_fail(FVA_EUNSUPPORTED, "slack fill supports at most %d heads", FVA_MAX_PHEAD);
   if (!row_ptr || !col_idx) return fva_fail(FVA_EINVAL, "row_ptr / col_idx is NULL");
-  if (!scores_in && (!q_perm || !k_perm)) return fva_fail(FVA_EINVAL, "q_perm / k_perm is NULL");
+  if (!scores_in && !pooled && (!q_perm || !k_perm)) return fva_fail(FVA_EINVAL, "q_perm / k_perm is NULL");
+  if (pooled && (plan->pooled & 3) != 3)
+    return fva_fail(FVA_EINVAL, "fva_permute_pool has not produced the pooled means of both Q and K");
 
-  if (!scores_in) {
+  if (!scores_in && !pooled) {
+    plan->pooled = 0;   // qbar / kbar now hold the means of q_perm / k_perm
     if (d.dtype == FVA_DTYPE_BF16) {
       if (d.head_dim == 128) launch_pool<uint16_t, 128>(plan, q_perm, k_perm, stream);
       else launch_pool<uint16_t, 64>(plan, q_perm, k_perm, stream);
@@ -754,6 +756,8 @@ extern "C" int fva_select(fva_plan_t plan, const void* q_perm, const void* k_per
       if (d.head_dim == 128) launch_pool<float, 128>(plan, q_perm, k_perm, stream);
       else launch_pool<float, 64>(plan, q_perm, k_perm, stream);
     }
+  }
+  if (!scores_in) {
     if (d.head_dim == 128) launch_score<128>(plan, stream);
     else launch_score<64>(plan, stream);
   }
@@ -769,6 +773,8 @@ extern "C" int fva_select(fva_plan_t plan, const void* q_perm, const void* k_per
                      plan->rowmask, plan->nw)
   if (ni <= 4) FVA_SELECT(4);
   else if (ni <= 8) FVA_SELECT(8);
+  else if (ni <= 10) FVA_SELECT(10);
+  else if (ni <= 12) FVA_SELECT(12);
   else if (ni <= 16) FVA_SELECT(16);
   else if (ni <= 24) FVA_SELECT(24);
   else if (ni <= 32) FVA_SELECT(32);
@@ -793,7 +799,24 @@ extern "C" int fva_select(fva_plan_t plan, const void* q_perm, const void* k_per
                      row_ptr, in.n_rows);
   hipLaunchKernelGGL(k_emit, dim3(sel_grid), dim3(256), 0, stream, plan->rowmask, row_ptr, plan->headoff, col_idx,
                      plan->nw, in.n_blk, in.n_rows);
-  return fva_after_launch(stream, "fva_select");
+  return fva_after_launch(stream, pooled ? "fva_select_pooled" : "fva_select");
+}
+
+}  // namespace
+
+extern "C" int fva_select(fva_plan_t plan, const void* q_perm, const void* k_perm, const float* p,
+                          int32_t p_count, int32_t k_min, int32_t slack_mode, const float* scores_in,
+                          float* scores_out, int32_t* row_ptr, int32_t* col_idx, int32_t* head_nnz,
+                          hipStream_t stream) {
+  return select_impl(plan, q_perm, k_perm, false, p, p_count, k_min, slack_mode, scores_in, scores_out, row_ptr,
+                     col_idx, head_nnz, stream);
+}
+
+extern "C" int fva_select_pooled(fva_plan_t plan, const float* p, int32_t p_count, int32_t k_min,
+                                 int32_t slack_mode, float* scores_out, int32_t* row_ptr, int32_t* col_idx,
+                                 int32_t* head_nnz, hipStream_t stream) {
+  return select_impl(plan, nullptr, nullptr, true, p, p_count, k_min, slack_mode, nullptr, scores_out, row_ptr,
+                     col_idx, head_nnz, stream);
 }
 
 // ------------------------------------------------------------------ reuse

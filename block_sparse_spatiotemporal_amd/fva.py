@@ -22,6 +22,7 @@ FVA_OK, FVA_EINVAL, FVA_EUNSUPPORTED, FVA_EHIP, FVA_ENOMEM = range(5)
 ORDER = {"tile": 0, "hilbert": 1}
 DTYPE = {"bf16": 0, "f32": 1}
 LAYOUT_ROWS, LAYOUT_VT = 0, 1
+FVA_POOL_Q, FVA_POOL_K = 0, 1
 SLACK = {"none": 0, "median": 1}
 SCHED = {"persistent": 0, "plain": 1}
 
@@ -64,9 +65,13 @@ def lib() -> ctypes.CDLL:
             "fva_plan_destroy": (None, [c_vp]),
             "fva_permute": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_vp]),
             "fva_permute_rope": (c_i32, [c_vp, c_vp, c_vp, c_i32, ctypes.c_double, c_vp]),
+            "fva_permute_pool": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_vp]),
+            "fva_select_pooled": (c_i32, [c_vp, P(ctypes.c_float), c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp,
+                                          c_vp]),
             "fva_select": (c_i32, [c_vp, c_vp, c_vp, P(ctypes.c_float), c_i32, c_i32, c_i32, c_vp, c_vp,
                                    c_vp, c_vp, c_vp, c_vp]),
             "fva_attention": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp]),
+            "fva_attention_raster": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp]),
             "fva_unpermute": (c_i32, [c_vp, c_vp, c_vp, c_vp]),
             "fva_mask_overlap": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
             "fva_mask_accumulate": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp]),
@@ -244,6 +249,32 @@ def fva_unpermute(plan: Plan, x_perm, x_raster, stream=None):
     _check(lib().fva_unpermute(plan.handle, _ptr(x_perm), _ptr(x_raster), _stream(stream)))
 
 
+def fva_permute_pool(plan: Plan, x_raster, x_perm, which, stream=None):
+    """fva_permute (rows) of Q (which="q") or K (which="k") that also leaves
+    the pooled means in the plan's workspace for fva_select_pooled."""
+    _expect(x_raster, plan.raster_shape(), plan.torch_dtype, "x_raster")
+    _expect(x_perm, plan.perm_shape(), plan.torch_dtype, "x_perm")
+    w = {"q": FVA_POOL_Q, "k": FVA_POOL_K}[which] if isinstance(which, str) else int(which)
+    _check(lib().fva_permute_pool(plan.handle, _ptr(x_raster), _ptr(x_perm), w, _stream(stream)))
+
+
+def fva_select_pooled(plan: Plan, p, k_min, row_ptr, col_idx, slack="none", scores_out=None, head_nnz=None,
+                      stream=None):
+    d = plan.desc
+    if scores_out is not None:
+        _expect(scores_out, (d.batch, d.heads, plan.n_blk, plan.n_blk), torch.float32, "scores_out")
+    _expect(row_ptr, (plan.n_rows + 1,), torch.int32, "row_ptr")
+    if col_idx.dtype != torch.int32 or col_idx.numel() < plan.info.max_nnz:
+        raise ValueError("col_idx must be int32 with capacity max_nnz")
+    if head_nnz is not None:
+        _expect(head_nnz, (d.batch * d.heads,), torch.int32, "head_nnz")
+    pl = [float(x) for x in (p if hasattr(p, "__len__") else [p])]
+    parr = (ctypes.c_float * len(pl))(*pl)
+    _check(lib().fva_select_pooled(plan.handle, parr, len(pl), int(k_min),
+                                   SLACK[slack] if isinstance(slack, str) else int(slack), _ptr(scores_out),
+                                   _ptr(row_ptr), _ptr(col_idx), _ptr(head_nnz), _stream(stream)))
+
+
 def fva_select(plan: Plan, q_perm, k_perm, p, k_min, row_ptr, col_idx, slack="none", scores_in=None,
                scores_out=None, head_nnz=None, stream=None):
     d = plan.desc
@@ -282,6 +313,21 @@ def fva_attention(plan: Plan, q_perm, k_perm, vt_perm, row_ptr, col_idx, o_perm,
     _check(lib().fva_attention(plan.handle, _ptr(q_perm), _ptr(k_perm), _ptr(vt_perm), _ptr(row_ptr),
                                _ptr(col_idx), _ptr(o_perm), SCHED[sched] if isinstance(sched, str) else int(sched),
                                _ptr(wg_times), _stream(stream)))
+
+
+def fva_attention_raster(plan: Plan, q_perm, k_perm, vt_perm, row_ptr, col_idx, o_raster, sched="persistent",
+                         stream=None):
+    for t, n in ((q_perm, "q_perm"), (k_perm, "k_perm")):
+        _expect(t, plan.perm_shape(), plan.torch_dtype, n)
+    if vt_perm.numel() != q_perm.numel() or vt_perm.dtype != plan.torch_dtype:
+        raise ValueError("vt_perm has the wrong size or dtype")
+    _expect(o_raster, plan.raster_shape(), plan.torch_dtype, "o_raster")
+    _expect(row_ptr, (plan.n_rows + 1,), torch.int32, "row_ptr")
+    if col_idx.dtype != torch.int32:
+        raise ValueError("col_idx must be int32")
+    _check(lib().fva_attention_raster(plan.handle, _ptr(q_perm), _ptr(k_perm), _ptr(vt_perm), _ptr(row_ptr),
+                                      _ptr(col_idx), _ptr(o_raster),
+                                      SCHED[sched] if isinstance(sched, str) else int(sched), _stream(stream)))
 
 
 def fva_attention_lse(plan: Plan, q_perm, k_perm, vt_perm, row_ptr, col_idx, o_perm, o32, lse, stream=None):
@@ -341,14 +387,31 @@ class Buffers:
 
 
 def attention_call(plan: Plan, q, k, v, out, p, k_min, bufs: Buffers, slack="none", sched="persistent",
-                   scores_out=None, wg_times=None, stream=None):
+                   scores_out=None, wg_times=None, fused=False, stream=None):
     """One full attention call, raster in and raster out:
-    permute(Q, K, V) -> select -> attention -> unpermute."""
-    fva_permute(plan, q, bufs.q, LAYOUT_ROWS, stream)
-    fva_permute(plan, k, bufs.k, LAYOUT_ROWS, stream)
+    permute(Q, K, V) -> select -> attention -> unpermute.  With fused=True
+    the permutes of Q and K also pool (fva_permute_pool, fva_select_pooled)
+    and the attention writes raster rows itself (fva_attention_raster; bufs.o
+    is then not written, and wg_times is not available)."""
+    if fused:
+        fva_permute_pool(plan, q, bufs.q, "q", stream)
+        fva_permute_pool(plan, k, bufs.k, "k", stream)
+    else:
+        fva_permute(plan, q, bufs.q, LAYOUT_ROWS, stream)
+        fva_permute(plan, k, bufs.k, LAYOUT_ROWS, stream)
     fva_permute(plan, v, bufs.vt, LAYOUT_VT, stream)
-    fva_select(plan, bufs.q, bufs.k, p, k_min, bufs.row_ptr, bufs.col_idx, slack=slack, scores_out=scores_out,
-               head_nnz=bufs.head_nnz, stream=stream)
+    if fused:
+        fva_select_pooled(plan, p, k_min, bufs.row_ptr, bufs.col_idx, slack=slack, scores_out=scores_out,
+                          head_nnz=bufs.head_nnz, stream=stream)
+    else:
+        fva_select(plan, bufs.q, bufs.k, p, k_min, bufs.row_ptr, bufs.col_idx, slack=slack,
+                   scores_out=scores_out, head_nnz=bufs.head_nnz, stream=stream)
+    if fused:
+        if wg_times is not None:
+            raise ValueError("wg_times needs the unfused call")
+        fva_attention_raster(plan, bufs.q, bufs.k, bufs.vt, bufs.row_ptr, bufs.col_idx, out, sched=sched,
+                             stream=stream)
+        return
     fva_attention(plan, bufs.q, bufs.k, bufs.vt, bufs.row_ptr, bufs.col_idx, bufs.o, sched=sched,
                   wg_times=wg_times, stream=stream)
     fva_unpermute(plan, bufs.o, out, stream)

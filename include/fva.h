@@ -22,6 +22,9 @@
  *   fva_select(...)      -> CSR block lists (row_ptr, col_idx)
  *   fva_attention(...)   -> O in block order
  *   fva_unpermute(O)     -> O in raster order
+ * (fva_attention_raster does the last two steps in one pass;
+ *  fva_permute_pool for Q and K with fva_select_pooled fold the pooling
+ *  into the permutes.)
  *
  * Conventions shared by every call:
  *   - Raster tensors are [B, N, H, D] contiguous, token n = (t*GH + h)*GW + w
@@ -72,6 +75,8 @@ enum {
                             for V                                            */
 };
 enum { FVA_SLACK_NONE = 0, FVA_SLACK_MEDIAN = 1 };
+/* Which tensor fva_permute_pool pools. */
+enum { FVA_POOL_Q = 0, FVA_POOL_K = 1 };
 enum { FVA_SCHED_PERSISTENT = 0, FVA_SCHED_PLAIN = 1 };
 
 typedef struct fva_plan_s* fva_plan_t;
@@ -149,6 +154,20 @@ void fva_plan_destroy(fva_plan_t plan);
 int fva_permute(fva_plan_t plan, const void* x_raster, void* x_perm, int32_t layout,
                 hipStream_t stream);
 
+/* fva_permute (FVA_LAYOUT_ROWS) of Q or K that also computes the pooled means
+ * the coarse stage scores ("Video Sparse Attention" section 3: the mean of
+ * each (4,4,4) cube; "DFSAttn" trick 2: for K on a plan with sub-blocks, the
+ * mean of each non-empty (2,2,2) sub-block instead), while the rows are at
+ * hand, so fva_select_pooled need not read the block-order tensor again.
+ *   which    FVA_POOL_Q or FVA_POOL_K.
+ * x_perm receives exactly what fva_permute writes.  The means go to the
+ * plan's workspace (fp64), where fva_select_pooled reads them; they are the
+ * same bits fva_select's own pooling produces.  A later fva_select that pools
+ * its own inputs overwrites them (fva_select_pooled then refuses until both
+ * Q and K are pooled again). */
+int fva_permute_pool(fva_plan_t plan, const void* x_raster, void* x_perm, int32_t which,
+                     hipStream_t stream);
+
 /* fva_permute (FVA_LAYOUT_ROWS) fused with a 3D rotary position encoding
  * that uses a global time index ("Accelerating Video Generation Inference
  * with Sequential-Parallel 3D Positional Encoding Using a Global Time Index",
@@ -203,6 +222,16 @@ int fva_select(fva_plan_t plan, const void* q_perm, const void* k_perm, const fl
                float* scores_out, int32_t* row_ptr, int32_t* col_idx, int32_t* head_nnz,
                hipStream_t stream);
 
+/* fva_select on the pooled means of the latest fva_permute_pool calls for Q
+ * and K on this plan (same stream, or ordered before this call): pool is
+ * skipped, score and select run as in fva_select, with the same results.
+ * Arguments as for fva_select without q_perm, k_perm and scores_in.
+ * FVA_EINVAL when Q or K has not been pooled since the plan was created or
+ * since the last fva_select that pooled its own inputs. */
+int fva_select_pooled(fva_plan_t plan, const float* p, int32_t p_count, int32_t k_min,
+                      int32_t slack_mode, float* scores_out, int32_t* row_ptr, int32_t* col_idx,
+                      int32_t* head_nnz, hipStream_t stream);
+
 /* Fine stage ("Video Sparse Attention" section 3; load balancing of uneven
  * per-head work from "FVAttn" section 02, here across the compute units of
  * one GPU).  For every valid query token i of block I:
@@ -226,6 +255,18 @@ int fva_select(fva_plan_t plan, const void* q_perm, const void* k_perm, const fl
 int fva_attention(fva_plan_t plan, const void* q_perm, const void* k_perm, const void* vt_perm,
                   const int32_t* row_ptr, const int32_t* col_idx, void* o_perm,
                   int32_t sched_mode, uint64_t* wg_times, hipStream_t stream);
+
+/* fva_attention followed by fva_unpermute in one pass: each output row is
+ * written straight to its raster position, so the block-order O is never
+ * stored and read back ("Video Sparse Attention" section 3: the gather to
+ * blocks is undone after the fine stage).
+ *   o_raster   [B, N, H, D], plan dtype.  Only valid tokens' rows are
+ *              written; rows of other tokens are left as they are.
+ * The other arguments are those of fva_attention (no wg_times).  The result
+ * equals fva_attention + fva_unpermute bit for bit. */
+int fva_attention_raster(fva_plan_t plan, const void* q_perm, const void* k_perm, const void* vt_perm,
+                         const int32_t* row_ptr, const int32_t* col_idx, void* o_raster,
+                         int32_t sched_mode, hipStream_t stream);
 
 /* Forward pass of a training step: fva_attention that also keeps what the
  * backward pass needs.

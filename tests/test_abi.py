@@ -96,6 +96,9 @@ def test_null_arguments_rejected_before_any_device_work():
     assert L.fva_permute(None, None, None, 0, None) == fva.FVA_EINVAL
     assert L.fva_unpermute(None, None, None, None) == fva.FVA_EINVAL
     assert L.fva_attention(None, None, None, None, None, None, None, 0, None, None) == fva.FVA_EINVAL
+    assert L.fva_attention_raster(None, None, None, None, None, None, None, 0, None) == fva.FVA_EINVAL
+    assert L.fva_permute_pool(None, None, None, 0, None) == fva.FVA_EINVAL
     p = (ctypes.c_float * 1)(0.9)
+    assert L.fva_select_pooled(None, p, 1, 0, 0, None, None, None, None, None) == fva.FVA_EINVAL
     assert L.fva_select(None, None, None, p, 1, 0, 0, None, None, None, None, None, None) == fva.FVA_EINVAL
     L.fva_plan_destroy(None)   # accepted

@@ -260,3 +260,72 @@ def test_launch_shapes_bitwise_equal(monkeypatch):
             ref = out
         else:
             assert torch.equal(out, ref), (group, stages, chunk, sched, order, pair)
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: f"{w.name}-{w.grid}-D{w.D}")
+@pytest.mark.parametrize("sched", ["persistent", "plain"])
+def test_attention_raster_equals_attention_unpermute(w, sched):
+    """fva_attention_raster writes each row straight to its raster position:
+    bit for bit fva_attention + fva_unpermute, and within tolerance of the
+    oracle on the same lists."""
+    plan, opl, (q, k, v), (q64, k64, v64), meta = _plan_and_inputs(w)
+    p = meta["p_head"][0] if not isinstance(w.p, tuple) else meta["p_head"].tolist()
+    b = fva.Buffers(plan)
+    ref = torch.empty_like(q)
+    fva.attention_call(plan, q, k, v, ref, p, w.k_min, b, sched=sched)
+    got = torch.full_like(q, float("nan"))
+    fva.fva_attention_raster(plan, b.q, b.k, b.vt, b.row_ptr, b.col_idx, got, sched=sched)
+    got2 = torch.full_like(q, float("nan"))
+    fva.attention_call(plan, q, k, v, got2, p, w.k_min, fva.Buffers(plan), sched=sched, fused=True)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref) and torch.equal(got2, ref)
+    rp = b.row_ptr.cpu().numpy().astype(np.int64)
+    ci = b.col_idx[: rp[-1]].cpu().numpy().astype(np.int64)
+    o64 = O.unpermute(O.attention(O.permute(q64, opl), O.permute(k64, opl), O.permute(v64, opl), rp, ci, opl), opl)
+    assert np.max(np.abs(to_f64(got) - o64)) < (2e-2 if w.dtype == "bf16" else 1e-4)
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: f"{w.name}-{w.grid}-D{w.D}")
+def test_permute_pool_and_select_pooled_equal_separate_path(w):
+    """fva_permute_pool writes what fva_permute writes, and fva_select_pooled
+    gives the lists (and fp32 scores) fva_select gives on the same tensors:
+    the fused means are the same bits."""
+    plan, opl, (q, k, v), _, meta = _plan_and_inputs(w)
+    p = meta["p_head"][0] if not isinstance(w.p, tuple) else meta["p_head"].tolist()
+    d = plan.desc
+    sq = (d.batch, d.heads, plan.n_blk, plan.n_blk)
+    a, b = fva.Buffers(plan), fva.Buffers(plan)
+    s_a = torch.empty(sq, dtype=torch.float32, device="cuda")
+    s_b = torch.empty(sq, dtype=torch.float32, device="cuda")
+    fva.fva_permute(plan, q, a.q)
+    fva.fva_permute(plan, k, a.k)
+    fva.fva_select(plan, a.q, a.k, p, w.k_min, a.row_ptr, a.col_idx, slack=w.slack, scores_out=s_a)
+    b.q.fill_(float("nan"))
+    fva.fva_permute_pool(plan, q, b.q, "q")
+    fva.fva_permute_pool(plan, k, b.k, "k")
+    fva.fva_select_pooled(plan, p, w.k_min, b.row_ptr, b.col_idx, slack=w.slack, scores_out=s_b)
+    torch.cuda.synchronize()
+    assert torch.equal(a.q, b.q) and torch.equal(a.k, b.k)
+    assert torch.equal(s_a, s_b)
+    assert torch.equal(a.row_ptr, b.row_ptr)
+    n = int(a.row_ptr[-1].item())
+    assert torch.equal(a.col_idx[:n], b.col_idx[:n])
+
+
+def test_select_pooled_needs_both_pools():
+    w = synth.scaled(synth.WORKLOADS["wan1.3b_480p"], H=2, grid=(9, 10, 13))
+    plan, _, (q, k, v), _, _ = _plan_and_inputs(w)
+    b = fva.Buffers(plan)
+    with pytest.raises(fva.FvaError) as e:
+        fva.fva_select_pooled(plan, 0.9, 16, b.row_ptr, b.col_idx)
+    assert e.value.code == fva.FVA_EINVAL
+    fva.fva_permute_pool(plan, q, b.q, "q")
+    with pytest.raises(fva.FvaError):
+        fva.fva_select_pooled(plan, 0.9, 16, b.row_ptr, b.col_idx)
+    fva.fva_permute_pool(plan, k, b.k, "k")
+    fva.fva_select_pooled(plan, 0.9, 16, b.row_ptr, b.col_idx)
+    # a select that pools its own inputs replaces the means: pooled again needed
+    fva.fva_select(plan, b.q, b.k, 0.9, 16, b.row_ptr, b.col_idx)
+    with pytest.raises(fva.FvaError):
+        fva.fva_select_pooled(plan, 0.9, 16, b.row_ptr, b.col_idx)
+    torch.cuda.synchronize()
