@@ -178,21 +178,29 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, 
   constexpr int KV = 16 * D / 2 / 256;             // double2 per thread per tile
   __shared__ double ks_lds[2][16][KS];
   const double* kh = kbar + (int64_t)bh * nkeys * D;
-  double2 kn[KV];
-  auto kfetch = [&](int kt) {
+  // The tile in flight is a value returned by kfetch and consumed by kstore
+  // in the same iteration, fetched unconditionally (the last iteration
+  // re-reads the last tile into the idle buffer), so it stays in registers:
+  // an array kept across the loop with conditional writes ended up in
+  // scratch memory, and every prefetch then waited for its loads at once.
+  struct KTile { double2 v[KV]; };
+  auto kfetch = [&](int kt) -> KTile {
+    KTile t;
+    kt = min(kt, ntiles - 1);
 #pragma unroll
     for (int v = 0; v < KV; ++v) {
       const int e = threadIdx.x + 256 * v;         // double2 index within the tile
       const int r = e / (D / 2), d2 = e - r * (D / 2);
-      kn[v] = *(const double2*)(kh + (int64_t)min(kt * 16 + r, nkeys - 1) * D + 2 * d2);
+      t.v[v] = *(const double2*)(kh + (int64_t)min(kt * 16 + r, nkeys - 1) * D + 2 * d2);
     }
+    return t;
   };
-  auto kstore = [&](int buf) {
+  auto kstore = [&](int buf, const KTile& t) {
 #pragma unroll
     for (int v = 0; v < KV; ++v) {
       const int e = threadIdx.x + 256 * v;
       const int r = e / (D / 2), d2 = e - r * (D / 2);
-      *(double2*)&ks_lds[buf][r][2 * d2] = kn[v];
+      *(double2*)&ks_lds[buf][r][2 * d2] = t.v[v];
     }
   };
   // non-empty sub-blocks of every block, one byte per block (bit s: sub-block s)
@@ -204,8 +212,7 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, 
       for (int t = 0; t < 8; ++t) mbits |= (sub_cnt[j * 8 + t] > 0 ? 1u : 0u) << t;
       sub_ok[j] = (uint8_t)mbits;
     }
-  kfetch(0);
-  kstore(0);
+  kstore(0, kfetch(0));
   __syncthreads();
   // Logits go out through a per-wave LDS tile of 16 query rows x 64 block
   // columns, written back as whole 512-byte row pieces.
@@ -221,7 +228,7 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, 
   };
   double m_run = -INFINITY, s_run = 0.0;
   for (int kt = 0; kt < ntiles; ++kt) {
-    if (kt + 1 < ntiles) kfetch(kt + 1);
+    const KTile nxt = kfetch(kt + 1);
     const double2* ks = (const double2*)&ks_lds[kt & 1][l16][QD * g];
     f64x4 acc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
@@ -284,7 +291,7 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, 
       }
     }
     if (kt % TPF == TPF - 1 || kt == ntiles - 1) flush(kt);
-    if (kt + 1 < ntiles) kstore((kt + 1) & 1);
+    kstore((kt + 1) & 1, nxt);
     __syncthreads();
   }
   // merge (max, sum) over the four lane groups that share query l16
