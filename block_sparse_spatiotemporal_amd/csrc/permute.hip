@@ -249,9 +249,15 @@ __global__ __launch_bounds__(kThreads) void k_permute_pool(const uint4* __restri
   static_assert(NCH % kThreads == 0, "whole chunks per thread");
   __shared__ uint4 tile[NCH];
   __shared__ double part[SUB ? 1 : RG][D];
+  __shared__ uint8_t s_pos[SUB ? 64 : 1];   // the block's sub-block member positions
+  __shared__ int s_cnt[SUB ? 8 : 1];
   const int blk = blockIdx.x, bh = blockIdx.y;
   const int b = bh / heads, h = bh - b * heads;
   const int t = threadIdx.x;
+  if (SUB) {
+    if (t < 64) s_pos[t] = sub_pos[(int64_t)blk * 64 + t];
+    if (t < 8) s_cnt[t] = sub_cnt[blk * 8 + t];
+  }
   uint4* out = dst + ((int64_t)bh * n_pad + (int64_t)blk * 64) * CPR;
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
@@ -284,11 +290,11 @@ __global__ __launch_bounds__(kThreads) void k_permute_pool(const uint4* __restri
     double* o = bar + ((int64_t)bh * n_blk + blk) * 8 * D;
     for (int e = t; e < 8 * D; e += kThreads) {
       const int sb = e / D, d = e - sb * D;
-      const uint8_t* pos = sub_pos + ((int64_t)blk * 8 + sb) * 8;
+      const uint8_t* pos = s_pos + sb * 8;
       double acc = 0.0;
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc += (double)ld_val(x + (int)pos[i] * D + d);
-      const int cnt = sub_cnt[blk * 8 + sb];
+      const int cnt = s_cnt[sb];
       o[e] = cnt ? acc / (double)cnt : 0.0;
     }
   }
