@@ -60,6 +60,40 @@ __device__ __forceinline__ T wave_incl_scan(T v, int lane) {
   return v;
 }
 
+// The values of lanes l and l^16 (X = 16) or l and l^32 (X = 32) of an fp64
+// x, in some order, without an LDS round trip: v_permlane16/32_swap of each
+// 32-bit half with itself.  Max and sum of the pair are then exact and
+// symmetric, the same bits as combining x with __shfl_xor(x, X).
+template <int X>
+__device__ __forceinline__ void lane_pair(double x, double& a, double& b) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = (uint32_t)u, hi = (uint32_t)(u >> 32);
+  uint32_t l0, l1, h0, h1;
+  if constexpr (X == 16) {
+    const auto rl = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto rh = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    l0 = rl[0], l1 = rl[1], h0 = rh[0], h1 = rh[1];
+  } else {
+    const auto rl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const auto rh = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    l0 = rl[0], l1 = rl[1], h0 = rh[0], h1 = rh[1];
+  }
+  a = __builtin_bit_cast(double, ((uint64_t)h0 << 32) | l0);
+  b = __builtin_bit_cast(double, ((uint64_t)h1 << 32) | l1);
+}
+template <int X>
+__device__ __forceinline__ double pair_max(double x) {
+  double a, b;
+  lane_pair<X>(x, a, b);
+  return fmax(a, b);
+}
+template <int X>
+__device__ __forceinline__ double pair_sum(double x) {
+  double a, b;
+  lane_pair<X>(x, a, b);
+  return a + b;
+}
+
 __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -260,7 +294,7 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, 
     } else {
       // sub-key m = g + 4*i of the tile is sub-block m%8 of block kt*2 + m/8:
       // acc[2*b2] and acc[2*b2+1] are sub-blocks g and g+4 of block kt*2+b2.
-      double yb[2];
+      double cb[2], eb[2];
 #pragma unroll
       for (int b2 = 0; b2 < 2; ++b2) {
         const int blk = kt * 2 + b2;
@@ -268,27 +302,24 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, 
         const double v0 = (ok >> g & 1) ? acc[2 * b2] * scale : -INFINITY;
         const double v1 = (ok >> (g + 4) & 1) ? acc[2 * b2 + 1] * scale : -INFINITY;
         // log-sum-exp over the block's 8 sub-blocks (2 per lane, 4 lane groups):
-        // the max first, then one exponential per sub-block and one log
+        // the max first, then one exponential per sub-block
         double c = fmax(v0, v1);
-        c = fmax(c, __shfl_xor(c, 16));
-        c = fmax(c, __shfl_xor(c, 32));
+        c = pair_max<32>(pair_max<16>(c));
         double e = c > -INFINITY ? exp(v0 - c) + exp(v1 - c) : 0.0;
-        e += __shfl_xor(e, 16);
-        e += __shfl_xor(e, 32);
-        yb[b2] = c > -INFINITY ? c + log(e) : -INFINITY;
+        e = pair_sum<32>(pair_sum<16>(e));
+        cb[b2] = c, eb[b2] = e;
       }
-      // every lane group now holds both block logits; for the row statistics
-      // group 0 counts block kt*2 and group 1 block kt*2+1 (merged at the end)
-      const double yo = g == 0 ? yb[0] : (g == 1 ? yb[1] : -INFINITY);
+      // every lane group now holds both blocks' (max, sum); group 0 owns block
+      // kt*2 and group 1 block kt*2+1: one log each, its logit written out and
+      // counted in the row statistics (groups merged at the end)
+      const double cm = g == 1 ? cb[1] : cb[0], em = g == 1 ? eb[1] : eb[0];
+      const double yo = g < 2 && cm > -INFINITY ? cm + log(em) : -INFINITY;
       if (yo > m_run) {
         s_run *= exp(m_run - yo);
         m_run = yo;
       }
       if (yo > -INFINITY) s_run += exp(yo - m_run);
-      if (g == 0) {
-        yt[w][l16][(kt % TPF) * 2] = yb[0];
-        yt[w][l16][(kt % TPF) * 2 + 1] = yb[1];
-      }
+      if (g < 2) yt[w][l16][(kt % TPF) * 2 + g] = yo;
     }
     if (kt % TPF == TPF - 1 || kt == ntiles - 1) flush(kt);
     kstore((kt + 1) & 1, nxt);

@@ -1,4 +1,5 @@
-"""Full-size workloads, in the launch configuration bench.py times (persistent
+"""Full-size workloads, in the launch configuration bench.py times (the fused
+calls fva_permute_pool, fva_select_pooled and fva_attention_raster, persistent
 schedule, default group and ring depth), checked against the oracle on what
 the oracle can compute in a test's time:
 
@@ -37,7 +38,7 @@ def _run(name):
     S = torch.empty(w.B, w.H, plan.n_blk, plan.n_blk, dtype=torch.float32, device="cuda")
     p_head = meta["p_head"]
     p = p_head.tolist() if isinstance(w.p, tuple) else float(p_head[0])
-    fva.attention_call(plan, qd, kd, vd, out, p, w.k_min, bufs, slack=w.slack, scores_out=S)
+    fva.attention_call(plan, qd, kd, vd, out, p, w.k_min, bufs, slack=w.slack, scores_out=S, fused=True)
     torch.cuda.synchronize()
     rp = bufs.row_ptr.cpu().numpy().astype(np.int64)
     ci = bufs.col_idx[: rp[-1]].cpu().numpy().astype(np.int64)
