@@ -369,6 +369,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a) {
   __shared__ float k_lds[32][D + 1];
   __shared__ float v_lds[32][D + 1];
   __shared__ int s_item;
+  __shared__ uint32_t s_set[FVA_MAX_NBLK / 32];   // the row's blocks as a set
   const int tid = threadIdx.x;
   const int qi = tid >> 2, part = tid & 3;
   const uint64_t t0 = wall_clock64();
@@ -385,10 +386,19 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a) {
       o[d] = 0.0f;
     }
     float m_run = -INFINITY, l_run = 0.0f;
-    const int e0 = a.row_ptr[r], e1 = a.row_ptr[r + 1];
-    for (int e = e0; e < e1; ++e) {
+    // The row read as a set (an id listed twice counts once, ids outside the
+    // plan are dropped), walked in ascending order.
+    const int nwd = (a.n_blk + 31) >> 5;
+    for (int i = tid; i < nwd; i += 256) s_set[i] = 0;
+    __syncthreads();
+    for (int e = a.row_ptr[r] + tid; e < a.row_ptr[r + 1]; e += 256) {
       const int J = a.col_idx[e];
-      if ((unsigned)J >= (unsigned)a.n_blk) continue;   // ids outside the plan are skipped
+      if ((unsigned)J < (unsigned)a.n_blk) atomicOr(&s_set[J >> 5], 1u << (J & 31));
+    }
+    __syncthreads();
+    for (int wd = 0; wd < nwd; ++wd)
+    for (uint32_t set = s_set[wd]; set; set &= set - 1) {
+      const int J = 32 * wd + __builtin_ctz(set);
       const uint64_t mJ = a.blk_mask[J];
       for (int u = 0; u < 2; ++u) {
         const uint32_t mh = (uint32_t)(mJ >> (32 * u));
