@@ -319,6 +319,9 @@ def test_select_pooled_needs_both_pools():
     with pytest.raises(fva.FvaError) as e:
         fva.fva_select_pooled(plan, 0.9, 16, b.row_ptr, b.col_idx)
     assert e.value.code == fva.FVA_EINVAL
+    with pytest.raises(fva.FvaError) as e:   # neither Q nor K
+        fva.fva_permute_pool(plan, q, b.q, 7)
+    assert e.value.code == fva.FVA_EINVAL
     fva.fva_permute_pool(plan, q, b.q, "q")
     with pytest.raises(fva.FvaError):
         fva.fva_select_pooled(plan, 0.9, 16, b.row_ptr, b.col_idx)
