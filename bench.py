@@ -190,6 +190,28 @@ def main():
     st_mean = {n: float(x.mean()) for n, x in stage.items()}
     st_med = {n: float(np.median(x)) for n, x in stage.items()}
 
+    # the same call captured once in a HIP graph and replayed (fused form only)
+    graph_ms = None
+    if not args.unfused:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            call()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            call()
+        torch.cuda.synchronize()
+        e_g0, e_g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e_g0.record()
+        for _ in range(args.steps):
+            graph.replay()
+        e_g1.record()
+        torch.cuda.synchronize()
+        graph_ms = e_g0.elapsed_time(e_g1) / args.steps
+        del graph
+
     # the fused permute + 3D rotary encoding (outside the attention call),
     # timed alone on Q of the same workload
     e_r0, e_r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -310,6 +332,7 @@ def main():
         "stage_ms_mean": {n: round(x, 4) for n, x in st_mean.items()},
         "stage_ms_median": {n: round(x, 4) for n, x in st_med.items()},
         "core_ms": round(st_mean["select"] + st_mean["attention"], 4),
+        "graph_ms_per_call": round(graph_ms, 4) if graph_ms is not None else None,
         "hbm_gbs": {"permute_rows": round(perm_bytes / (st_mean["permute_q"] * 1e-3) / 1e9, 1),
                     "permute_vt": round(perm_bytes / (st_mean["permute_v"] * 1e-3) / 1e9, 1),
                     "select": round(sel_bytes / (st_mean["select"] * 1e-3) / 1e9, 1),

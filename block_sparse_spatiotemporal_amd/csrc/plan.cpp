@@ -46,6 +46,10 @@ int fva_after_launch(hipStream_t s, const char* what) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fva_fail(FVA_EHIP, "%s launch: %s", what, hipGetErrorString(e));
   if (fva_debug_enabled()) {
+    // a stream being captured into a graph cannot be synchronised; its
+    // launches are checked when the graph runs
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone) return FVA_OK;
     e = hipStreamSynchronize(s);
     if (e != hipSuccess) return fva_fail(FVA_EHIP, "%s: %s", what, hipGetErrorString(e));
   }

@@ -38,7 +38,14 @@
  *     Arguments are validated before anything is enqueued: on a non-zero
  *     status nothing was written.  A kernel fault surfaces at the caller's
  *     next synchronisation; with FVA_DEBUG=1 in the environment every call
- *     synchronises and checks after its launches.
+ *     synchronises and checks after its launches (not while its stream is
+ *     being captured into a graph).
+ *   - Graph capture: the per-call entry points (everything except plan
+ *     creation and destruction) only launch kernels on `stream`: no
+ *     allocation, no memset or copy node, no host synchronisation, so a
+ *     sequence of calls can be captured once and replayed.  Host-side
+ *     arguments (p, k_min, modes) are fixed at capture; tensor contents
+ *     are read at each replay.
  *   - A plan is not safe for concurrent calls on different streams: its
  *     workspace is shared.  No C++ exception crosses this interface.
  */

@@ -4,8 +4,8 @@ import sys
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-# every library call synchronises and checks its launches (and the attention
-# kernel's pipeline fault flag) while the tests run
+# every library call synchronises and checks its launches while the tests run
+# (except inside a graph capture, where the library skips the synchronisation)
 os.environ.setdefault("FVA_DEBUG", "1")
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
