@@ -192,19 +192,24 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
       un_hi |= s_bits[128 * g + 2 * lane + 1];
     }
     // Two identical walks over the union: one issues loads NST-1 steps
-    // ahead, the other follows the computation.
+    // ahead, the other follows the computation.  The step count (two
+    // halves per union block) is known up front, so neither walk tests
+    // for its end and the waits need no bookkeeping of what is in flight.
     BitWalk iw, cw;
+    int total;
+    {
+      int c = __popc(un_lo) + __popc(un_hi);
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o);
+      total = 2 * __builtin_amdgcn_readfirstlane(c);
+    }
     const char* kbase = (const char*)(a.k + head * D);
     const char* vbase = (const char*)(a.vt + head * D);
     int issued = 0;       // steps whose loads are issued
     int curJ = 0;
-    bool more = true;
     // Issue the direct loads of the next step (block curJ, half issued%2).
-    auto issue_next = [&]() __attribute__((always_inline)) -> bool {
-      if ((issued & 1) == 0) {
-        more = iw.next(un_lo, un_hi, nw, &curJ);
-        if (!more) return false;
-      }
+    auto issue_next = [&]() __attribute__((always_inline)) {
+      if ((issued & 1) == 0) curJ = iw.next_known(un_lo, un_hi);
       const int u = issued & 1;
       const int J = curJ;
       const char* ksrc = kbase + ((int64_t)J * 64 + 32 * u) * D * 2;
@@ -217,7 +222,6 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
         dma16(vsrc, voff[j], dst + HALF + i * 1024);
       }
       ++issued;
-      return true;
     };
 
     const bool has_row = Iq >= 0;
@@ -239,32 +243,32 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
 
 #pragma unroll
     for (int st = 0; st < NST - 1; ++st)
-      if (more) issue_next();
+      if (st < total) issue_next();
 
     int J = 0;
     bool mine = false, full = false;
     // Unrolled by the ring depth so each copy of the step reads a fixed
     // stage: the stage offset then folds into the LDS reads' immediate
     // offsets instead of costing address arithmetic every step.
-    for (int st0 = 0; st0 < issued; st0 += NST) {
+    for (int st0 = 0; st0 < total; st0 += NST) {
 #pragma unroll
     for (int kk = 0; kk < NST; ++kk) {
       const int st = st0 + kk;
-      if (st >= issued) break;
+      if (st >= total) break;
       const int u = NST % 2 == 0 ? (kk & 1) : (st & 1);   // half of the block
       if (u == 0) {
-        cw.next(un_lo, un_hi, nw, &J);
+        J = cw.next_known(un_lo, un_hi);
         mine = lane_word(own_lo, own_hi, J >> 6) >> (J & 63) & 1;
         full = lane_word(full_lo, full_hi, J >> 6) >> (J & 63) & 1;
       }
-      // wait for this wave's loads of step st; later steps may stay in flight
-      const int ahead = issued - 1 - st;
-      if (ahead >= 3) wait_vm<3 * PW>();
-      else if (ahead == 2) wait_vm<2 * PW>();
-      else if (ahead == 1) wait_vm<PW>();
+      // wait for this wave's loads of step st; the NST-2 steps issued after
+      // it may stay in flight (fewer near the end of the walk)
+      if (st + NST - 2 < total) wait_vm<(NST - 2) * PW>();
+      else if (NST >= 4 && st + 2 < total) wait_vm<2 * PW>();
+      else if (NST >= 3 && st + 1 < total) wait_vm<PW>();
       else wait_vm<0>();
       barrier_no_fence();
-      if (more) issue_next();   // into the stage retired by the barrier
+      if (st + NST - 1 < total) issue_next();   // into the stage retired by the barrier
 
       uint32_t mh = 0;
       if (mine) mh = full ? 0xFFFFFFFFu : (uint32_t)(sload(a.blk_mask, J) >> (32 * u));

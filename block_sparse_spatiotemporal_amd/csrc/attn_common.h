@@ -128,6 +128,13 @@ struct BitWalk {
     bits &= bits - 1;
     return true;
   }
+  // The next set bit when the caller knows one is left (no end test).
+  __device__ __forceinline__ int next_known(uint32_t lo, uint32_t hi) {
+    while (bits == 0) bits = lane_word(lo, hi, ++w);
+    const int J = 64 * w + __builtin_ctzll(bits);
+    bits &= bits - 1;
+    return J;
+  }
 };
 
 }  // namespace fva_attn
