@@ -205,23 +205,22 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
     }
     const char* kbase = (const char*)(a.k + head * D);
     const char* vbase = (const char*)(a.vt + head * D);
-    int issued = 0;       // steps whose loads are issued
     int curJ = 0;
-    // Issue the direct loads of the next step (block curJ, half issued%2).
-    auto issue_next = [&]() __attribute__((always_inline)) {
-      if ((issued & 1) == 0) curJ = iw.next_known(un_lo, un_hi);
-      const int u = issued & 1;
+    // Issue the direct loads of the next step into ring stage `stage`: half
+    // u of block curJ (the walk advances on the first half).  Both arguments
+    // are compile-time constants at every call site of the unrolled loop.
+    auto issue_next = [&](int stage, int u) __attribute__((always_inline)) {
+      if (u == 0) curJ = iw.next_known(un_lo, un_hi);
       const int J = curJ;
       const char* ksrc = kbase + ((int64_t)J * 64 + 32 * u) * D * 2;
       const char* vsrc = vbase + (int64_t)J * 64 * D * 2 + u * HALF;
-      const uint32_t dst = lds_addr(ring) + (issued % NST) * STAGE;
+      const uint32_t dst = lds_addr(ring) + stage * STAGE;
 #pragma unroll
       for (int j = 0; j < LPW; ++j) {
         const int i = NW * j + w;
         dma16(ksrc, koff[j], dst + i * 1024);
         dma16(vsrc, voff[j], dst + HALF + i * 1024);
       }
-      ++issued;
     };
 
     const bool has_row = Iq >= 0;
@@ -243,7 +242,7 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
 
 #pragma unroll
     for (int st = 0; st < NST - 1; ++st)
-      if (st < total) issue_next();
+      if (st < total) issue_next(st, st & 1);
 
     int J = 0;
     bool mine = false, full = false;
@@ -268,7 +267,8 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
       else if (NST >= 3 && st + 1 < total) wait_vm<PW>();
       else wait_vm<0>();
       barrier_no_fence();
-      if (st + NST - 1 < total) issue_next();   // into the stage retired by the barrier
+      if (st + NST - 1 < total)   // step st + NST - 1, into the stage retired by the barrier
+        issue_next((kk + NST - 1) % NST, NST % 2 == 0 ? ((kk + NST - 1) & 1) : ((st + NST - 1) & 1));
 
       uint32_t mh = 0;
       if (mine) mh = full ? 0xFFFFFFFFu : (uint32_t)(sload(a.blk_mask, J) >> (32 * u));
