@@ -196,13 +196,7 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
     // halves per union block) is known up front, so neither walk tests
     // for its end and the waits need no bookkeeping of what is in flight.
     BitWalk iw, cw;
-    int total;
-    {
-      int c = __popc(un_lo) + __popc(un_hi);
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o);
-      total = 2 * __builtin_amdgcn_readfirstlane(c);
-    }
+    const int total = union_steps(un_lo, un_hi);
     const char* kbase = (const char*)(a.k + head * D);
     const char* vbase = (const char*)(a.vt + head * D);
     int curJ = 0;

@@ -114,6 +114,15 @@ __device__ __forceinline__ uint64_t lane_word(uint32_t lo, uint32_t hi, int w) {
          (uint32_t)__builtin_amdgcn_readlane((int)lo, w);
 }
 
+// Steps of a walk over such a bitmap: two 32-position halves per set bit,
+// summed over the wave (wave-uniform result).
+__device__ __forceinline__ int union_steps(uint32_t lo, uint32_t hi) {
+  int c = __popc(lo) + __popc(hi);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o);
+  return 2 * __builtin_amdgcn_readfirstlane(c);
+}
+
 // Ascending walk over the set bits of such a bitmap; the state is
 // wave-uniform, so the walk is scalar arithmetic with no memory access.
 struct BitWalk {

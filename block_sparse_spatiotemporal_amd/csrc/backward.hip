@@ -167,11 +167,13 @@ __global__ __launch_bounds__(64) void k_zero_i32(int32_t* __restrict__ p, int n)
 // Wait until at most `ahead` steps of this wave's direct loads (PW each) are
 // still in flight.
 template <int PW, int NST>
-__device__ __forceinline__ void wait_steps(int ahead) {
+__device__ __forceinline__ void wait_steps(int st, int total) {
+  // the loads of step st are this wave's oldest except for those of the
+  // min(NST - 2, total - 1 - st) steps issued after it
   static_assert(NST >= 2 && NST <= 4 && (NST - 1) * PW < 64, "vmcnt range");
-  if (NST >= 4 && ahead >= 3) wait_vm<(NST >= 4 ? 3 * PW : 0)>();
-  else if (NST >= 3 && ahead >= 2) wait_vm<(NST >= 3 ? 2 * PW : 0)>();
-  else if (ahead >= 1) wait_vm<PW>();
+  if (st + NST - 2 < total) wait_vm<(NST - 2) * PW>();
+  else if (NST >= 4 && st + 2 < total) wait_vm<(NST >= 4 ? 2 * PW : 0)>();
+  else if (NST >= 3 && st + 1 < total) wait_vm<PW>();
   else wait_vm<0>();
 }
 
@@ -308,12 +310,9 @@ __global__ __launch_bounds__(128 * G, 2) void k_bwd_dq(BwdArgs a) {
   const char* vbase = (const char*)(a.v + head * D);
   const char* tbase = (const char*)(a.kt + head * D);
   int issued = 0, curJ = 0;
-  bool more = true;
+  const int total = union_steps(un_lo, un_hi);   // two halves per union block
   auto issue_next = [&]() __attribute__((always_inline)) {
-    if ((issued & 1) == 0) {
-      more = iw.next(un_lo, un_hi, a.nw, &curJ);
-      if (!more) return;
-    }
+    if ((issued & 1) == 0) curJ = iw.next_known(un_lo, un_hi);
     const int u = issued & 1;
     const int64_t roff0 = ((int64_t)curJ * 64 + 32 * u) * D * 2;
     const int64_t toff0 = (int64_t)curJ * 64 * D * 2 + u * HALF;
@@ -333,19 +332,19 @@ __global__ __launch_bounds__(128 * G, 2) void k_bwd_dq(BwdArgs a) {
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
 #pragma unroll
   for (int st = 0; st < NST - 1; ++st)
-    if (more) issue_next();
+    if (st < total) issue_next();
 
   int J = 0;
   bool mine = false, full = false;
-  for (int st = 0; st < issued; ++st) {
+  for (int st = 0; st < total; ++st) {
     if ((st & 1) == 0) {
-      cw.next(un_lo, un_hi, a.nw, &J);
+      J = cw.next_known(un_lo, un_hi);
       mine = lane_word(own_lo, own_hi, J >> 6) >> (J & 63) & 1;
       full = lane_word(full_lo, full_hi, J >> 6) >> (J & 63) & 1;
     }
-    wait_steps<PW, NST>(issued - 1 - st);
+    wait_steps<PW, NST>(st, total);
     barrier_no_fence();
-    if (more) issue_next();
+    if (st + NST - 1 < total) issue_next();
 
     const int u = st & 1;
     uint32_t mh = 0;
@@ -456,12 +455,9 @@ __global__ __launch_bounds__(128 * G, G) void k_bwd_dkdv(BwdArgs a) {
   // floats [LDW w, LDW (w+1)) of the stage's [32 lse | 32 delta]
   const float* lbase = (LDW * w < 32 ? a.lse + LDW * w : (const float*)a.delta + (LDW * w - 32)) + head;
   int issued = 0, curI = 0;
-  bool more = true;
+  const int total = union_steps(un_lo, un_hi);   // two halves per union block
   auto issue_next = [&]() __attribute__((always_inline)) {
-    if ((issued & 1) == 0) {
-      more = iw.next(un_lo, un_hi, a.nw, &curI);
-      if (!more) return;
-    }
+    if ((issued & 1) == 0) curI = iw.next_known(un_lo, un_hi);
     const int u = issued & 1;
     const int64_t roff0 = ((int64_t)curI * 64 + 32 * u) * D * 2;
     const int64_t toff0 = (int64_t)curI * 64 * D * 2 + u * HALF;
@@ -483,20 +479,20 @@ __global__ __launch_bounds__(128 * G, G) void k_bwd_dkdv(BwdArgs a) {
   for (int dt = 0; dt < DT; ++dt) dk[dt] = dv[dt] = f32x16{};
 #pragma unroll
   for (int st = 0; st < NST - 1; ++st)
-    if (more) issue_next();
+    if (st < total) issue_next();
 
   int I = 0;
   uint64_t qm64 = 0;
   bool mine = false;
-  for (int st = 0; st < issued; ++st) {
+  for (int st = 0; st < total; ++st) {
     if ((st & 1) == 0) {
-      cw.next(un_lo, un_hi, a.nw, &I);
+      I = cw.next_known(un_lo, un_hi);
       mine = lane_word(own_lo, own_hi, I >> 6) >> (I & 63) & 1;
       qm64 = sload(a.blk_mask, I);
     }
-    wait_steps<PW, NST>(issued - 1 - st);
+    wait_steps<PW, NST>(st, total);
     barrier_no_fence();
-    if (more) issue_next();
+    if (st + NST - 1 < total) issue_next();
 
     const int u = st & 1;
     const uint32_t qm = mine ? (uint32_t)(qm64 >> (32 * u)) : 0u;
@@ -639,12 +635,9 @@ __global__ __launch_bounds__(128 * G, OCC) void k_bwd_dkv(BwdArgs a) {
   // floats [LDW w, LDW (w+1)) of the stage's [32 lse | 32 delta]
   const float* lbase = (LDW * w < 32 ? a.lse + LDW * w : (const float*)a.delta + (LDW * w - 32)) + head;
   int issued = 0, curI = 0;
-  bool more = true;
+  const int total = union_steps(un_lo, un_hi);   // two halves per union block
   auto issue_next = [&]() __attribute__((always_inline)) {
-    if ((issued & 1) == 0) {
-      more = iw.next(un_lo, un_hi, a.nw, &curI);
-      if (!more) return;
-    }
+    if ((issued & 1) == 0) curI = iw.next_known(un_lo, un_hi);
     const int u = issued & 1;
     const int64_t roff0 = ((int64_t)curI * 64 + 32 * u) * D * 2;
     const int64_t toff0 = (int64_t)curI * 64 * D * 2 + u * HALF;
@@ -669,20 +662,20 @@ __global__ __launch_bounds__(128 * G, OCC) void k_bwd_dkv(BwdArgs a) {
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
 #pragma unroll
   for (int st = 0; st < NST - 1; ++st)
-    if (more) issue_next();
+    if (st < total) issue_next();
 
   int I = 0;
   uint64_t qm64 = 0;
   bool mine = false;
-  for (int st = 0; st < issued; ++st) {
+  for (int st = 0; st < total; ++st) {
     if ((st & 1) == 0) {
-      cw.next(un_lo, un_hi, a.nw, &I);
+      I = cw.next_known(un_lo, un_hi);
       mine = lane_word(own_lo, own_hi, I >> 6) >> (I & 63) & 1;
       qm64 = sload(a.blk_mask, I);
     }
-    wait_steps<PW, NST>(issued - 1 - st);
+    wait_steps<PW, NST>(st, total);
     barrier_no_fence();
-    if (more) issue_next();
+    if (st + NST - 1 < total) issue_next();
 
     const int u = st & 1;
     const uint32_t qm = mine ? (uint32_t)(qm64 >> (32 * u)) : 0u;
