@@ -239,7 +239,9 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
       if (st < total) issue_next(st, st & 1);
 
     int J = 0;
-    bool mine = false, full = false;
+    // valid-key mask of the current block for this wave: zero when the
+    // wave's row does not list the block, all ones for a block without pads
+    uint64_t kmask = 0;
     // Unrolled by the ring depth so each copy of the step reads a fixed
     // stage: the stage offset then folds into the LDS reads' immediate
     // offsets instead of costing address arithmetic every step.
@@ -251,8 +253,9 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
       const int u = NST % 2 == 0 ? (kk & 1) : (st & 1);   // half of the block
       if (u == 0) {
         J = cw.next_known(un_lo, un_hi);
-        mine = lane_word(own_lo, own_hi, J >> 6) >> (J & 63) & 1;
-        full = lane_word(full_lo, full_hi, J >> 6) >> (J & 63) & 1;
+        const bool mine = lane_word(own_lo, own_hi, J >> 6) >> (J & 63) & 1;
+        const bool full = lane_word(full_lo, full_hi, J >> 6) >> (J & 63) & 1;
+        kmask = !mine ? 0ull : (full ? ~0ull : sload(a.blk_mask, J));
       }
       // wait for this wave's loads of step st; the NST-2 steps issued after
       // it may stay in flight (fewer near the end of the walk)
@@ -264,8 +267,7 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
       if (st + NST - 1 < total)   // step st + NST - 1, into the stage retired by the barrier
         issue_next((kk + NST - 1) % NST, NST % 2 == 0 ? ((kk + NST - 1) & 1) : ((st + NST - 1) & 1));
 
-      uint32_t mh = 0;
-      if (mine) mh = full ? 0xFFFFFFFFu : (uint32_t)(sload(a.blk_mask, J) >> (32 * u));
+      const uint32_t mh = (uint32_t)(kmask >> (32 * u));
       if (mh == 0) continue;   // not in this row's list, or a half of pad keys (uniform per wave)
       const uint4* kst = ring + kk * (STAGE / 16);
       const uint4* vst = kst + HALF / 16;
