@@ -335,20 +335,22 @@ __global__ __launch_bounds__(128 * G, 2) void k_bwd_dq(BwdArgs a) {
     if (st < total) issue_next();
 
   int J = 0;
-  bool mine = false, full = false;
+  // valid-key mask of the current block for this wave (zero when the row
+  // does not list it), a scalar word taken once per block
+  uint64_t kmask = 0;
   for (int st = 0; st < total; ++st) {
     if ((st & 1) == 0) {
       J = cw.next_known(un_lo, un_hi);
-      mine = lane_word(own_lo, own_hi, J >> 6) >> (J & 63) & 1;
-      full = lane_word(full_lo, full_hi, J >> 6) >> (J & 63) & 1;
+      const bool mine = lane_word(own_lo, own_hi, J >> 6) >> (J & 63) & 1;
+      const bool full = lane_word(full_lo, full_hi, J >> 6) >> (J & 63) & 1;
+      kmask = !mine ? 0ull : (full ? ~0ull : sload(a.blk_mask, J));
     }
     wait_steps<PW, NST>(st, total);
     barrier_no_fence();
     if (st + NST - 1 < total) issue_next();
 
     const int u = st & 1;
-    uint32_t mh = 0;
-    if (mine) mh = full ? 0xFFFFFFFFu : (uint32_t)(sload(a.blk_mask, J) >> (32 * u));
+    const uint32_t mh = (uint32_t)(kmask >> (32 * u));
     if (mh == 0) continue;   // not in this row, or a half of pad keys
     const uint4* kst = ring + (st % NST) * (STAGE / 16);
     const uint4* vst = kst + HALF / 16;
@@ -482,21 +484,22 @@ __global__ __launch_bounds__(128 * G, G) void k_bwd_dkdv(BwdArgs a) {
     if (st < total) issue_next();
 
   int I = 0;
+  // valid-query mask of the current block for this wave (zero when the
+  // column does not list it), a scalar word taken once per block
   uint64_t qm64 = 0;
-  bool mine = false;
   for (int st = 0; st < total; ++st) {
     if ((st & 1) == 0) {
       I = cw.next_known(un_lo, un_hi);
-      mine = lane_word(own_lo, own_hi, I >> 6) >> (I & 63) & 1;
-      qm64 = sload(a.blk_mask, I);
+      const bool mine = lane_word(own_lo, own_hi, I >> 6) >> (I & 63) & 1;
+      qm64 = mine && kmask != 0 ? sload(a.blk_mask, I) : 0ull;
     }
     wait_steps<PW, NST>(st, total);
     barrier_no_fence();
     if (st + NST - 1 < total) issue_next();
 
     const int u = st & 1;
-    const uint32_t qm = mine ? (uint32_t)(qm64 >> (32 * u)) : 0u;
-    if (qm == 0 || kmask == 0) continue;   // not in this column, pad queries, or a wave of pad keys
+    const uint32_t qm = (uint32_t)(qm64 >> (32 * u));
+    if (qm == 0) continue;   // not in this column, pad queries, or a wave of pad keys
     const uint4* qst = ring + (st % NST) * (STAGE / 16);
     const uint4* dst_ = qst + HALF / 16;
     const uint4* qtst = qst + 2 * HALF / 16;
@@ -665,21 +668,22 @@ __global__ __launch_bounds__(128 * G, OCC) void k_bwd_dkv(BwdArgs a) {
     if (st < total) issue_next();
 
   int I = 0;
+  // valid-query mask of the current block for this wave (zero when the
+  // column does not list it), a scalar word taken once per block
   uint64_t qm64 = 0;
-  bool mine = false;
   for (int st = 0; st < total; ++st) {
     if ((st & 1) == 0) {
       I = cw.next_known(un_lo, un_hi);
-      mine = lane_word(own_lo, own_hi, I >> 6) >> (I & 63) & 1;
-      qm64 = sload(a.blk_mask, I);
+      const bool mine = lane_word(own_lo, own_hi, I >> 6) >> (I & 63) & 1;
+      qm64 = mine && kmask != 0 ? sload(a.blk_mask, I) : 0ull;
     }
     wait_steps<PW, NST>(st, total);
     barrier_no_fence();
     if (st + NST - 1 < total) issue_next();
 
     const int u = st & 1;
-    const uint32_t qm = mine ? (uint32_t)(qm64 >> (32 * u)) : 0u;
-    if (qm == 0 || kmask == 0) continue;   // not in this column, pad queries, or a wave of pad keys
+    const uint32_t qm = (uint32_t)(qm64 >> (32 * u));
+    if (qm == 0) continue;   // not in this column, pad queries, or a wave of pad keys
     const uint4* qst = ring + (st % NST) * (STAGE / 16);
     const uint4* t1 = qst + HALF / 16;       // dO rows (dK) or dO^T (dV)
     const uint4* t2 = qst + 2 * HALF / 16;   // Q^T (dK)
