@@ -309,22 +309,22 @@ __global__ __launch_bounds__(128 * G, 2) void k_bwd_dq(BwdArgs a) {
   const char* kbase = (const char*)(a.k + head * D);
   const char* vbase = (const char*)(a.v + head * D);
   const char* tbase = (const char*)(a.kt + head * D);
-  int issued = 0, curJ = 0;
+  int curJ = 0;
   const int total = union_steps(un_lo, un_hi);   // two halves per union block
-  auto issue_next = [&]() __attribute__((always_inline)) {
-    if ((issued & 1) == 0) curJ = iw.next_known(un_lo, un_hi);
-    const int u = issued & 1;
+  // loads of half u of the walk's next block into ring stage `stage` (a
+  // compile-time constant at every call site of the unrolled loop)
+  auto issue_next = [&](int stage, int u) __attribute__((always_inline)) {
+    if (u == 0) curJ = iw.next_known(un_lo, un_hi);
     const int64_t roff0 = ((int64_t)curJ * 64 + 32 * u) * D * 2;
     const int64_t toff0 = (int64_t)curJ * 64 * D * 2 + u * HALF;
-    const uint32_t dst = lds_addr(ring) + (issued % NST) * STAGE;
+    const uint32_t dst = lds_addr(ring) + stage * STAGE;
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
       const uint32_t o1 = (NW * j + w) * 1024;
-      dma16u(kbase + roff0, roff[j], dst + o1);
-      dma16u(vbase + roff0, roff[j], dst + HALF + o1);
-      dma16u(tbase + toff0, toff[j], dst + 2 * HALF + o1);
+      dma16(kbase + roff0, roff[j], dst + o1);
+      dma16(vbase + roff0, roff[j], dst + HALF + o1);
+      dma16(tbase + toff0, toff[j], dst + 2 * HALF + o1);
     }
-    ++issued;
   };
 
   f32x16 acc[DT];
@@ -332,13 +332,19 @@ __global__ __launch_bounds__(128 * G, 2) void k_bwd_dq(BwdArgs a) {
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
 #pragma unroll
   for (int st = 0; st < NST - 1; ++st)
-    if (st < total) issue_next();
+    if (st < total) issue_next(st, st & 1);
 
   int J = 0;
   // valid-key mask of the current block for this wave (zero when the row
   // does not list it), a scalar word taken once per block
   uint64_t kmask = 0;
-  for (int st = 0; st < total; ++st) {
+  // unrolled by the ring depth: copy kk reads stage kk (offsets fold into
+  // the LDS reads' immediates) and loads into stage (kk + NST - 1) % NST
+  for (int st0 = 0; st0 < total; st0 += NST) {
+#pragma unroll
+  for (int kk = 0; kk < NST; ++kk) {
+    const int st = st0 + kk;
+    if (st >= total) break;
     if ((st & 1) == 0) {
       J = cw.next_known(un_lo, un_hi);
       const bool mine = lane_word(own_lo, own_hi, J >> 6) >> (J & 63) & 1;
@@ -347,12 +353,12 @@ __global__ __launch_bounds__(128 * G, 2) void k_bwd_dq(BwdArgs a) {
     }
     wait_steps<PW, NST>(st, total);
     barrier_no_fence();
-    if (st + NST - 1 < total) issue_next();
+    if (st + NST - 1 < total) issue_next((kk + NST - 1) % NST, (st + NST - 1) & 1);
 
     const int u = st & 1;
     const uint32_t mh = (uint32_t)(kmask >> (32 * u));
     if (mh == 0) continue;   // not in this row, or a half of pad keys
-    const uint4* kst = ring + (st % NST) * (STAGE / 16);
+    const uint4* kst = ring + kk * (STAGE / 16);
     const uint4* vst = kst + HALF / 16;
     const uint4* tst = kst + 2 * HALF / 16;
     f32x16 s = {}, dp = {};
@@ -382,6 +388,7 @@ __global__ __launch_bounds__(128 * G, 2) void k_bwd_dq(BwdArgs a) {
       acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(tst[d * 4 + ((0 + h) ^ sw)]), db0, acc[dt], 0, 0, 0);
       acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(tst[d * 4 + ((2 + h) ^ sw)]), db1, acc[dt], 0, 0, 0);
     }
+  }
   }
   if (!has_row) continue;
   // acc[dt][r]: dQ^T[32 dt + 8 (r/4) + 4 h + r%4][query l32]
