@@ -666,19 +666,46 @@ __global__ __launch_bounds__(128 * G, OCC) void k_bwd_dkv(BwdArgs a) {
     if (lane < LDW / 4) dma16u(lbase + (int64_t)curI * 64 + 32 * u, lane * 16, dst + NT * HALF + 4 * LDW * w);
     ++issued;
   };
+  // the same loads into a ring stage and block half known at compile time
+  // (the dK loop below is unrolled by the ring depth)
+  auto issue_at = [&](int stage, int u) __attribute__((always_inline)) {
+    if (u == 0) curI = iw.next_known(un_lo, un_hi);
+    const int64_t roff0 = ((int64_t)curI * 64 + 32 * u) * D * 2;
+    const int64_t toff0 = (int64_t)curI * 64 * D * 2 + u * HALF;
+    const uint32_t dst = lds_addr(ring) + stage * STAGE;
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+      const uint32_t o1 = (NW * j + w) * 1024;
+      dma16(qbase + roff0, roff[j], dst + o1);
+      dma16(dbase + roff0, roff[j], dst + HALF + o1);
+      dma16(qtbase + toff0, toff[j], dst + 2 * HALF + o1);
+    }
+    if (lane < LDW / 4) dma16(lbase + (int64_t)curI * 64 + 32 * u, lane * 16, dst + NT * HALF + 4 * LDW * w);
+  };
 
   f32x16 acc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
 #pragma unroll
   for (int st = 0; st < NST - 1; ++st)
-    if (st < total) issue_next();
+    if (st < total) {
+      if (DK) issue_at(st, st & 1);
+      else issue_next();
+    }
 
   int I = 0;
   // valid-query mask of the current block for this wave (zero when the
   // column does not list it), a scalar word taken once per block
   uint64_t qm64 = 0;
-  for (int st = 0; st < total; ++st) {
+  // dK: unrolled by the ring depth, so copy kk reads stage kk (offsets fold
+  // into the LDS reads' immediates); dV keeps one copy (its unrolled form
+  // spills at three waves per SIMD)
+  constexpr int UNR = DK ? NST : 1;
+  for (int st0 = 0; st0 < total; st0 += UNR) {
+#pragma unroll
+  for (int kk = 0; kk < UNR; ++kk) {
+    const int st = st0 + kk;
+    if (st >= total) break;
     if ((st & 1) == 0) {
       I = cw.next_known(un_lo, un_hi);
       const bool mine = lane_word(own_lo, own_hi, I >> 6) >> (I & 63) & 1;
@@ -686,12 +713,15 @@ __global__ __launch_bounds__(128 * G, OCC) void k_bwd_dkv(BwdArgs a) {
     }
     wait_steps<PW, NST>(st, total);
     barrier_no_fence();
-    if (st + NST - 1 < total) issue_next();
+    if (st + NST - 1 < total) {
+      if (DK) issue_at((kk + NST - 1) % NST, (st + NST - 1) & 1);
+      else issue_next();
+    }
 
     const int u = st & 1;
     const uint32_t qm = (uint32_t)(qm64 >> (32 * u));
     if (qm == 0) continue;   // not in this column, pad queries, or a wave of pad keys
-    const uint4* qst = ring + (st % NST) * (STAGE / 16);
+    const uint4* qst = ring + (DK ? kk : st % NST) * (STAGE / 16);
     const uint4* t1 = qst + HALF / 16;       // dO rows (dK) or dO^T (dV)
     const uint4* t2 = qst + 2 * HALF / 16;   // Q^T (dK)
     const float* lds_l = (const float*)(qst + NT * HALF / 16);
@@ -727,6 +757,7 @@ __global__ __launch_bounds__(128 * G, OCC) void k_bwd_dkv(BwdArgs a) {
       acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(at[d * 4 + ((0 + h) ^ sw)]), xb0, acc[dt], 0, 0, 0);
       acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(at[d * 4 + ((2 + h) ^ sw)]), xb1, acc[dt], 0, 0, 0);
     }
+  }
   }
   if (!has_blk) continue;
   // acc[dt][r]: [32 dt + 8 (r/4) + 4 h + r%4][key l32]
