@@ -783,8 +783,8 @@ static int attention_launch(fva_plan_t plan, const void* q_perm, const void* k_p
     if (G == 1) FVA_LAUNCH((k_attn_bf16<64, NS, 1, false>), 128);             \
     else FVA_LAUNCH((k_attn_bf16<64, NS, 2, false>), 256);
     if (lse) {   // training forward: the default shape only
-      if (d.head_dim == 128) FVA_LAUNCH((k_attn_bf16<128, 4, 2, true>), 256);
-      else FVA_LAUNCH((k_attn_bf16<64, 4, 2, true>), 256);
+      if (d.head_dim == 128) FVA_LAUNCH((k_attn_bf16<128, 2, 2, true>), 256);
+      else FVA_LAUNCH((k_attn_bf16<64, 2, 2, true>), 256);
     } else if (d.head_dim == 128) {
       if (ns == 2) { FVA_BF16_128(2) }
       else if (ns == 3) { FVA_BF16_128(3) }
