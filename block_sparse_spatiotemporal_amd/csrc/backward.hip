@@ -666,8 +666,9 @@ __global__ __launch_bounds__(128 * G, OCC) void k_bwd_dkv(BwdArgs a) {
     if (lane < LDW / 4) dma16u(lbase + (int64_t)curI * 64 + 32 * u, lane * 16, dst + NT * HALF + 4 * LDW * w);
     ++issued;
   };
-  // the same loads into a ring stage and block half known at compile time
-  // (the dK loop below is unrolled by the ring depth)
+  // dK only: the same loads into a ring stage and block half known at
+  // compile time (the dK loop below is unrolled by the ring depth, so the
+  // stage offsets need no readfirstlane)
   auto issue_at = [&](int stage, int u) __attribute__((always_inline)) {
     if (u == 0) curI = iw.next_known(un_lo, un_hi);
     const int64_t roff0 = ((int64_t)curI * 64 + 32 * u) * D * 2;
