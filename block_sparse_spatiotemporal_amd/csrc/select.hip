@@ -348,8 +348,12 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, 
 // that bin holds <= 64 keys they are sorted across the wave (bitonic) and the
 // exact cut is read off a prefix sum.  Output: a bitmask of kept ids per row
 // and the kept count.
+// Ten mask words (up to 640 blocks, the 480P shapes) fit four waves per SIMD
+// in 128 VGPRs (4 of them spilled); the selection then took
+// 0.87 instead of 0.90 ms at the Wan-14B 480P shape, lists unchanged.  Wider
+// rows keep the compiler's choice: forcing four waves spills 23 and more.
 template <int NI>
-__global__ __launch_bounds__(256) void k_select(const double* __restrict__ z, const double2* __restrict__ rowstat,
+__global__ __launch_bounds__(256, NI == 10 ? 4 : 1) void k_select(const double* __restrict__ z, const double2* __restrict__ rowstat,
                                                 const float* __restrict__ scores_in, float* __restrict__ s_out,
                                                 SelectArgs pa, int p_count, int k_min, int n_blk,
                                                 int64_t n_rows, int32_t* __restrict__ rowcnt,
