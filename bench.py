@@ -76,9 +76,16 @@ def measured_traffic(workload):
     return float(m_b.group(1))
 
 
-def cpu_baseline(w, q, k, v, n_heads, p_head):
-    """The oracle, untuned, on the first n_heads (b, h) pairs of the same
-    inputs; scaled linearly to one whole call."""
+def cpu_baseline(w, q, k, v, n_heads, p_head, gpu_head_nnz, gpu_nnz):
+    """The oracle, untuned, on a sample of n_heads (b, h) pairs of the same
+    inputs, scaled to one whole call.
+
+    The sample spans the call's range of per-head cost: heads are ranked by
+    their kept-block count on the GPU lists and taken at evenly spaced
+    quantiles.  Stages whose cost is the same for every head (permute, pool,
+    score, select, unpermute) are scaled by the head count; the attention
+    stage, whose cost follows the kept blocks, is scaled by the call's kept
+    blocks over the sample's (the oracle's own count for the sampled heads)."""
     from block_sparse_spatiotemporal_amd import synth
     from oracle import fva_oracle as O
     try:
@@ -86,19 +93,75 @@ def cpu_baseline(w, q, k, v, n_heads, p_head):
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         blas_threads = 1
-    pairs = [(b, h) for b in range(w.B) for h in range(w.H)][:n_heads]
+    host_cores = len(os.sched_getaffinity(0))
+    all_pairs = [(b, h) for b in range(w.B) for h in range(w.H)]
+    n_heads = max(1, min(n_heads, len(all_pairs)))
+    ranked = np.argsort(np.asarray(gpu_head_nnz), kind="stable")
+    picks = sorted({int(ranked[int((i + 0.5) * len(all_pairs) / n_heads)]) for i in range(n_heads)})
+    pairs = [all_pairs[i] for i in picks]
     opl = O.plan(w.grid, tile=w.tile, order=w.order, sub=w.sub)
-    t0 = time.perf_counter()
+    t_head, t_attn, nnz_s = 0.0, 0.0, 0
     for b, h in pairs:
         sl = lambda a: synth.to_f64(a[b:b + 1, :, h:h + 1, :], w.dtype)
-        O.run(sl(q), sl(k), sl(v), opl, float(p_head[h]), w.k_min, "none")
-    dt = time.perf_counter() - t0
-    scale = (w.B * w.H) / len(pairs)
-    return {"value": round(dt * scale * 1e3, 1), "unit": "ms/call", "cores": int(blas_threads),
-            "kind": "oracle",
-            "sample": f"{len(pairs)} of {w.B * w.H} (b,h) heads of the same inputs, full path "
-                      f"(plan, permute, pool, score, select, attention, unpermute; no slack fill), "
-                      f"{dt:.1f} s, scaled x{scale:g}"}
+        qr, kr, vr = sl(q), sl(k), sl(v)
+        t0 = time.perf_counter()
+        qp, kp, vp = O.permute(qr, opl), O.permute(kr, opl), O.permute(vr, opl)
+        qbar = O.pool(qp, opl)
+        if opl.n_sub:
+            kbs, empty = O.pool_sub(kp, opl)
+            S = O.score_sub(qbar, kbs, empty)
+        else:
+            S = O.score(qbar, O.pool(kp, opl))
+        rp, ci = O.select(S, float(p_head[h]), w.k_min)
+        t1 = time.perf_counter()
+        op = O.attention(qp, kp, vp, rp, ci, opl)
+        t2 = time.perf_counter()
+        O.unpermute(op, opl)
+        t3 = time.perf_counter()
+        t_head += (t1 - t0) + (t3 - t2)
+        t_attn += t2 - t1
+        nnz_s += int(rp[-1])
+    s_head = len(all_pairs) / len(pairs)
+    s_attn = gpu_nnz / max(nnz_s, 1)
+    total = t_head * s_head + t_attn * s_attn
+    return {"value": round(total * 1e3, 1), "unit": "ms/call", "cores": int(blas_threads),
+            "host_cores": host_cores, "blas_threads": int(blas_threads), "kind": "oracle",
+            "sample": f"{len(pairs)} of {len(all_pairs)} (b,h) heads of the same inputs at evenly spaced "
+                      f"quantiles of per-head kept blocks ({nnz_s} of {gpu_nnz} kept blocks), full path "
+                      f"(plan, permute, pool, score, select, attention, unpermute; no slack fill): "
+                      f"per-head stages {t_head:.1f} s scaled x{s_head:g} by heads, attention "
+                      f"{t_attn:.1f} s scaled x{s_attn:.2f} by kept blocks"}
+
+
+def reuse_drift(w, plan, bufs, qd, kd, vd, out, p, sched, steps=4, step_std=0.1):
+    """What reusing a selection costs in output: steps 1..steps of a seeded
+    random walk on Q, K, V (N(0, step * step_std^2) added per element, torch's
+    generator seeded with the workload seed, re-rounded to the input dtype);
+    at each step the step-0 lists are reused and compared with a fresh
+    selection: Jaccard ratio of the kept (I, J) pairs over all heads, and the
+    max / mean absolute change of the output.  Overwrites bufs and out."""
+    import torch
+    from block_sparse_spatiotemporal_amd import fva
+    rp0, ci0 = bufs.row_ptr.clone(), bufs.col_idx.clone()
+    fresh, cached = torch.empty_like(out), torch.empty_like(out)
+    counts = torch.empty(w.B * w.H, 2, dtype=torch.int64, device="cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed)
+    res = []
+    for step in range(1, steps + 1):
+        sd = step_std * float(np.sqrt(step))
+        x = [(t.float() + sd * torch.randn(t.shape, generator=gen, device="cuda")).to(t.dtype) for t in (qd, kd, vd)]
+        fva.attention_call(plan, x[0], x[1], x[2], fresh, p, w.k_min, bufs, slack=w.slack, sched=sched, fused=True)
+        fva.fva_attention_raster(plan, bufs.q, bufs.k, bufs.vt, rp0, ci0, cached, sched=sched)
+        fva.fva_mask_overlap(plan, rp0, ci0, bufs.row_ptr, bufs.col_idx, counts)
+        torch.cuda.synchronize()
+        c = counts.sum(dim=0).tolist()
+        d = (cached.float() - fresh.float()).abs()
+        res.append({"step": step, "drift_std": round(sd, 4), "jaccard": round(c[0] / c[1], 4),
+                    "max_abs_out_change": round(d.max().item(), 5),
+                    "mean_abs_out_change": round(d.mean().item(), 6)})
+        del x, d
+    return res
 
 
 def copy_probe(mib, steps):
@@ -288,9 +351,19 @@ def main():
     nnz = int(bufs.row_ptr[-1].item())
     head_nnz = bufs.head_nnz.cpu().numpy()
     n_blk = plan.n_blk
+    # FLOPs per kept block pair: S = Q K^T and O += P V over 64 queries and
+    # 64 keys (4*64*64*D), the work counted with the pad tokens of a kept
+    # block included.  The kernel steps over 32-key halves and skips a half
+    # whose 32 keys are all padding, so the executed count, which the
+    # roofline uses, takes 4*64*32*D per non-empty half of each kept block.
     sparse_flop = nnz * 4.0 * 64 * 64 * w.D
+    _, _, bmask, _ = fva.fva_plan_tables(plan.desc)
+    halves = ((bmask & np.uint64(0xFFFFFFFF)) != 0).astype(np.int64) + ((bmask >> np.uint64(32)) != 0)
+    col = bufs.col_idx[:nnz].cpu().numpy()
+    exec_flop = float(halves[col].sum()) * 4.0 * 64 * 32 * w.D
     dense_flop = 4.0 * w.B * w.H * float(w.n_tokens) ** 2 * w.D
-    attn_tflops = sparse_flop / (st_mean["attention"] * 1e-3) / 1e12
+    attn_tflops = exec_flop / (st_mean["attention"] * 1e-3) / 1e12
+    attn_tflops_padded = sparse_flop / (st_mean["attention"] * 1e-3) / 1e12
     dens = head_nnz / float(n_blk * n_blk)
 
     # algorithmic bytes of the HBM-bound stages (valid rows at the element size)
@@ -325,7 +398,11 @@ def main():
         "dense_equiv_tflops": round(dense_flop / (ms_call * 1e-3) / 1e12, 2),
         "attention_sparse_tflops": round(attn_tflops, 2),
         "mfma_util_pct": round(100.0 * attn_tflops / PEAK_BF16_TFLOPS, 2),
+        "executed_tflop_per_call": round(exec_flop / 1e12, 3),
         "sparse_tflop_per_call": round(sparse_flop / 1e12, 3),
+        "mfma_util_padded_blocks_pct": round(100.0 * attn_tflops_padded / PEAK_BF16_TFLOPS, 2),
+        "flop_count": "mfma_util and roofline: 4*64*32*D per non-empty 32-key half of each kept block "
+                      "(executed); *_padded_blocks: 4*64*64*D per kept block",
         "nnz_blocks": nnz,
         "density": {"mean": round(float(dens.mean()), 4), "min": round(float(dens.min()), 4),
                     "max": round(float(dens.max()), 4)},
@@ -350,7 +427,8 @@ def main():
                      "launch_ms": round(st_mean["attention"], 4)},
     }
     if not args.no_cpu:
-        res["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_heads, p_head)
+        res["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_heads, p_head, head_nnz, nnz)
+    res["reuse"]["drift"] = reuse_drift(w, plan, bufs, qd, kd, vd, out, p, args.sched)
     print(json.dumps(res), flush=True)
 
 

@@ -4,6 +4,7 @@ Usage: python -m block_sparse_spatiotemporal_amd.build   (or call build()).
 """
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import shutil
 import subprocess
@@ -29,7 +30,7 @@ def build(verbose: bool = False) -> str:
     os.makedirs(objdir, exist_ok=True)
     common = ["-O3", "-std=c++17", "-fPIC", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
               "-Wall", "-Wno-unused-function"]
-    objs = []
+    objs, cmds = [], []
     for src in SOURCES:
         obj = os.path.join(objdir, src + ".o")
         cmd = [hipcc()] + common + ["-c", os.path.join(CSRC, src), "-o", obj]
@@ -37,8 +38,14 @@ def build(verbose: bool = False) -> str:
                     "-packed-fp32-ops", "-ffp-contract=fast"]
         if verbose:
             print(" ".join(cmd), flush=True)
-        subprocess.run(cmd, check=True)
+        cmds.append(cmd)
         objs.append(obj)
+    # the sources compile independently: run them side by side
+    jobs = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", "4"))))
+    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+        for r in list(ex.map(lambda c: subprocess.run(c), cmds)):
+            if r.returncode != 0:
+                raise subprocess.CalledProcessError(r.returncode, r.args)
     tmp = LIB + ".tmp"
     subprocess.run([hipcc(), "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp] + objs, check=True)
     os.replace(tmp, LIB)

@@ -664,6 +664,7 @@ int attn_order() {
 // XCD gets the same number of them (12 heads: half-heads, 3 per XCD, 2.5%
 // faster).  Plain grid: 32, since in-order dispatch would stall every XCD
 // behind the one holding the heaviest head.  FVA_ATTN_CHUNK overrides it.
+constexpr int kMaxChunk = 4096;
 int attn_chunk(int groups_per_head, int n_heads, bool persistent) {
   int g = n_heads, b = kXcds;
   while (b) { const int t = g % b; g = b; b = t; }   // gcd(n_heads, 8)
@@ -671,7 +672,9 @@ int attn_chunk(int groups_per_head, int n_heads, bool persistent) {
   const int dflt = persistent ? (groups_per_head + parts - 1) / parts : 32;
   const char* v = getenv("FVA_ATTN_CHUNK");
   int n = v ? atoi(v) : dflt;
-  if (n < 1 || n > 65536) n = dflt;
+  // the plan sizes wg_times (max_wg) for plain grids rounded up to 8 chunks
+  // of at most kMaxChunk groups
+  if (n < 1 || n > kMaxChunk) n = dflt;
   return n;
 }
 
@@ -727,6 +730,13 @@ static int attention_launch(fva_plan_t plan, const void* q_perm, const void* k_p
   int G = d.dtype == FVA_DTYPE_BF16 ? (lse ? 2 : attn_group()) : 1;   // the training form is G = 2 only
   if (d.head_dim == 64 && G > 2) G = 2;   // a 4 KB half splits over at most 4 waves
   const bool paired = G == 2 && attn_pair() == 1;
+  const int64_t n_items = (int64_t)n_bh * ((in.n_blk + G - 1) / G);
+  const int chunk = attn_chunk((in.n_blk + G - 1) / G, n_bh, sched_mode == FVA_SCHED_PERSISTENT);
+  {  // a plain grid rounds up to 8 chunks; wg_times holds 2*max_wg stamps
+    const int64_t deal = (int64_t)kXcds * chunk;
+    if (sched_mode == FVA_SCHED_PLAIN && (n_items + deal - 1) / deal * deal > in.max_wg)
+      return fva_fail(FVA_EINVAL, "plain grid exceeds max_wg %d", in.max_wg);
+  }
   if (paired) {
     fva_csr_bits(plan, row_ptr, col_idx, plan->rowmask, stream);
     fva_pair_blocks(plan, plan->rowmask, plan->pairs, stream);
@@ -758,10 +768,10 @@ static int attention_launch(fva_plan_t plan, const void* q_perm, const void* k_p
   a.n_tok = in.n_tokens;
   a.heads = d.heads;
   a.n_pad = in.n_pad;
-  a.n_items = n_bh * ((in.n_blk + G - 1) / G);
+  a.n_items = (int)n_items;
   a.n_blk = in.n_blk;
   a.persistent = sched_mode == FVA_SCHED_PERSISTENT;
-  a.chunk = attn_chunk((in.n_blk + G - 1) / G, n_bh, sched_mode == FVA_SCHED_PERSISTENT);
+  a.chunk = chunk;
   a.scale = 1.0f / sqrtf((float)d.head_dim);
 
 #define FVA_LAUNCH(KERNEL, THREADS)                                                              \

@@ -149,10 +149,10 @@ __global__ __launch_bounds__(kThreads) void k_permute_vt(const T* __restrict__ s
 // Pairs of the t, h and w axes for a head dimension: D/2 split as evenly as
 // possible, t first.
 __host__ __device__ inline void rope_split(int D, int* pt, int* ph, int* pw) {
-  const int n = D / 2;
-  *ph = n / 3;
-  *pw = n / 3;
-  *pt = n - *ph - *pw;
+  const int n = D / 2, q = n / 3, r = n % 3;
+  *pt = q + (r > 0);
+  *ph = q + (r > 1);
+  *pw = q;
 }
 
 // cos/sin table of one call: rows are axis positions (T rows for t, then H

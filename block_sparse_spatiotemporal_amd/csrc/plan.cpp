@@ -375,6 +375,10 @@ extern "C" int fva_plan_create(fva_plan_t* out, const fva_plan_desc* desc, hipSt
   return FVA_OK;
 }
 
+extern "C" int fva_plan(fva_plan_t* out, const fva_plan_desc* desc, hipStream_t stream) {
+  return fva_plan_create(out, desc, stream);
+}
+
 extern "C" int fva_plan_query(fva_plan_t plan, fva_plan_info* info) {
   if (!plan || !info) return fva_fail(FVA_EINVAL, "plan or info is NULL");
   *info = plan->info;

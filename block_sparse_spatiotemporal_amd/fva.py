@@ -151,7 +151,7 @@ class Plan:
         self.dtype = dtype
         self.torch_dtype = torch.bfloat16 if dtype == "bf16" else torch.float32
         h = c_vp()
-        _check(lib().fva_plan_create(ctypes.byref(h), ctypes.byref(self.desc), _stream(stream)))
+        _check(lib().fva_plan(ctypes.byref(h), ctypes.byref(self.desc), _stream(stream)))
         self.handle = h
         self.info = fva_plan_info()
         _check(lib().fva_plan_query(h, ctypes.byref(self.info)))

@@ -243,3 +243,18 @@ def make_dout(w: Workload, threads: int | None = None, heads=None, scale: float 
     with ThreadPoolExecutor(max_workers=nthr) as ex:
         list(ex.map(work, pairs))
     return out
+
+
+_DRIFT = 1001   # spawn-key slot for the drift streams (apart from any (b, h, tensor) key)
+
+
+def drift(w: Workload, x: np.ndarray, tensor: int, step: int, step_std: float = 0.1) -> np.ndarray:
+    """Inputs of a later denoising step: ``x`` (a storage array from ``make``)
+    after ``step`` steps of a seeded random walk, i.e. plus
+    N(0, step * step_std^2) per element, one independent stream per
+    (tensor, step) pair, re-rounded to the workload's storage type.
+    ``tensor`` names the stream (0: Q, 1: K, 2: V)."""
+    f = bf16_bits_to_f32(x) if w.dtype == "bf16" else np.asarray(x, dtype=np.float32)
+    rng = _rng(w.seed, _DRIFT, tensor, step)
+    y = f + np.float32(step_std * np.sqrt(step)) * rng.standard_normal(f.shape, dtype=np.float32)
+    return f32_to_bf16_bits(y) if w.dtype == "bf16" else y.astype(np.float32)

@@ -141,6 +141,11 @@ int fva_plan_tables(const fva_plan_desc* desc, int32_t* perm, int32_t* blk_cnt,
  * handle.  The plan owns its device memory until fva_plan_destroy. */
 int fva_plan_create(fva_plan_t* out, const fva_plan_desc* desc, hipStream_t stream);
 
+/* The same call under the short name of the five-call sequence
+ * (fva_plan, fva_permute, fva_select, fva_attention, fva_unpermute):
+ * identical arguments, behaviour and status codes. */
+int fva_plan(fva_plan_t* out, const fva_plan_desc* desc, hipStream_t stream);
+
 /* Sizes of an existing plan. */
 int fva_plan_query(fva_plan_t plan, fva_plan_info* info);
 
@@ -182,7 +187,8 @@ int fva_permute_pool(fva_plan_t plan, const void* x_raster, void* x_perm, int32_
  * t_offset, so it needs no other chunk; section 2.3: the frequencies are
  * precomputed as one contiguous table).  For the raster token at grid
  * position (t, h, w) the D/2 dimension pairs (2p, 2p+1) are split over the
- * axes as evenly as possible, t first (D = 128: 22, 21, 21 pairs); pair i of
+ * axes as evenly as possible, the remainder to t then h (D = 128: 22, 21,
+ * 21 pairs; D = 64: 11, 11, 10); pair i of
  * an axis with P pairs turns by pos * base^(-i/P), pos being t + t_offset,
  * h or w.  The angles' cosines and sines are tabulated in fp64 on the device
  * for this call; the rotation runs in fp64 and is rounded once to the plan
@@ -357,7 +363,14 @@ int fva_mask_from_counts(fva_plan_t plan, const int32_t* counts, int32_t min_cou
                          int32_t* col_idx, int32_t* head_nnz, hipStream_t stream);
 
 /* Scatter block-order [B, H, N_pad, D] (FVA_LAYOUT_ROWS) back to raster
- * [B, N, H, D], dropping pad positions.  Inverse of fva_permute. */
+ * [B, N, H, D], dropping pad positions ("Video Sparse Attention" section 3:
+ * the cube-contiguous token order exists only for the fine stage, and the
+ * caller's sequence order is restored after it; "DFSAttn" trick 1: the
+ * Hilbert reordering is undone after attention).  Inverse of fva_permute:
+ * x_raster[b, perm[pos], h, :] = x_perm[b, h, pos, :] for every valid pos;
+ * raster rows are written once each, nothing else is touched.
+ * x_perm and x_raster must not overlap.  Errors: FVA_EINVAL for NULL
+ * pointers or an unknown plan dtype. */
 int fva_unpermute(fva_plan_t plan, const void* x_perm, void* x_raster, hipStream_t stream);
 
 /* Message for the last non-zero status returned on this thread. */

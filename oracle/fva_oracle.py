@@ -91,15 +91,6 @@ def hilbert_key(coords, bits: int) -> int:
     return key
 
 
-def hilbert_point(key: int, bits: int, n: int = 3):
-    """Inverse of ``hilbert_key`` by exhaustive table (small cubes only)."""
-    side = 1 << bits
-    for c in np.ndindex(*(side,) * n):
-        if hilbert_key(c, bits) == key:
-            return c
-    raise ValueError(key)
-
-
 # --------------------------------------------------------------------------
 # Plan: padding, block order and per-position tables.  [VSA] section 3 (cube
 # tiles), [DFSAttn] trick 1 (Hilbert order).  Tokens are in raster ("book")
@@ -398,9 +389,9 @@ def run(q, k, v, pl: Plan, p_head, k_min: int, slack: str = "none"):
 def rope_pairs(head_dim: int):
     """Number of rotation pairs given to the t, h and w axes."""
     n = head_dim // 2
-    pw = n // 3
-    ph = n // 3
-    return n - ph - pw, ph, pw
+    q, r = divmod(n, 3)
+    # the remainder goes one pair at a time to t, then h
+    return q + (1 if r > 0 else 0), q + (1 if r > 1 else 0), q
 
 
 def rope_angles(grid, head_dim: int, t_offset: int = 0, base: float = 10000.0):

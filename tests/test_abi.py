@@ -18,6 +18,26 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, s), s
 
 
+def test_five_call_sequence_names_are_exported():
+    # plan -> permute -> select -> attention -> unpermute, each a C symbol
+    L = fva.lib()
+    for s in ("fva_plan", "fva_permute", "fva_select", "fva_attention", "fva_unpermute",
+              "fva_plan_destroy", "fva_plan_query", "fva_last_error"):
+        assert s in fva.header_symbols(), s
+        assert hasattr(L, s), s
+
+
+def test_fva_plan_validates_like_plan_create():
+    L = fva.lib()
+    d = fva.make_desc(1, 1, 96, (4, 4, 4))           # head_dim 96 is not built
+    h = ctypes.c_void_p()
+    for fn in (L.fva_plan, L.fva_plan_create):
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(fva.fva_plan_desc), ctypes.c_void_p]
+        assert fn(ctypes.byref(h), ctypes.byref(d), None) == fva.FVA_EUNSUPPORTED
+        assert fn(None, ctypes.byref(d), None) == fva.FVA_EINVAL
+
+
 @pytest.mark.parametrize("grid,order,sub,dtype,hd", [
     ((8, 16, 16), "tile", (0, 0, 0), "f32", 64),
     ((21, 30, 52), "tile", (0, 0, 0), "bf16", 128),
@@ -102,3 +122,19 @@ def test_null_arguments_rejected_before_any_device_work():
     assert L.fva_select_pooled(None, p, 1, 0, 0, None, None, None, None, None) == fva.FVA_EINVAL
     assert L.fva_select(None, None, None, p, 1, 0, 0, None, None, None, None, None, None) == fva.FVA_EINVAL
     L.fva_plan_destroy(None)   # accepted
+
+
+@pytest.mark.parametrize("batch,heads,grid", [
+    (1, 1, (1, 1, 1)), (1, 12, (21, 30, 52)), (2, 40, (21, 30, 52)),
+    (1, 40, (21, 45, 80)), (1, 1, (64, 64, 64)), (8, 64, (4, 4, 4)),
+])
+def test_plain_grid_fits_wg_times_over_the_chunk_range(batch, heads, grid):
+    # FVA_ATTN_CHUNK is honoured in [1, 4096]; a plain launch rounds its grid up
+    # to whole deals of 8 chunks, and every workgroup stamps wg_times[2*wg..]:
+    # the plan's max_wg must cover the largest such grid for every group size.
+    info = fva.fva_plan_dims(fva.make_desc(batch, heads, 128, grid))
+    for G in (1, 2, 4):
+        items = batch * heads * -(-info.n_blk // G)
+        for chunk in (1, 7, 32, 1000, 4095, 4096):
+            deal = 8 * chunk
+            assert -(-items // deal) * deal <= info.max_wg, (G, chunk)

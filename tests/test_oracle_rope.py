@@ -9,9 +9,30 @@ from oracle import fva_oracle as O
 
 
 def test_pair_split_is_even_t_first():
+    # D/2 pairs over (t, h, w) as evenly as possible, the remainder to t then h:
+    # 64 = 22+21+21, 48 = 16+16+16, 32 = 11+11+10, 5 = 2+2+1, 4 = 2+1+1, 3 = 1+1+1
     assert O.rope_pairs(128) == (22, 21, 21)
-    assert O.rope_pairs(64) == (12, 10, 10)
-    assert sum(O.rope_pairs(6)) == 3
+    assert O.rope_pairs(96) == (16, 16, 16)
+    assert O.rope_pairs(64) == (11, 11, 10)
+    assert O.rope_pairs(10) == (2, 2, 1)
+    assert O.rope_pairs(8) == (2, 1, 1)
+    assert O.rope_pairs(6) == (1, 1, 1)
+
+
+def test_hand_worked_frequencies_small_base():
+    # D = 12: two pairs per axis; base 16 makes pair i of an axis turn by
+    # pos * 16**(-i/2), i.e. by pos and by pos/4.  Token (t=1, h=2, w=3) of a
+    # (2, 3, 4) grid with t_offset 1 sits at raster n = (1*3 + 2)*4 + 3 = 23
+    # and has positions t = 2, h = 2, w = 3, so the six pair angles are
+    # 2, 0.5 (t), 2, 0.5 (h), 3, 0.75 (w).
+    x = np.zeros((1, 24, 1, 12))
+    x[0, 23, 0] = [1, 0, 0, 1, 1, 0, 0, 1, 1, 0, 0, 1]
+    out = O.rope(x, (2, 3, 4), t_offset=1, base=16.0)[0, 23, 0]
+    c, s = math.cos, math.sin
+    want = [c(2), s(2), -s(0.5), c(0.5),      # t pairs: (1,0) by 2, (0,1) by 0.5
+            c(2), s(2), -s(0.5), c(0.5),      # h pairs
+            c(3), s(3), -s(0.75), c(0.75)]    # w pairs
+    assert np.allclose(out, want, atol=1e-15)
 
 
 def test_hand_worked_example():
