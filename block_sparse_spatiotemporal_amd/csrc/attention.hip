@@ -9,6 +9,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdlib>
+#include <mutex>
 
 #include "attn_common.h"
 #include "fva_internal.h"
@@ -837,4 +838,112 @@ extern "C" int fva_attention_lse(fva_plan_t plan, const void* q_perm, const void
   if (plan->desc.dtype != FVA_DTYPE_BF16) return fva_fail(FVA_EUNSUPPORTED, "the training path is bf16 only");
   return attention_launch(plan, q_perm, k_perm, vt_perm, row_ptr, col_idx, o_perm, FVA_SCHED_PERSISTENT, nullptr,
                           lse, o32, false, stream);
+}
+
+// ------------------------------------------------------ no-allocation entry
+// fva_attention_static: fva_attention for callers that cannot allocate device
+// memory (code under graph capture, serving loops, harnesses that forbid
+// hipMalloc).  It takes the plan descriptor instead of a plan and keeps
+// everything a plan would own for the call in one file-scope device array:
+// the block validity tables, built by a kernel from the descriptor (tile
+// order), and the scheduler's row bitmaps, pair table, work list and
+// cursors.  Each device holds its own copy until the process ends; calls on
+// one device share it, so calls that overlap on a device race.
+namespace {
+
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_static_mu;
+void* g_static_ptr[kMaxDevices];   // device address of `scratch` per device
+int g_static_cus[kMaxDevices];     // compute units per device
+
+// Validity tables of a tile-order plan: blk_mask[j] bit i set when local
+// position i of block j lies inside the token grid; blk_full bit j set when
+// block j has all 64 positions valid (64 words, blocks up to 4096).
+__global__ __launch_bounds__(256) void k_static_tables(int GT, int GH, int GW, int tt, int th, int tw, int nbh,
+                                                       int nbw, int n_blk, uint64_t* __restrict__ blk_mask,
+                                                       uint64_t* __restrict__ blk_full) {
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  uint64_t m = 0;
+  if (j < n_blk) {
+    const int bt = j / (nbh * nbw), bh = (j / nbw) % nbh, bw = j % nbw;
+    for (int loc = 0; loc < FVA_BLK; ++loc) {
+      const int t = bt * tt + loc / (th * tw), h = bh * th + (loc / tw) % th, w = bw * tw + loc % tw;
+      if (t < GT && h < GH && w < GW) m |= uint64_t(1) << loc;
+    }
+    blk_mask[j] = m;
+  }
+  // one bit per block; lanes of a wave cover 64 consecutive blocks = one word
+  const uint64_t full = __ballot(j < n_blk && m == ~uint64_t(0));
+  if ((threadIdx.x & 63) == 0 && j / 64 < 64) blk_full[j / 64] = full;
+}
+
+}  // namespace
+
+extern "C" int fva_attention_static(const fva_plan_desc* desc, const void* q_perm, const void* k_perm,
+                                    const void* vt_perm, const int32_t* row_ptr, const int32_t* col_idx,
+                                    void* o_perm, hipStream_t stream) {
+  if (!desc) return fva_fail(FVA_EINVAL, "desc is NULL");
+  if (!q_perm || !k_perm || !vt_perm || !o_perm) return fva_fail(FVA_EINVAL, "tensor pointer is NULL");
+  if (!row_ptr || !col_idx) return fva_fail(FVA_EINVAL, "row_ptr / col_idx is NULL");
+  fva_plan_info in;
+  int rc = fva_plan_dims(desc, &in);
+  if (rc) return rc;
+  if (desc->order != FVA_ORDER_TILE)
+    return fva_fail(FVA_EUNSUPPORTED, "fva_attention_static supports tile order only");
+  // scratch carve-up, 256-byte aligned regions
+  const int nw = (in.n_blk + 63) / 64;
+  auto up = [](size_t b) { return (b + 255) & ~size_t(255); };
+  const size_t o_mask = 0, o_full = o_mask + up(sizeof(uint64_t) * in.n_blk), o_cnt = o_full + up(sizeof(uint64_t) * 64),
+               o_bits = o_cnt + up(sizeof(int32_t) * 64), o_work = o_bits + up(sizeof(uint64_t) * in.n_rows * nw),
+               o_pairs = o_work + up(sizeof(int32_t) * in.n_rows), need = o_pairs + up(sizeof(int2) * in.n_rows);
+  if (need > kStaticScratchBytes)
+    return fva_fail(FVA_EUNSUPPORTED, "fva_attention_static: this shape needs %zu bytes of scratch, the maximum is %zu",
+                    need, kStaticScratchBytes);
+  int dev = 0;
+  if ((rc = fva_hip_check(hipGetDevice(&dev), "hipGetDevice"))) return rc;
+  if (dev < 0 || dev >= kMaxDevices) return fva_fail(FVA_EUNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  void* base = nullptr;
+  int cus = 0;
+  {
+    // once per device, with that device current: the device address of its
+    // copy of `scratch` (the array's name is only a host-side stand-in)
+    std::lock_guard<std::mutex> lock(g_static_mu);
+    if (!g_static_ptr[dev]) {
+      void* ptr = nullptr;
+      if ((rc = fva_hip_check(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress"))) return rc;
+      int n = 0;
+      if ((rc = fva_hip_check(hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev),
+                              "hipDeviceGetAttribute")))
+        return rc;
+      g_static_cus[dev] = n > 0 ? n : 1;
+      g_static_ptr[dev] = ptr;
+    }
+    base = g_static_ptr[dev];
+    cus = g_static_cus[dev];
+  }
+  char* s = (char*)base;
+  fva_plan_s p{};
+  p.desc = *desc;
+  p.info = in;
+  p.esize = desc->dtype == FVA_DTYPE_BF16 ? 2 : 4;
+  p.nw = nw;
+  p.device = dev;
+  p.num_cu = cus;
+  p.stream = stream;
+  p.blk_mask = (uint64_t*)(s + o_mask);
+  p.blk_full = (uint64_t*)(s + o_full);
+  p.counters = (int32_t*)(s + o_cnt);
+  p.rowmask = (uint64_t*)(s + o_bits);
+  p.worklist = (int32_t*)(s + o_work);
+  p.pairs = (int2*)(s + o_pairs);
+  const int nbh = in.padded[1] / desc->tile[1], nbw = in.padded[2] / desc->tile[2];
+  // at least 16 workgroups so every blk_full word (64 of them) is written
+  const unsigned tgrid = (unsigned)std::max((in.n_blk + 255) / 256, 16);
+  hipLaunchKernelGGL(k_static_tables, dim3(tgrid), dim3(256), 0, stream, desc->grid[0], desc->grid[1], desc->grid[2],
+                     desc->tile[0], desc->tile[1], desc->tile[2], nbh, nbw, (int)in.n_blk, p.blk_mask, p.blk_full);
+  return attention_launch(&p, q_perm, k_perm, vt_perm, row_ptr, col_idx, o_perm, FVA_SCHED_PERSISTENT, nullptr,
+                          nullptr, nullptr, false, stream);
 }

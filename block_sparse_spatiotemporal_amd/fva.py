@@ -61,6 +61,8 @@ def lib() -> ctypes.CDLL:
             "fva_plan_dims": (c_i32, [P(fva_plan_desc), P(fva_plan_info)]),
             "fva_plan_tables": (c_i32, [P(fva_plan_desc), c_vp, c_vp, c_vp, c_vp]),
             "fva_plan_create": (c_i32, [P(c_vp), P(fva_plan_desc), c_vp]),
+            "fva_plan": (c_i32, [P(c_vp), P(fva_plan_desc), c_vp]),
+            "fva_attention_static": (c_i32, [P(fva_plan_desc)] + [c_vp] * 7),
             "fva_plan_query": (c_i32, [c_vp, P(fva_plan_info)]),
             "fva_plan_destroy": (None, [c_vp]),
             "fva_permute": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_vp]),
@@ -313,6 +315,13 @@ def fva_attention(plan: Plan, q_perm, k_perm, vt_perm, row_ptr, col_idx, o_perm,
     _check(lib().fva_attention(plan.handle, _ptr(q_perm), _ptr(k_perm), _ptr(vt_perm), _ptr(row_ptr),
                                _ptr(col_idx), _ptr(o_perm), SCHED[sched] if isinstance(sched, str) else int(sched),
                                _ptr(wg_times), _stream(stream)))
+
+
+def fva_attention_static(desc: fva_plan_desc, q_perm, k_perm, vt_perm, row_ptr, col_idx, o_perm, stream=None):
+    """fva_attention without a plan and without any device allocation (the
+    library's static scratch; tile order; persistent schedule)."""
+    _check(lib().fva_attention_static(ctypes.byref(desc), _ptr(q_perm), _ptr(k_perm), _ptr(vt_perm),
+                                      _ptr(row_ptr), _ptr(col_idx), _ptr(o_perm), _stream(stream)))
 
 
 def fva_attention_raster(plan: Plan, q_perm, k_perm, vt_perm, row_ptr, col_idx, o_raster, sched="persistent",

@@ -362,6 +362,31 @@ int fva_mask_accumulate(fva_plan_t plan, const int32_t* row_ptr, const int32_t* 
 int fva_mask_from_counts(fva_plan_t plan, const int32_t* counts, int32_t min_count, int32_t* row_ptr,
                          int32_t* col_idx, int32_t* head_nnz, hipStream_t stream);
 
+/* fva_attention for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * It needs no plan: it takes the plan descriptor, and everything a plan
+ * would own for the call (the block validity tables, built on the device
+ * from the descriptor, and the scheduler's row bitmaps, pair table, work
+ * list and cursors) lives in one static device array of 16 MiB that the
+ * library holds on each device it runs on until the process ends.  It calls
+ * no hipMalloc / hipFree and allocates nothing else.
+ *   desc      as for fva_plan_create; FVA_ORDER_TILE only
+ *             (FVA_EUNSUPPORTED otherwise).
+ *   other arguments as for fva_attention with FVA_SCHED_PERSISTENT and no
+ *             wg_times; o_perm is written in block order [B, H, N_pad, D].
+ * The result equals fva_attention's on a plan of the same descriptor, bit
+ * for bit (the same kernels).
+ * Limit: the scratch must hold 8*n_blk + 8*n_rows*ceil(n_blk/64) +
+ * 12*n_rows bytes plus alignment (Wan 480P at B*H = 80: 4.6 MiB; 720P at
+ * 40 heads: 11.3 MiB); a larger shape returns FVA_EUNSUPPORTED with a
+ * message before anything is enqueued.
+ * Concurrency: every call on a device shares that device's array; calls
+ * that overlap on one device (on different streams) race.  Calls in one
+ * stream are ordered and safe.  The first call on a device looks up the
+ * array's device address once (a host-side query, no allocation). */
+int fva_attention_static(const fva_plan_desc* desc, const void* q_perm, const void* k_perm, const void* vt_perm,
+                         const int32_t* row_ptr, const int32_t* col_idx, void* o_perm, hipStream_t stream);
+
 /* Scatter block-order [B, H, N_pad, D] (FVA_LAYOUT_ROWS) back to raster
  * [B, N, H, D], dropping pad positions ("Video Sparse Attention" section 3:
  * the cube-contiguous token order exists only for the fine stage, and the
