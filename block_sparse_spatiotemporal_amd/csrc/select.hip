@@ -50,14 +50,44 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
+// Inclusive wave prefix sum with DPP moves (no LDS traffic): row_shr 1, 2,
+// 4, 8 scan each row of 16 lanes, then row_bcast 15 and 31 carry the row
+// totals into the rows above.  Lanes a DPP move cannot source read 0.
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x, int ctrl_id) {
+  switch (ctrl_id) {
+    case 0: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);   // row_shr:1
+    case 1: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);   // row_shr:2
+    case 2: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);   // row_shr:4
+    case 3: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);   // row_shr:8
+    case 4: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);   // row_bcast:15
+    default: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  }
+}
 template <typename T>
 __device__ __forceinline__ T wave_incl_scan(T v, int lane) {
+  (void)lane;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    T u = __shfl_up(v, o);
-    if (lane >= o) v += u;
+  for (int c = 0; c < 6; ++c) {
+    if constexpr (sizeof(T) == 8) {
+      const uint64_t u = (uint64_t)v;
+      const uint64_t t = ((uint64_t)dpp_u32((uint32_t)(u >> 32), c) << 32) | dpp_u32((uint32_t)u, c);
+      v = (T)(u + t);
+    } else {
+      v = (T)((uint32_t)v + dpp_u32((uint32_t)v, c));
+    }
   }
   return v;
+}
+// The value of lane `src` (wave-uniform) of x.
+template <typename T>
+__device__ __forceinline__ T lane_value(T x, int src) {
+  if constexpr (sizeof(T) == 8) {
+    const uint64_t u = (uint64_t)x;
+    return (T)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(u >> 32), src) << 32) |
+               (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, src));
+  } else {
+    return (T)__builtin_amdgcn_readlane((int)x, src);
+  }
 }
 
 // The values of lanes l and l^16 (X = 16) or l and l^32 (X = 32) of an fp64
@@ -342,8 +372,10 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, 
 // read from scores_in.  The kept set
 // is the shortest prefix in (score desc, id asc) order whose fixed-point
 // mass reaches p, extended to the floor min(k_min, n).  It is found by an
-// MSD radix select over the 48-bit key (score bits << 16 | (0xFFFF - J)):
-// each level builds a 256-bin histogram of mass and count in LDS, keeps the
+// MSD radix select over the 48-bit key (score bits << 16 | (0xFFFF - J)),
+// starting below its always-zero sign bit so the first digit is the score's
+// exponent: each level builds a 256-bin histogram of mass and count in LDS
+// (prefix sums across the wave by DPP row shifts and broadcasts), keeps the
 // bin where the mass target or the count target is crossed, and as soon as
 // that bin holds <= 64 keys they are sorted across the wave (bitonic) and the
 // exact cut is read off a prefix sum.  Output: a bitmask of kept ids per row
@@ -407,7 +439,11 @@ __global__ __launch_bounds__(256, NI == 10 ? 4 : 1) void k_select(const double* 
       if (lane + 64 * i < n) active |= 1ull << i;
     bool all = false;
     for (int level = 0; level < 6; ++level) {
-      const int shift = 40 - 8 * level;
+      // key bit 47 (the score's sign) is 0 for every clamped score, so the
+      // levels take bits 46..39, 38..31, ..., 14..7, then 7..0 (bit 7 is
+      // already fixed by the prefix there): the first digit is the whole
+      // exponent, which splits a row over more bins than sign + 7 bits
+      const int shift = level < 5 ? 39 - 8 * level : 0;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         hmass[wv][lane * 4 + t] = 0;
@@ -436,7 +472,7 @@ __global__ __launch_bounds__(256, NI == 10 ? 4 : 1) void k_select(const double* 
       }
       const uint64_t mi = wave_incl_scan<uint64_t>(lm, lane);
       const uint32_t ci = wave_incl_scan<uint32_t>(lc, lane);
-      const uint64_t mtot = __shfl(mi, 63);
+      const uint64_t mtot = lane_value(mi, 63);
       if (level == 0 && useP && mtot < needP) {   // total mass never reaches p: keep all
         all = true;
         break;
@@ -462,26 +498,29 @@ __global__ __launch_bounds__(256, NI == 10 ? 4 : 1) void k_select(const double* 
           }
         }
         const uint64_t vp = __ballot(myP >= 0), vf = __ballot(myF >= 0);
-        if (vp) bP = __shfl(myP, __ffsll((unsigned long long)vp) - 1);
-        if (vf) bF = __shfl(myF, __ffsll((unsigned long long)vf) - 1);
+        if (vp) bP = lane_value(myP, __ffsll((unsigned long long)vp) - 1);
+        if (vf) bF = lane_value(myF, __ffsll((unsigned long long)vf) - 1);
       }
       const int bs = max(bP, bF);
       if (bP < bs) useP = false;
       if (bF < bs) useF = false;
-      // mass / count strictly above bin bs
-      uint64_t ma = 0;
-      uint32_t ca = 0;
+      // mass / count strictly above bin bs: the lanes before the one owning
+      // bs (its exclusive prefix) plus that lane's bins before bs
+      uint64_t ma;
+      uint32_t ca;
+      {
+        uint64_t pm = mi - lm;
+        uint32_t pc = ci - lc;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        if (lane * 4 + t < bs) {
-          ma += bm[t];
-          ca += bc[t];
+        for (int t = 0; t < 4; ++t) {
+          if (lane * 4 + t < bs) {
+            pm += bm[t];
+            pc += bc[t];
+          }
         }
+        ma = bs > 0 ? lane_value(pm, bs >> 2) : 0;
+        ca = bs > 0 ? lane_value(pc, bs >> 2) : 0;
       }
-      ma = wave_incl_scan<uint64_t>(ma, lane);
-      ca = wave_incl_scan<uint32_t>(ca, lane);
-      ma = __shfl(ma, 63);
-      ca = __shfl(ca, 63);
       if (useP) needP -= ma;
       if (useF) needF -= (int)ca;
       kAbove += (int)ca;
@@ -519,7 +558,7 @@ __global__ __launch_bounds__(256, NI == 10 ? 4 : 1) void k_select(const double* 
       }
       const int tF = useF ? needF : 0;
       const int t = max(max(tP, tF), 1);
-      thr = __shfl(kk, t - 1);
+      thr = lane_value(kk, t - 1);
       kept = kAbove + t;
     }
   }
