@@ -291,8 +291,10 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, 
     wave_sync_lds();
   };
   double m_run = -INFINITY, s_run = 0.0;
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const KTile nxt = kfetch(kt + 1);
+  // The products of tile kt run on the matrix cores while the same wave does
+  // the fp64 log-sum-exp of tile kt-1 (independent work, so the two overlap
+  // inside the wave): the loop carries the previous tile's accumulator.
+  auto products = [&](int kt) __attribute__((always_inline)) -> f64x4 {
     const double2* ks = (const double2*)&ks_lds[kt & 1][l16][QD * g];
     f64x4 acc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
@@ -301,9 +303,16 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, 
       acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a.x, qv[2 * c], acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a.y, qv[2 * c + 1], acc, 0, 0, 0);
     }
-    // acc[i]: key kt*16 + g + 4*i, query l16 (fp64 16x16x4 accumulator layout)
+    return acc;
+  };
+  // acc[i]: key kt*16 + g + 4*i, query l16 (fp64 16x16x4 accumulator layout).
+  // The exponentials are taken against the new running max before the
+  // (rare, per lane) rescale, and added after it in the same order as a
+  // rescale-first loop would: the same bits, with the vector work in one
+  // branch-free stretch.
+  auto lse = [&](int kt, const f64x4& acc) __attribute__((always_inline)) {
     if (!SUB) {
-      double yv[4];
+      double yv[4], ev[4];
       double tmax = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -311,13 +320,19 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, 
         yv[i] = j < n_blk ? acc[i] * scale : -INFINITY;
         tmax = fmax(tmax, yv[i]);
       }
+      const double m_new = fmax(m_run, tmax);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const double e = exp(yv[i] - m_new);
+        ev[i] = m_new > -INFINITY ? e : 0.0;
+      }
       if (tmax > m_run) {   // rescale only when the running max grows
         s_run *= exp(m_run - tmax);
         m_run = tmax;
       }
       if (m_run > -INFINITY) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s_run += exp(yv[i] - m_run);
+        for (int i = 0; i < 4; ++i) s_run += ev[i];
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) yt[w][l16][(kt % TPF) * 16 + g + 4 * i] = yv[i];
@@ -335,7 +350,8 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, 
         // the max first, then one exponential per sub-block
         double c = fmax(v0, v1);
         c = pair_max<32>(pair_max<16>(c));
-        double e = c > -INFINITY ? exp(v0 - c) + exp(v1 - c) : 0.0;
+        const double e2 = exp(v0 - c) + exp(v1 - c);
+        double e = c > -INFINITY ? e2 : 0.0;
         e = pair_sum<32>(pair_sum<16>(e));
         cb[b2] = c, eb[b2] = e;
       }
@@ -343,18 +359,35 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, 
       // kt*2 and group 1 block kt*2+1: one log each, its logit written out and
       // counted in the row statistics (groups merged at the end)
       const double cm = g == 1 ? cb[1] : cb[0], em = g == 1 ? eb[1] : eb[0];
-      const double yo = g < 2 && cm > -INFINITY ? cm + log(em) : -INFINITY;
+      const double lg = cm + log(em);
+      const double yo = g < 2 && cm > -INFINITY ? lg : -INFINITY;
+      const double m_new = fmax(m_run, yo);
+      const double er = exp(yo - m_new);
       if (yo > m_run) {
         s_run *= exp(m_run - yo);
         m_run = yo;
       }
-      if (yo > -INFINITY) s_run += exp(yo - m_run);
+      if (yo > -INFINITY) s_run += er;
       if (g < 2) yt[w][l16][(kt % TPF) * 2 + g] = yo;
     }
-    if (kt % TPF == TPF - 1 || kt == ntiles - 1) flush(kt);
-    kstore((kt + 1) & 1, nxt);
+  };
+  f64x4 acc_prev = products(0);
+  {
+    const KTile nxt = kfetch(1);
+    kstore(1, nxt);
     __syncthreads();
   }
+  for (int kt = 1; kt < ntiles; ++kt) {
+    const KTile nxt = kfetch(kt + 1);
+    const f64x4 acc = products(kt);
+    lse(kt - 1, acc_prev);
+    if ((kt - 1) % TPF == TPF - 1) flush(kt - 1);
+    kstore((kt + 1) & 1, nxt);
+    __syncthreads();
+    acc_prev = acc;
+  }
+  lse(ntiles - 1, acc_prev);
+  flush(ntiles - 1);
   // merge (max, sum) over the four lane groups that share query l16
 #pragma unroll
   for (int o = 16; o <= 32; o <<= 1) {
