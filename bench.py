@@ -252,6 +252,19 @@ def main():
     stage = {n: np.array([e[j].elapsed_time(e[j + 1]) for e in evs]) for j, n in enumerate(names)}
     st_mean = {n: float(x.mean()) for n, x in stage.items()}
     st_med = {n: float(np.median(x)) for n, x in stage.items()}
+    per_call = np.array([e[0].elapsed_time(e[len(names)]) for e in evs])
+
+    # cold caches: a 512 MB scratch write (twice the 256 MB Infinity Cache,
+    # far above the L2s) between calls, each call timed on its own
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    cold = []
+    for i in range(min(args.steps, 10)):
+        scratch.fill_(i & 0xFF)
+        ec = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+        call(ec)
+        torch.cuda.synchronize()
+        cold.append(ec[0].elapsed_time(ec[len(names)]))
+    del scratch
 
     # the same call captured once in a HIP graph and replayed (fused form only)
     graph_ms = None
@@ -408,6 +421,10 @@ def main():
                     "max": round(float(dens.max()), 4)},
         "stage_ms_mean": {n: round(x, 4) for n, x in st_mean.items()},
         "stage_ms_median": {n: round(x, 4) for n, x in st_med.items()},
+        "call_ms": {"median": round(float(np.median(per_call)), 4), "min": round(float(per_call.min()), 4),
+                    "p90": round(float(np.percentile(per_call, 90)), 4)},
+        "cold_cache_call_ms": {"median": round(float(np.median(cold)), 4), "min": round(float(np.min(cold)), 4),
+                               "calls": len(cold), "scratch_mb_between_calls": 512},
         "core_ms": round(st_mean["select"] + st_mean["attention"], 4),
         "graph_ms_per_call": round(graph_ms, 4) if graph_ms is not None else None,
         "hbm_gbs": {"permute_rows": round(perm_bytes / (st_mean["permute_q"] * 1e-3) / 1e9, 1),
