@@ -342,8 +342,8 @@ def main():
             fva.fva_attention_lse(plan, bufs.q, bufs.k, bufs.vt, bufs.row_ptr, bufs.col_idx, bufs.o, tb.o32, tb.lse)
         e_b[1].record()
         for _ in range(args.steps):
-            fva.fva_attention_backward(plan, bufs.q, tb.q_vt, bufs.k, tb.k_vt, tb.v, tb.o32, tb.lse, tb.do,
-                                       tb.do_vt, bufs.row_ptr, bufs.col_idx, tb.dq, tb.dk, tb.dv)
+            fva.fva_attention_backward(plan, bufs.q, bufs.k, tb.v, tb.o32, tb.lse, tb.do, tb.do_vt,
+                                       bufs.row_ptr, bufs.col_idx, tb.dq, tb.dk, tb.dv)
         e_b[2].record()
         for _ in range(args.steps):
             fva.attention_backward_call(plan, qd, kd, vd, dod, dq, dk, dv, bufs, tb)

@@ -75,9 +75,7 @@ __global__ __launch_bounds__(256) void k_bits_transpose(const uint64_t* __restri
 // ------------------------------------------------------------------ kernels
 struct BwdArgs {
   const uint16_t* q;        // [B*H, n_pad, D] rows
-  const uint16_t* qt;       // Q in the VT layout
   const uint16_t* k;        // rows
-  const uint16_t* kt;       // K in the VT layout
   const uint16_t* v;        // rows
   const float* o32;         // forward output before rounding, rows
   const float* lse;         // [B*H, n_pad] log2-sum-exp2 of the scaled scores (forward pass)
@@ -202,6 +200,63 @@ __device__ __forceinline__ void tile_offsets(int w, int lane, uint32_t* roff, ui
   }
 }
 
+// Transposed LDS reads (ds_read_b64_tr_b16).  In each group of 16 lanes,
+// every lane names 8 bytes (4 bf16) of LDS; lane j of the group receives, as
+// its element e (e = 0..3), element j % 4 of what lane 4 e + j / 4 named.  So
+// if source lane s names row r0 + s / 4 at columns c0 + 4 (s % 4)..+3 of a
+// row-major tile, lane j receives column c0 + j of rows r0..r0+3.
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+
+// Lane parts of the transposed-read addresses.  For D = 128 the chunk swizzle
+// kswz is row & 15, and every address tr_operand<128> forms is one of two
+// lane constants (for an even or an odd column-tile term) plus an immediate.
+struct TrBase {
+  uint32_t e, o;
+};
+template <int D>
+__device__ __forceinline__ TrBase tr_base(uint32_t ring_lds, int lane) {
+  if constexpr (D == 128) {
+    const int g = lane >> 4, s = lane & 15, gb = g >> 1;
+    const int rl = 4 * gb + (s >> 2);                              // row within 8
+    const int clow = (2 * (g & 1) + ((s & 3) >> 1)) ^ (s >> 2);   // low bits of the chunk
+    const uint32_t e = ring_lds + rl * 256 + 16 * (4 * gb + clow) + (s & 1) * 8;
+    return TrBase{e, e - 128 * gb};
+  } else {
+    return TrBase{ring_lds, ring_lds};
+  }
+}
+
+// A operand (32 x 16) of a product whose k index runs over the rows of a
+// 32-row, D-column tile in LDS (16-byte chunks swizzled by kswz, as the row
+// tiles of the ring are stored), taken in the key order of the B operand fed
+// from an S-shaped accumulator: lane (i, h) element e holds row
+// 16 ks + 8 (e / 4) + 4 h + e % 4 at column 32 dt + i.  Two transposed reads,
+// one per 4-row run; `tile` is the tile's byte offset inside the ring.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(uint32_t tile, const TrBase& tb, int dt, int ks, int lane) {
+  uint32_t o0, o1;
+  if constexpr (D == 128) {
+    // chunk of column 32 dt + 16 (g&1) + 4 (s&3) in row 16 ks + 8 half + rl:
+    // 4 (X ^ (g >> 1)) + clow with X = dt ^ 2 half
+    const int X0 = dt, X1 = dt ^ 2;
+    o0 = ((X0 & 1) ? tb.o : tb.e) + tile + (16 * ks) * 256 + 64 * X0;
+    o1 = ((X1 & 1) ? tb.o : tb.e) + tile + (16 * ks + 8) * 256 + 64 * X1;
+  } else {
+    const int g = lane >> 4, s = lane & 15;
+    const int d = 32 * dt + 16 * (g & 1) + 4 * (s & 3);
+    const int r0 = 16 * ks + 4 * (g >> 1) + (s >> 2), r1 = r0 + 8;
+    o0 = tb.e + tile + r0 * (D * 2) + (((d >> 3) ^ kswz<D>(r0)) << 4) + ((d & 7) << 1);
+    o1 = tb.e + tile + r1 * (D * 2) + (((d >> 3) ^ kswz<D>(r1)) << 4) + ((d & 7) << 1);
+  }
+  // whole-vector casts: element-wise extraction from the builtin's bf16x4
+  // result is avoided
+  const bf16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(uintptr_t)o0);
+  const bf16x4_t y = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(uintptr_t)o1);
+  const uint2 ux = __builtin_bit_cast(uint2, x), uy = __builtin_bit_cast(uint2, y);
+  return __builtin_bit_cast(bf16x8, make_uint4(ux.x, ux.y, uy.x, uy.y));
+}
+
 // The blocks of group `item` (G consecutive ids from I0, or a pair from the
 // pair table), -1 past the head's last block.  Wave-uniform.
 template <int G>
@@ -245,16 +300,17 @@ __device__ __forceinline__ void group_bits(const uint64_t* bits, int64_t head_ro
 //   dP^T (32 keys x 32 queries) = V_half . dO^T     (dO in registers)
 //   dS^T = P^T * (dP^T - delta),  P^T = exp2(S^T * scale * log2 e - lse)
 //   dQ^T (D x 32 queries) += K^T_half . dS^T        (dS^T straight from the accumulators)
-// K rows, V rows and K^T (VT layout) of each half stream through an
-// NST-stage ring of direct loads, published by one barrier per step.
+// K rows and V rows of each half stream through an NST-stage ring of direct
+// loads, published by one barrier per step; K^T is read from the K rows by
+// transposed LDS reads.
 template <int D, int NST, int G>
 __global__ __launch_bounds__(128 * G, 2) void k_bwd_dq(BwdArgs a) {
   constexpr int NW = 2 * G;
   constexpr int KS = D / 16, DT = D / 32, KCH = D / 8;
   constexpr int HALF = 32 * D * 2;
-  constexpr int STAGE = 3 * HALF;
+  constexpr int STAGE = 2 * HALF;
   constexpr int LPW = HALF / 1024 / NW;  // direct loads per wave per tile
-  constexpr int PW = 3 * LPW;            // per wave per step
+  constexpr int PW = 2 * LPW;            // per wave per step
   static_assert(LPW >= 1 && (HALF / 1024) % NW == 0, "tile loads split evenly over the waves");
   __shared__ __attribute__((aligned(1024))) uint4 ring[NST * STAGE / 16];
   __shared__ int s_item;
@@ -308,7 +364,6 @@ __global__ __launch_bounds__(128 * G, 2) void k_bwd_dq(BwdArgs a) {
   BitWalk iw, cw;
   const char* kbase = (const char*)(a.k + head * D);
   const char* vbase = (const char*)(a.v + head * D);
-  const char* tbase = (const char*)(a.kt + head * D);
   int curJ = 0;
   const int total = union_steps(un_lo, un_hi);   // two halves per union block
   // loads of half u of the walk's next block into ring stage `stage` (a
@@ -316,17 +371,16 @@ __global__ __launch_bounds__(128 * G, 2) void k_bwd_dq(BwdArgs a) {
   auto issue_next = [&](int stage, int u) __attribute__((always_inline)) {
     if (u == 0) curJ = iw.next_known(un_lo, un_hi);
     const int64_t roff0 = ((int64_t)curJ * 64 + 32 * u) * D * 2;
-    const int64_t toff0 = (int64_t)curJ * 64 * D * 2 + u * HALF;
     const uint32_t dst = lds_addr(ring) + stage * STAGE;
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
       const uint32_t o1 = (NW * j + w) * 1024;
       dma16(kbase + roff0, roff[j], dst + o1);
       dma16(vbase + roff0, roff[j], dst + HALF + o1);
-      dma16(tbase + toff0, toff[j], dst + 2 * HALF + o1);
     }
   };
 
+  const TrBase trb = tr_base<D>(lds_addr(ring), lane);
   f32x16 acc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
@@ -360,7 +414,6 @@ __global__ __launch_bounds__(128 * G, 2) void k_bwd_dq(BwdArgs a) {
     if (mh == 0) continue;   // not in this row, or a half of pad keys
     const uint4* kst = ring + kk * (STAGE / 16);
     const uint4* vst = kst + HALF / 16;
-    const uint4* tst = kst + 2 * HALF / 16;
     f32x16 s = {}, dp = {};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -383,10 +436,8 @@ __global__ __launch_bounds__(128 * G, 2) void k_bwd_dq(BwdArgs a) {
     const bf16x8 db1 = __builtin_convertvector(d1, bf16x8);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const int d = 32 * dt + l32;
-      const int sw = vswz(d);
-      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(tst[d * 4 + ((0 + h) ^ sw)]), db0, acc[dt], 0, 0, 0);
-      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(tst[d * 4 + ((2 + h) ^ sw)]), db1, acc[dt], 0, 0, 0);
+      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(kk * STAGE, trb, dt, 0, lane), db0, acc[dt], 0, 0, 0);
+      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(kk * STAGE, trb, dt, 1, lane), db1, acc[dt], 0, 0, 0);
     }
   }
   }
@@ -407,17 +458,17 @@ __global__ __launch_bounds__(128 * G, 2) void k_bwd_dq(BwdArgs a) {
 //   S  (32 queries x 32 keys) = Q_half . K^T,   dP = dO_half . V^T
 //   P = exp2(S * scale * log2 e - lse),  dS = P * (dP - delta)
 //   dV^T (D x 32 keys) += dO^T_half . P,   dK^T += Q^T_half . dS
-// The ring stage holds Q rows, dO rows, Q^T and dO^T (VT layout) of the
-// half, and the half's 32 lse then 32 delta values (each wave brings
-// 256/NW bytes of those).
+// The ring stage holds Q rows, dO rows and dO^T (VT layout) of the half
+// (Q^T is read from the Q rows by transposed LDS reads), and the half's 32
+// lse then 32 delta values (each wave brings 256/NW bytes of those).
 template <int D, int NST, int G>
 __global__ __launch_bounds__(128 * G, G) void k_bwd_dkdv(BwdArgs a) {
   constexpr int NW = 2 * G;
   constexpr int KS = D / 16, DT = D / 32, KCH = D / 8;
   constexpr int HALF = 32 * D * 2;
-  constexpr int STAGE = 4 * HALF + 256;
+  constexpr int STAGE = 3 * HALF + 256;
   constexpr int LPW = HALF / 1024 / NW;
-  constexpr int PW = 4 * LPW + 1;
+  constexpr int PW = 3 * LPW + 1;
   constexpr int LDW = 64 / NW;           // lse/delta floats each wave brings
   static_assert(LPW >= 1 && (HALF / 1024) % NW == 0, "tile loads split evenly over the waves");
   __shared__ __attribute__((aligned(1024))) uint4 ring[NST * STAGE / 16];
@@ -459,7 +510,6 @@ __global__ __launch_bounds__(128 * G, G) void k_bwd_dkdv(BwdArgs a) {
   BitWalk iw, cw;
   const char* qbase = (const char*)(a.q + head * D);
   const char* dbase = (const char*)(a.dout + head * D);
-  const char* qtbase = (const char*)(a.qt + head * D);
   const char* dtbase = (const char*)(a.dot + head * D);
   // floats [LDW w, LDW (w+1)) of the stage's [32 lse | 32 delta]
   const float* lbase = (LDW * w < 32 ? a.lse + LDW * w : (const float*)a.delta + (LDW * w - 32)) + head;
@@ -476,13 +526,13 @@ __global__ __launch_bounds__(128 * G, G) void k_bwd_dkdv(BwdArgs a) {
       const uint32_t o1 = (NW * j + w) * 1024;
       dma16u(qbase + roff0, roff[j], dst + o1);
       dma16u(dbase + roff0, roff[j], dst + HALF + o1);
-      dma16u(qtbase + toff0, toff[j], dst + 2 * HALF + o1);
-      dma16u(dtbase + toff0, toff[j], dst + 3 * HALF + o1);
+      dma16u(dtbase + toff0, toff[j], dst + 2 * HALF + o1);
     }
-    if (lane < LDW / 4) dma16u(lbase + (int64_t)curI * 64 + 32 * u, lane * 16, dst + 4 * HALF + 4 * LDW * w);
+    if (lane < LDW / 4) dma16u(lbase + (int64_t)curI * 64 + 32 * u, lane * 16, dst + 3 * HALF + 4 * LDW * w);
     ++issued;
   };
 
+  const TrBase trb = tr_base<D>(lds_addr(ring), lane);
   f32x16 dk[DT], dv[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dk[dt] = dv[dt] = f32x16{};
@@ -509,9 +559,9 @@ __global__ __launch_bounds__(128 * G, G) void k_bwd_dkdv(BwdArgs a) {
     if (qm == 0) continue;   // not in this column, pad queries, or a wave of pad keys
     const uint4* qst = ring + (st % NST) * (STAGE / 16);
     const uint4* dst_ = qst + HALF / 16;
-    const uint4* qtst = qst + 2 * HALF / 16;
-    const uint4* dtst = qst + 3 * HALF / 16;
-    const float* lds_l = (const float*)(qst + 4 * HALF / 16);
+    const uint4* dtst = qst + 2 * HALF / 16;
+    const float* lds_l = (const float*)(qst + 3 * HALF / 16);
+    const uint32_t qtile = (uint32_t)((st % NST) * STAGE);   // Q rows: Q^T by transposed reads
     // Two phases keep the live registers low enough for two waves per
     // SIMD: S -> P -> dV, then dP -> dS -> dK (P kept in fp32 between).
     // element r of S, dP: query 8*(r/4) + 4*h + r%4 of this half, key l32
@@ -559,10 +609,8 @@ __global__ __launch_bounds__(128 * G, G) void k_bwd_dkdv(BwdArgs a) {
       const bf16x8 db0 = __builtin_convertvector(ds.lo, bf16x8), db1 = __builtin_convertvector(ds.hi, bf16x8);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const int d = 32 * dt + l32;
-        const int sw = vswz(d);
-        dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qtst[d * 4 + ((0 + h) ^ sw)]), db0, dk[dt], 0, 0, 0);
-        dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qtst[d * 4 + ((2 + h) ^ sw)]), db1, dk[dt], 0, 0, 0);
+        dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(qtile, trb, dt, 0, lane), db0, dk[dt], 0, 0, 0);
+        dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(qtile, trb, dt, 1, lane), db1, dk[dt], 0, 0, 0);
       }
     }
   }
@@ -588,13 +636,14 @@ __global__ __launch_bounds__(128 * G, G) void k_bwd_dkdv(BwdArgs a) {
 //        stage: Q rows, dO^T (VT layout), 32 lse
 //   dK:  S = Q_half . K^T,  dP = dO_half . V^T,  P,  dS = P (dP - delta),
 //        dK^T += Q^T_half . dS
-//        stage: Q rows, dO rows, Q^T (VT layout), 32 lse, 32 delta
+//        stage: Q rows, dO rows, 32 lse, 32 delta (Q^T by transposed reads
+//        of the Q rows)
 template <int D, int NST, int G, bool DK, int OCC>
 __global__ __launch_bounds__(128 * G, OCC) void k_bwd_dkv(BwdArgs a) {
   constexpr int NW = 2 * G;
   constexpr int KS = D / 16, DT = D / 32, KCH = D / 8;
   constexpr int HALF = 32 * D * 2;
-  constexpr int NT = DK ? 3 : 2;          // 32-row tiles per stage
+  constexpr int NT = 2;                   // 32-row tiles per stage
   constexpr int LDB = DK ? 256 : 128;     // lse (and delta) bytes per stage
   constexpr int STAGE = NT * HALF + LDB;
   constexpr int LPW = HALF / 1024 / NW;
@@ -640,7 +689,6 @@ __global__ __launch_bounds__(128 * G, OCC) void k_bwd_dkv(BwdArgs a) {
   BitWalk iw, cw;
   const char* qbase = (const char*)(a.q + head * D);
   const char* dbase = (const char*)(a.dout + head * D);
-  const char* qtbase = (const char*)(a.qt + head * D);
   const char* dtbase = (const char*)(a.dot + head * D);
   // floats [LDW w, LDW (w+1)) of the stage's [32 lse | 32 delta]
   const float* lbase = (LDW * w < 32 ? a.lse + LDW * w : (const float*)a.delta + (LDW * w - 32)) + head;
@@ -656,12 +704,8 @@ __global__ __launch_bounds__(128 * G, OCC) void k_bwd_dkv(BwdArgs a) {
     for (int j = 0; j < LPW; ++j) {
       const uint32_t o1 = (NW * j + w) * 1024;
       dma16u(qbase + roff0, roff[j], dst + o1);
-      if (DK) {
-        dma16u(dbase + roff0, roff[j], dst + HALF + o1);
-        dma16u(qtbase + toff0, toff[j], dst + 2 * HALF + o1);
-      } else {
-        dma16u(dtbase + toff0, toff[j], dst + HALF + o1);
-      }
+      if (DK) dma16u(dbase + roff0, roff[j], dst + HALF + o1);
+      else dma16u(dtbase + toff0, toff[j], dst + HALF + o1);
     }
     if (lane < LDW / 4) dma16u(lbase + (int64_t)curI * 64 + 32 * u, lane * 16, dst + NT * HALF + 4 * LDW * w);
     ++issued;
@@ -672,18 +716,17 @@ __global__ __launch_bounds__(128 * G, OCC) void k_bwd_dkv(BwdArgs a) {
   auto issue_at = [&](int stage, int u) __attribute__((always_inline)) {
     if (u == 0) curI = iw.next_known(un_lo, un_hi);
     const int64_t roff0 = ((int64_t)curI * 64 + 32 * u) * D * 2;
-    const int64_t toff0 = (int64_t)curI * 64 * D * 2 + u * HALF;
     const uint32_t dst = lds_addr(ring) + stage * STAGE;
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
       const uint32_t o1 = (NW * j + w) * 1024;
       dma16(qbase + roff0, roff[j], dst + o1);
       dma16(dbase + roff0, roff[j], dst + HALF + o1);
-      dma16(qtbase + toff0, toff[j], dst + 2 * HALF + o1);
     }
     if (lane < LDW / 4) dma16(lbase + (int64_t)curI * 64 + 32 * u, lane * 16, dst + NT * HALF + 4 * LDW * w);
   };
 
+  const TrBase trb = tr_base<D>(lds_addr(ring), lane);
   f32x16 acc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
@@ -724,7 +767,6 @@ __global__ __launch_bounds__(128 * G, OCC) void k_bwd_dkv(BwdArgs a) {
     if (qm == 0) continue;   // not in this column, pad queries, or a wave of pad keys
     const uint4* qst = ring + (DK ? kk : st % NST) * (STAGE / 16);
     const uint4* t1 = qst + HALF / 16;       // dO rows (dK) or dO^T (dV)
-    const uint4* t2 = qst + 2 * HALF / 16;   // Q^T (dK)
     const float* lds_l = (const float*)(qst + NT * HALF / 16);
     // element r: query 8*(r/4) + 4*h + r%4 of this half, key l32
     typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -750,13 +792,16 @@ __global__ __launch_bounds__(128 * G, OCC) void k_bwd_dkv(BwdArgs a) {
       }
     }
     const bf16x8 xb0 = __builtin_convertvector(x.lo, bf16x8), xb1 = __builtin_convertvector(x.hi, bf16x8);
-    const uint4* at = DK ? t2 : t1;   // Q^T (dK) or dO^T (dV)
+    // dK: Q^T by transposed reads of the stage's Q rows; dV: the dO^T tile
+    const uint32_t qtile = (uint32_t)((DK ? kk : st % NST) * STAGE);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const int d = 32 * dt + l32;
       const int sw = vswz(d);
-      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(at[d * 4 + ((0 + h) ^ sw)]), xb0, acc[dt], 0, 0, 0);
-      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(at[d * 4 + ((2 + h) ^ sw)]), xb1, acc[dt], 0, 0, 0);
+      const bf16x8 a0 = DK ? tr_operand<D>(qtile, trb, dt, 0, lane) : as_bf16x8(t1[d * 4 + ((0 + h) ^ sw)]);
+      const bf16x8 a1 = DK ? tr_operand<D>(qtile, trb, dt, 1, lane) : as_bf16x8(t1[d * 4 + ((2 + h) ^ sw)]);
+      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, xb0, acc[dt], 0, 0, 0);
+      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, xb1, acc[dt], 0, 0, 0);
     }
   }
   }
@@ -872,13 +917,12 @@ extern "C" int fva_mask_transpose(fva_plan_t plan, const int32_t* row_ptr, const
   return fva_after_launch(stream, "fva_mask_transpose");
 }
 
-extern "C" int fva_attention_backward(fva_plan_t plan, const void* q_perm, const void* q_vt, const void* k_perm,
-                                      const void* k_vt, const void* v_perm, const float* o32, const float* lse,
-                                      const void* do_perm, const void* do_vt, const int32_t* row_ptr,
-                                      const int32_t* col_idx, void* dq_perm, void* dk_perm, void* dv_perm,
-                                      hipStream_t stream) {
+extern "C" int fva_attention_backward(fva_plan_t plan, const void* q_perm, const void* k_perm, const void* v_perm,
+                                      const float* o32, const float* lse, const void* do_perm, const void* do_vt,
+                                      const int32_t* row_ptr, const int32_t* col_idx, void* dq_perm, void* dk_perm,
+                                      void* dv_perm, hipStream_t stream) {
   if (!plan) return fva_fail(FVA_EINVAL, "plan is NULL");
-  if (!q_perm || !q_vt || !k_perm || !k_vt || !v_perm || !o32 || !lse || !do_perm || !do_vt)
+  if (!q_perm || !k_perm || !v_perm || !o32 || !lse || !do_perm || !do_vt)
     return fva_fail(FVA_EINVAL, "input pointer is NULL");
   if (!row_ptr || !col_idx) return fva_fail(FVA_EINVAL, "row_ptr / col_idx is NULL");
   if (!dq_perm || !dk_perm || !dv_perm) return fva_fail(FVA_EINVAL, "gradient pointer is NULL");
@@ -888,9 +932,7 @@ extern "C" int fva_attention_backward(fva_plan_t plan, const void* q_perm, const
   launch_lists(plan, row_ptr, col_idx, stream);
   BwdArgs a{};
   a.q = (const uint16_t*)q_perm;
-  a.qt = (const uint16_t*)q_vt;
   a.k = (const uint16_t*)k_perm;
-  a.kt = (const uint16_t*)k_vt;
   a.v = (const uint16_t*)v_perm;
   a.o32 = o32;
   a.lse = lse;
@@ -939,7 +981,7 @@ extern "C" int fva_attention_backward(fva_plan_t plan, const void* q_perm, const
                        ok);
   }
   if (d.head_dim == 128) {
-    bwd_launch(k_bwd_dq<128, 3, GQ>, 128 * GQ, GQ, a, plan, cq, oq, pq, stream);
+    bwd_launch(k_bwd_dq<128, 4, GQ>, 128 * GQ, GQ, a, plan, cq, oq, pq, stream);
     if (kmode == 0) {
       if (dv_occ == 3) bwd_launch(k_bwd_dkv<128, 3, 2, false, 3>, 256, 2, a, plan, cv, ok, pk, stream);
       else bwd_launch(k_bwd_dkv<128, 3, 2, false, 2>, 256, 2, a, plan, cv, ok, pk, stream);
@@ -951,7 +993,7 @@ extern "C" int fva_attention_backward(fva_plan_t plan, const void* q_perm, const
       bwd_launch(k_bwd_dkdv<128, 2, 1>, 128, 1, a, plan, cv, ok, pk, stream);
     }
   } else {
-    bwd_launch(k_bwd_dq<64, 3, GQ>, 128 * GQ, GQ, a, plan, cq, oq, pq, stream);
+    bwd_launch(k_bwd_dq<64, 4, GQ>, 128 * GQ, GQ, a, plan, cq, oq, pq, stream);
     if (kmode == 0) {
       if (dv_occ == 3) bwd_launch(k_bwd_dkv<64, 3, 2, false, 3>, 256, 2, a, plan, cv, ok, pk, stream);
       else bwd_launch(k_bwd_dkv<64, 3, 2, false, 2>, 256, 2, a, plan, cv, ok, pk, stream);

@@ -79,7 +79,7 @@ def lib() -> ctypes.CDLL:
             "fva_mask_accumulate": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp]),
             "fva_mask_from_counts": (c_i32, [c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp]),
             "fva_attention_lse": (c_i32, [c_vp] * 10),
-            "fva_attention_backward": (c_i32, [c_vp] * 16),
+            "fva_attention_backward": (c_i32, [c_vp] * 14),
             "fva_mask_transpose": (c_i32, [c_vp] * 6),
             "fva_last_error": (ctypes.c_char_p, []),
         }
@@ -351,10 +351,10 @@ def fva_attention_lse(plan: Plan, q_perm, k_perm, vt_perm, row_ptr, col_idx, o_p
                                    _ptr(col_idx), _ptr(o_perm), _ptr(o32), _ptr(lse), _stream(stream)))
 
 
-def fva_attention_backward(plan: Plan, q_perm, q_vt, k_perm, k_vt, v_perm, o32, lse, do_perm, do_vt,
+def fva_attention_backward(plan: Plan, q_perm, k_perm, v_perm, o32, lse, do_perm, do_vt,
                            row_ptr, col_idx, dq_perm, dk_perm, dv_perm, stream=None):
     shp = plan.perm_shape()
-    for t, n in ((q_perm, "q_perm"), (q_vt, "q_vt"), (k_perm, "k_perm"), (k_vt, "k_vt"), (v_perm, "v_perm"),
+    for t, n in ((q_perm, "q_perm"), (k_perm, "k_perm"), (v_perm, "v_perm"),
                  (do_perm, "do_perm"), (do_vt, "do_vt"), (dq_perm, "dq_perm"),
                  (dk_perm, "dk_perm"), (dv_perm, "dv_perm")):
         if t.numel() != math.prod(shp) or t.dtype != plan.torch_dtype or not t.is_contiguous():
@@ -364,7 +364,7 @@ def fva_attention_backward(plan: Plan, q_perm, q_vt, k_perm, k_vt, v_perm, o32, 
     _expect(row_ptr, (plan.n_rows + 1,), torch.int32, "row_ptr")
     if col_idx.dtype != torch.int32:
         raise ValueError("col_idx must be int32")
-    _check(lib().fva_attention_backward(plan.handle, _ptr(q_perm), _ptr(q_vt), _ptr(k_perm), _ptr(k_vt),
+    _check(lib().fva_attention_backward(plan.handle, _ptr(q_perm), _ptr(k_perm),
                                         _ptr(v_perm), _ptr(o32), _ptr(lse), _ptr(do_perm), _ptr(do_vt),
                                         _ptr(row_ptr), _ptr(col_idx), _ptr(dq_perm), _ptr(dk_perm), _ptr(dv_perm),
                                         _stream(stream)))
@@ -427,15 +427,15 @@ def attention_call(plan: Plan, q, k, v, out, p, k_min, bufs: Buffers, slack="non
 
 
 class TrainBuffers:
-    """Extra block-order buffers of a training call: the VT layouts of Q, K
-    and dO, V and dO in rows, the fp32 output and per-query log-sum-exp of
-    the forward pass, the gradients."""
+    """Extra block-order buffers of a training call: V and dO in rows, dO in
+    the VT layout, the fp32 output and per-query log-sum-exp of the forward
+    pass, the gradients."""
 
     def __init__(self, plan: Plan):
         dev = torch.device("cuda")
         shp = plan.perm_shape()
         mk = lambda: torch.empty(shp, dtype=plan.torch_dtype, device=dev)
-        self.q_vt, self.k_vt, self.v, self.do, self.do_vt = mk(), mk(), mk(), mk(), mk()
+        self.v, self.do, self.do_vt = mk(), mk(), mk()
         self.dq, self.dk, self.dv = mk(), mk(), mk()
         self.lse = torch.empty(shp[:3], dtype=torch.float32, device=dev)
         self.o32 = torch.empty(shp, dtype=torch.float32, device=dev)
@@ -457,12 +457,10 @@ def attention_forward_train(plan: Plan, q, k, v, out, p, k_min, bufs: Buffers, t
 def attention_backward_call(plan: Plan, q, k, v, dout, dq, dk, dv, bufs: Buffers, tb: TrainBuffers, stream=None):
     """Backward pass after attention_forward_train on the same buffers:
     raster dO in, raster dQ, dK, dV out (same lists as the forward pass)."""
-    fva_permute(plan, q, tb.q_vt, LAYOUT_VT, stream)
-    fva_permute(plan, k, tb.k_vt, LAYOUT_VT, stream)
     fva_permute(plan, v, tb.v, LAYOUT_ROWS, stream)
     fva_permute(plan, dout, tb.do, LAYOUT_ROWS, stream)
     fva_permute(plan, dout, tb.do_vt, LAYOUT_VT, stream)
-    fva_attention_backward(plan, bufs.q, tb.q_vt, bufs.k, tb.k_vt, tb.v, tb.o32, tb.lse, tb.do, tb.do_vt,
+    fva_attention_backward(plan, bufs.q, bufs.k, tb.v, tb.o32, tb.lse, tb.do, tb.do_vt,
                            bufs.row_ptr, bufs.col_idx, tb.dq, tb.dk, tb.dv, stream)
     fva_unpermute(plan, tb.dq, dq, stream)
     fva_unpermute(plan, tb.dk, dk, stream)

@@ -306,7 +306,8 @@ int fva_attention_lse(fva_plan_t plan, const void* q_perm, const void* k_perm, c
  *   dQ = dS K / sqrt(D),  dK = dS^T Q / sqrt(D),  dV = P^T dO
  * Arguments (block order, bf16, B*H heads of N_pad tokens):
  *   q_perm, k_perm, v_perm, do_perm   FVA_LAYOUT_ROWS (fva_permute);
- *   q_vt, k_vt, do_vt                 the same tensors in FVA_LAYOUT_VT;
+ *   do_vt                             dO in FVA_LAYOUT_VT (K^T and Q^T are
+ *                                     read from the row layouts);
  *   o32, lse                          outputs of fva_attention_lse on the
  *                                     same Q, K, V and lists;
  *   row_ptr, col_idx                  the forward pass's CSR (set semantics);
@@ -316,11 +317,10 @@ int fva_attention_lse(fva_plan_t plan, const void* q_perm, const void* k_perm, c
  * rounded to bf16 as operands, the gradients to bf16 at the end.  Uses the
  * plan's workspace (not safe to overlap with other calls on the plan).
  * Errors: FVA_EINVAL for NULL pointers, FVA_EUNSUPPORTED for fp32 plans. */
-int fva_attention_backward(fva_plan_t plan, const void* q_perm, const void* q_vt, const void* k_perm,
-                           const void* k_vt, const void* v_perm, const float* o32, const float* lse,
-                           const void* do_perm, const void* do_vt, const int32_t* row_ptr,
-                           const int32_t* col_idx, void* dq_perm, void* dk_perm, void* dv_perm,
-                           hipStream_t stream);
+int fva_attention_backward(fva_plan_t plan, const void* q_perm, const void* k_perm, const void* v_perm,
+                           const float* o32, const float* lse, const void* do_perm, const void* do_vt,
+                           const int32_t* row_ptr, const int32_t* col_idx, void* dq_perm, void* dk_perm,
+                           void* dv_perm, hipStream_t stream);
 
 /* Transposed block lists: row (b, h, J) of the output lists, ascending, the
  * query blocks I whose row (b, h, I) of the input lists holds J (input rows

@@ -80,10 +80,9 @@ def _train(w, lists, dout_scale=1.0):
     shp = plan.perm_shape()
     mk = lambda: torch.empty(shp, dtype=plan.torch_dtype, device="cuda")
     qd, kd, vd, dod = (to_dev(x, w.dtype) for x in (q, k, v, do))
-    qp, kp, vt, o, qvt, kvt, vp, dop, dovt, dq, dk, dv = (mk() for _ in range(12))
+    qp, kp, vt, o, vp, dop, dovt, dq, dk, dv = (mk() for _ in range(10))
     for src, dst, lay in ((qd, qp, fva.LAYOUT_ROWS), (kd, kp, fva.LAYOUT_ROWS), (vd, vt, fva.LAYOUT_VT),
-                          (qd, qvt, fva.LAYOUT_VT), (kd, kvt, fva.LAYOUT_VT), (vd, vp, fva.LAYOUT_ROWS),
-                          (dod, dop, fva.LAYOUT_ROWS), (dod, dovt, fva.LAYOUT_VT)):
+                          (vd, vp, fva.LAYOUT_ROWS), (dod, dop, fva.LAYOUT_ROWS), (dod, dovt, fva.LAYOUT_VT)):
         fva.fva_permute(plan, src, dst, lay)
     rp, ci = _csr(lists)
     rpd, cid = _dev_i32(rp), _dev_i32(ci if len(ci) else np.zeros(1))
@@ -92,7 +91,7 @@ def _train(w, lists, dout_scale=1.0):
     fva.fva_attention_lse(plan, qp, kp, vt, rpd, cid, o, o32, lse)
     for g in (dq, dk, dv):
         g.fill_(float("nan"))   # every element must be written
-    fva.fva_attention_backward(plan, qp, qvt, kp, kvt, vp, o32, lse, dop, dovt, rpd, cid, dq, dk, dv)
+    fva.fva_attention_backward(plan, qp, kp, vp, o32, lse, dop, dovt, rpd, cid, dq, dk, dv)
     torch.cuda.synchronize()
     f64 = lambda t: t.float().cpu().numpy().astype(np.float64)
     ref_in = [O.permute(synth.to_f64(x, w.dtype), opl) for x in (q, k, v, do)]
@@ -198,10 +197,10 @@ def test_backward_rejects_fp32_plans_and_null():
     rp = torch.zeros(plan.n_rows + 1, dtype=torch.int32, device="cuda")
     ci = torch.zeros(1, dtype=torch.int32, device="cuda")
     with pytest.raises(fva.FvaError):
-        fva.fva_attention_backward(plan, t, t, t, t, t, t, lse, t, t, rp, ci, t, t, t)
+        fva.fva_attention_backward(plan, t, t, t, t, lse, t, t, rp, ci, t, t, t)
     with pytest.raises(fva.FvaError):
         fva.fva_attention_lse(plan, t, t, t, rp, ci, t, t, lse)
-    rc = fva.lib().fva_attention_backward(plan.handle, *([None] * 15))
+    rc = fva.lib().fva_attention_backward(plan.handle, *([None] * 13))
     assert rc == fva.FVA_EINVAL
 
 
