@@ -35,7 +35,7 @@ struct fva_plan_s {
   double* kbar;       // [B*H*n_blk*(n_sub or 1)*D] pooled K (per sub-block), fp64
   double* ybuf;       // [B*H*n_blk*n_blk] block logits, fp64
   float* sbuf;        // [B*H*n_blk*n_blk] fp32 scores the selection read
-  double2* rowstat;   // [n_rows] (max logit, sum of exp), fp64
+  double2* rowstat;   // [n_rows] row max of the block logits in .x, fp64
   int32_t* rowcnt;    // [n_rows] kept blocks per row
   uint64_t* rowmask;  // [n_rows*nw] kept-block bitmask per row
   int32_t* headcnt;   // [B*H]

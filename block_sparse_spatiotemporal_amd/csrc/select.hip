@@ -207,7 +207,7 @@ __global__ __launch_bounds__(64) void k_pool_sub(const T* __restrict__ k, double
 // ------------------------------------------------------------------ score
 // Block logits Y[bh, i, j] = q_bar_i . k_bar_j / sqrt(D) in fp64 (with
 // sub-blocks: the log-sum-exp over the non-empty sub-blocks of j, which makes
-// exp(Y) the sum of the sub-block terms), plus per-row (max, sum exp(y - max)).
+// exp(Y) the sum of the sub-block terms), plus the row max of Y.
 // fp64 matrix cores (v_mfma_f64_16x16x4_f64).  Workgroup = 4 waves, each
 // wave one 16-query tile; every wave sweeps all 16-key tiles, computing
 // Z^T = Kbar . Qbar^T so that lane l owns query l%16 and keys l/16 + 4*i.
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, 
       if (j < n_blk) yw[(int64_t)q * n_blk + j] = yt[w][q][lane];
     wave_sync_lds();
   };
-  double m_run = -INFINITY, s_run = 0.0;
+  double m_run = -INFINITY;
   // The products of tile kt run on the matrix cores while the same wave does
   // the fp64 log-sum-exp of tile kt-1 (independent work, so the two overlap
   // inside the wave): the loop carries the previous tile's accumulator.
@@ -306,33 +306,17 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, 
     return acc;
   };
   // acc[i]: key kt*16 + g + 4*i, query l16 (fp64 16x16x4 accumulator layout).
-  // The exponentials are taken against the new running max before the
-  // (rare, per lane) rescale, and added after it in the same order as a
-  // rescale-first loop would: the same bits, with the vector work in one
-  // branch-free stretch.
+  // Only the row max is kept here: the selection kernel takes every
+  // exponential of the row anyway and sums them there, so the score kernel's
+  // fp64 vector work (which does not overlap its fp64 products) stays small.
   auto lse = [&](int kt, const f64x4& acc) __attribute__((always_inline)) {
     if (!SUB) {
-      double yv[4], ev[4];
-      double tmax = -INFINITY;
+      double yv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = kt * 16 + g + 4 * i;
         yv[i] = j < n_blk ? acc[i] * scale : -INFINITY;
-        tmax = fmax(tmax, yv[i]);
-      }
-      const double m_new = fmax(m_run, tmax);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const double e = exp(yv[i] - m_new);
-        ev[i] = m_new > -INFINITY ? e : 0.0;
-      }
-      if (tmax > m_run) {   // rescale only when the running max grows
-        s_run *= exp(m_run - tmax);
-        m_run = tmax;
-      }
-      if (m_run > -INFINITY) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s_run += ev[i];
+        m_run = fmax(m_run, yv[i]);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) yt[w][l16][(kt % TPF) * 16 + g + 4 * i] = yv[i];
@@ -357,17 +341,11 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, 
       }
       // every lane group now holds both blocks' (max, sum); group 0 owns block
       // kt*2 and group 1 block kt*2+1: one log each, its logit written out and
-      // counted in the row statistics (groups merged at the end)
+      // counted in the row max (groups merged at the end)
       const double cm = g == 1 ? cb[1] : cb[0], em = g == 1 ? eb[1] : eb[0];
       const double lg = cm + log(em);
       const double yo = g < 2 && cm > -INFINITY ? lg : -INFINITY;
-      const double m_new = fmax(m_run, yo);
-      const double er = exp(yo - m_new);
-      if (yo > m_run) {
-        s_run *= exp(m_run - yo);
-        m_run = yo;
-      }
-      if (yo > -INFINITY) s_run += er;
+      m_run = fmax(m_run, yo);
       if (g < 2) yt[w][l16][(kt % TPF) * 2 + g] = yo;
     }
   };
@@ -388,15 +366,9 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, 
   }
   lse(ntiles - 1, acc_prev);
   flush(ntiles - 1);
-  // merge (max, sum) over the four lane groups that share query l16
-#pragma unroll
-  for (int o = 16; o <= 32; o <<= 1) {
-    const double mo = __shfl_xor(m_run, o), so = __shfl_xor(s_run, o);
-    const double mm = fmax(m_run, mo);
-    s_run = (m_run > -INFINITY ? s_run * exp(m_run - mm) : 0.0) + (mo > -INFINITY ? so * exp(mo - mm) : 0.0);
-    m_run = mm;
-  }
-  if (g == 0 && qvalid) rowstat[(int64_t)bh * n_blk + qi] = make_double2(m_run, s_run);
+  // the row max over the four lane groups that share query l16
+  m_run = pair_max<32>(pair_max<16>(m_run));
+  if (g == 0 && qvalid) rowstat[(int64_t)bh * n_blk + qi] = make_double2(m_run, 0.0);
 }
 
 // ------------------------------------------------------------------ select
@@ -435,22 +407,46 @@ __global__ __launch_bounds__(256, NI == 10 ? 4 : 1) void k_select(const double* 
 
   uint32_t bits[NI];
   {
-    double m = 0.0, inv = 1.0;
-    if (!scores_in) {
-      const double2 st = rowstat[r];
-      m = st.x, inv = 1.0 / st.y;
-    }
-    const double* zr = z + r * n;
     const float* sr = scores_in ? scores_in + r * n : nullptr;
     float* so = s_out ? s_out + r * n : nullptr;
+    if (sr) {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int j = lane + 64 * i;
-      bits[i] = 0;
-      if (j < n) {
-        const float s = sr ? sr[j] : (float)(exp(zr[j] - m) * inv);
-        if (so) so[j] = s;
-        bits[i] = clamp_bits(s);
+      for (int i = 0; i < NI; ++i) {
+        const int j = lane + 64 * i;
+        bits[i] = 0;
+        if (j < n) {
+          const float s = sr[j];
+          if (so) so[j] = s;
+          bits[i] = clamp_bits(s);
+        }
+      }
+    } else {
+      // S_j = exp(y_j - max) / sum_j' exp(y_j' - max): the exponentials in
+      // fp64 against the row max, their sum per lane in slot order and then
+      // across the wave by a butterfly (commutative pairwise adds, so every
+      // lane holds the same sum), each score rounded once to fp32
+      const double m = rowstat[r].x;
+      const double* zr = z + r * n;
+      double e[NI];
+      double sl = 0.0;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int j = lane + 64 * i;
+        e[i] = j < n ? exp(zr[j] - m) : 0.0;
+        sl += e[i];
+      }
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) sl += __shfl_xor(sl, o);
+      const double inv = 1.0 / sl;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int j = lane + 64 * i;
+        bits[i] = 0;
+        if (j < n) {
+          const float s = (float)(e[i] * inv);
+          if (so) so[j] = s;
+          bits[i] = clamp_bits(s);
+        }
       }
     }
   }
