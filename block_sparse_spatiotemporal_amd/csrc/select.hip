@@ -294,8 +294,13 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, 
   // The products of tile kt run on the matrix cores while the same wave does
   // the fp64 log-sum-exp of tile kt-1 (independent work, so the two overlap
   // inside the wave): the loop carries the previous tile's accumulator.
+  // With sub-blocks the tile's rows are read permuted, row r of the product
+  // taking sub-key 4 (r % 4) + r / 4: lane group g then holds sub-keys
+  // 4g..4g+3, half of one block, so a block's log-sum-exp needs one exchange
+  // between lane groups g and g ^ 1 instead of two rounds over all four.
+  const int arow = SUB ? 4 * (l16 & 3) + (l16 >> 2) : l16;
   auto products = [&](int kt) __attribute__((always_inline)) -> f64x4 {
-    const double2* ks = (const double2*)&ks_lds[kt & 1][l16][QD * g];
+    const double2* ks = (const double2*)&ks_lds[kt & 1][arow][QD * g];
     f64x4 acc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int c = 0; c < QD / 2; ++c) {
@@ -321,32 +326,24 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, 
 #pragma unroll
       for (int i = 0; i < 4; ++i) yt[w][l16][(kt % TPF) * 16 + g + 4 * i] = yv[i];
     } else {
-      // sub-key m = g + 4*i of the tile is sub-block m%8 of block kt*2 + m/8:
-      // acc[2*b2] and acc[2*b2+1] are sub-blocks g and g+4 of block kt*2+b2.
-      double cb[2], eb[2];
+      // acc[i] is sub-key 4g + i of the tile: sub-block 4 (g % 2) + i of
+      // block kt*2 + g/2.  Log-sum-exp over the block's 8 sub-blocks (4 per
+      // lane, lane groups g and g ^ 1): the max first, then one exponential
+      // per sub-block; lane groups 0 and 2 write the two blocks' logits.
+      const int blk = kt * 2 + (g >> 1);
+      const uint32_t ok = blk < n_blk ? (uint32_t)sub_ok[blk] >> (4 * (g & 1)) : 0u;
+      double v[4];
 #pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2) {
-        const int blk = kt * 2 + b2;
-        const uint32_t ok = blk < n_blk ? sub_ok[blk] : 0u;
-        const double v0 = (ok >> g & 1) ? acc[2 * b2] * scale : -INFINITY;
-        const double v1 = (ok >> (g + 4) & 1) ? acc[2 * b2 + 1] * scale : -INFINITY;
-        // log-sum-exp over the block's 8 sub-blocks (2 per lane, 4 lane groups):
-        // the max first, then one exponential per sub-block
-        double c = fmax(v0, v1);
-        c = pair_max<32>(pair_max<16>(c));
-        const double e2 = exp(v0 - c) + exp(v1 - c);
-        double e = c > -INFINITY ? e2 : 0.0;
-        e = pair_sum<32>(pair_sum<16>(e));
-        cb[b2] = c, eb[b2] = e;
-      }
-      // every lane group now holds both blocks' (max, sum); group 0 owns block
-      // kt*2 and group 1 block kt*2+1: one log each, its logit written out and
-      // counted in the row max (groups merged at the end)
-      const double cm = g == 1 ? cb[1] : cb[0], em = g == 1 ? eb[1] : eb[0];
-      const double lg = cm + log(em);
-      const double yo = g < 2 && cm > -INFINITY ? lg : -INFINITY;
+      for (int i = 0; i < 4; ++i) v[i] = (ok >> i & 1) ? acc[i] * scale : -INFINITY;
+      double c = fmax(fmax(v[0], v[1]), fmax(v[2], v[3]));
+      c = pair_max<16>(c);
+      const double e4 = (exp(v[0] - c) + exp(v[1] - c)) + (exp(v[2] - c) + exp(v[3] - c));
+      double e = c > -INFINITY ? e4 : 0.0;
+      e = pair_sum<16>(e);
+      const double lg = c + log(e);
+      const double yo = (g & 1) == 0 && c > -INFINITY ? lg : -INFINITY;
       m_run = fmax(m_run, yo);
-      if (g < 2) yt[w][l16][(kt % TPF) * 2 + g] = yo;
+      if ((g & 1) == 0) yt[w][l16][(kt % TPF) * 2 + (g >> 1)] = yo;
     }
   };
   f64x4 acc_prev = products(0);
