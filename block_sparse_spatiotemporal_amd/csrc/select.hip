@@ -204,6 +204,34 @@ __global__ __launch_bounds__(64) void k_pool_sub(const T* __restrict__ k, double
   }
 }
 
+// exp(x) for x <= 0 (-inf and anything below -746 give 0), in fp64 with a
+// 64-entry table: x = k ln2/64 + r, |r| <= ln2/128, with ln2/64 split in a
+// 32-bit head (k * head exact for |k| < 2^20) and a tail; exp(r) by its
+// degree-5 Taylor polynomial (remainder below 4e-17); exp(x) =
+// 2^(k >> 6) * tab[k & 63] * exp(r) with tab[j] = 2^(j/64).  About 13 fp64
+// instructions against about 20 for the library exp, within a few units in
+// the last place of it (4.4e-16 relative in a host emulation with exact table
+// entries).
+__device__ __forceinline__ double exp_neg(double x, const double* tab) {
+  const double xc = fmax(x, -746.0);
+  const double k = __builtin_rint(xc * 92.33248261689366);          // 64 / ln 2
+  double r = fma(-k, 0.010830424695086549, xc);                     // head of ln 2 / 64
+  r = fma(-k, 1.162596423439437e-12, r);                            // tail of ln 2 / 64
+  double p = fma(r, 1.0 / 120.0, 1.0 / 24.0);
+  p = fma(p, r, 1.0 / 6.0);
+  p = fma(p, r, 0.5);
+  p = fma(p, r, 1.0);
+  p = fma(p, r, 1.0);
+  const int ki = (int)k;
+  return ldexp(tab[ki & 63] * p, ki >> 6);
+}
+
+// tab[j] = 2^(j/64) for exp_neg; filled by the first 64 threads (callers
+// synchronise before use).
+__device__ __forceinline__ void exp_neg_table(double* tab) {
+  if (threadIdx.x < 64) tab[threadIdx.x] = exp2((double)threadIdx.x / 64.0);
+}
+
 // ------------------------------------------------------------------ score
 // Block logits Y[bh, i, j] = q_bar_i . k_bar_j / sqrt(D) in fp64 (with
 // sub-blocks: the log-sum-exp over the non-empty sub-blocks of j, which makes
@@ -276,6 +304,8 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, 
       for (int t = 0; t < 8; ++t) mbits |= (sub_cnt[j * 8 + t] > 0 ? 1u : 0u) << t;
       sub_ok[j] = (uint8_t)mbits;
     }
+  __shared__ double exp_tab[64];
+  exp_neg_table(exp_tab);
   kstore(0, kfetch(0));
   __syncthreads();
   // Logits go out through a per-wave LDS tile of 16 query rows x 64 block
@@ -337,7 +367,8 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, 
       for (int i = 0; i < 4; ++i) v[i] = (ok >> i & 1) ? acc[i] * scale : -INFINITY;
       double c = fmax(fmax(v[0], v[1]), fmax(v[2], v[3]));
       c = pair_max<16>(c);
-      const double e4 = (exp(v[0] - c) + exp(v[1] - c)) + (exp(v[2] - c) + exp(v[3] - c));
+      const double e4 = (exp_neg(v[0] - c, exp_tab) + exp_neg(v[1] - c, exp_tab)) +
+                        (exp_neg(v[2] - c, exp_tab) + exp_neg(v[3] - c, exp_tab));
       double e = c > -INFINITY ? e4 : 0.0;
       e = pair_sum<16>(e);
       const double lg = c + log(e);
@@ -395,6 +426,9 @@ __global__ __launch_bounds__(256, NI == 10 ? 4 : 1) void k_select(const double* 
   __shared__ unsigned long long hmass[4][256];
   __shared__ unsigned int hcnt[4][256];
   __shared__ unsigned long long lkey[4][64];
+  __shared__ double exp_tab[64];
+  exp_neg_table(exp_tab);
+  __syncthreads();
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int64_t r = (int64_t)blockIdx.x * 4 + wv;
   if (r >= n_rows) return;
@@ -429,7 +463,7 @@ __global__ __launch_bounds__(256, NI == 10 ? 4 : 1) void k_select(const double* 
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int j = lane + 64 * i;
-        e[i] = j < n ? exp(zr[j] - m) : 0.0;
+        e[i] = j < n ? exp_neg(zr[j] - m, exp_tab) : 0.0;
         sl += e[i];
       }
 #pragma unroll
