@@ -12,6 +12,7 @@
 #define FVA_MAX_PHEAD 512 // per-head p values passed by value to the kernels
 #define FVA_MAX_NBLK 4096 // blocks per head the selection kernels support
 #define FVA_MAX_SCHED_HEADS 4096  // B*H the attention scheduler supports
+#define FVA_MAX_SCORE_SPLIT 8     // key ranges the score grid may be split into
 
 struct fva_plan_s {
   fva_plan_desc desc;
@@ -35,7 +36,8 @@ struct fva_plan_s {
   double* kbar;       // [B*H*n_blk*(n_sub or 1)*D] pooled K (per sub-block), fp64
   double* ybuf;       // [B*H*n_blk*n_blk] block logits, fp64
   float* sbuf;        // [B*H*n_blk*n_blk] fp32 scores the selection read
-  double2* rowstat;   // [n_rows] row max of the block logits in .x, fp64
+  double* rowmax;     // [FVA_MAX_SCORE_SPLIT][n_rows] row max of the block logits per key range, fp64
+  int score_split;    // key ranges of the latest score launch (rows of rowmax in use)
   int32_t* rowcnt;    // [n_rows] kept blocks per row
   uint64_t* rowmask;  // [n_rows*nw] kept-block bitmask per row
   int32_t* headcnt;   // [B*H]

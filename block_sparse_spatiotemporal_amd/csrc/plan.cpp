@@ -169,7 +169,7 @@ static void layout_workspace(const fva_plan_desc* d, const fva_plan_info& in, si
   offs[5] = c.take(sizeof(double) * bh * in.n_blk * d->head_dim);        // qbar
   offs[6] = c.take(sizeof(double) * bh * in.n_blk * (in.n_sub ? 8 : 1) * d->head_dim);  // kbar
   offs[7] = c.take(sizeof(double) * bh * in.n_blk * in.n_blk);           // ybuf
-  offs[8] = c.take(sizeof(double2) * in.n_rows);                         // rowstat
+  offs[8] = c.take(sizeof(double) * FVA_MAX_SCORE_SPLIT * in.n_rows);     // rowmax
   offs[9] = c.take(sizeof(int32_t) * in.n_rows);                         // rowcnt
   offs[10] = c.take(sizeof(uint64_t) * in.n_rows * nw);                  // rowmask
   offs[11] = c.take(sizeof(int32_t) * bh);                               // headcnt
@@ -327,7 +327,8 @@ extern "C" int fva_plan_create(fva_plan_t* out, const fva_plan_desc* desc, hipSt
   p->qbar = (double*)(b + offs[5]);
   p->kbar = (double*)(b + offs[6]);
   p->ybuf = (double*)(b + offs[7]);
-  p->rowstat = (double2*)(b + offs[8]);
+  p->rowmax = (double*)(b + offs[8]);
+  p->score_split = 1;
   p->rowcnt = (int32_t*)(b + offs[9]);
   p->rowmask = (uint64_t*)(b + offs[10]);
   p->headcnt = (int32_t*)(b + offs[11]);

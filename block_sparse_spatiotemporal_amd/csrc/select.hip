@@ -237,14 +237,17 @@ __device__ __forceinline__ void exp_neg_table(double* tab) {
 // sub-blocks: the log-sum-exp over the non-empty sub-blocks of j, which makes
 // exp(Y) the sum of the sub-block terms), plus the row max of Y.
 // fp64 matrix cores (v_mfma_f64_16x16x4_f64).  Workgroup = 4 waves, each
-// wave one 16-query tile; every wave sweeps all 16-key tiles, computing
-// Z^T = Kbar . Qbar^T so that lane l owns query l%16 and keys l/16 + 4*i.
+// wave one 16-query tile; every wave sweeps the 16-key tiles of its
+// workgroup's key range (gridDim.z ranges split the tiles evenly, so the grid
+// fills whole rounds of the compute units), computing Z^T = Kbar . Qbar^T so
+// that lane l owns query l%16 and keys l/16 + 4*i.  Each range writes its
+// own row max (rowmax[range][row]); the selection takes their maximum.
 // fp64 keeps the logits exact to ~1e-15, so the fp32 scores the selection
 // reads carry only their final rounding.
 template <bool SUB, int D>
 __global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, const double* __restrict__ kbar,
                                                const int32_t* __restrict__ sub_cnt, double* __restrict__ y,
-                                               double2* __restrict__ rowstat, int n_blk, double scale) {
+                                               double* __restrict__ rowmax, int n_blk, double scale) {
   constexpr int QD = D / 4;   // d values per lane group (k-steps of 4)
   const int bh = blockIdx.y;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -254,6 +257,10 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, 
   const bool qvalid = qi < n_blk;
   const int nkeys = SUB ? n_blk * 8 : n_blk;
   const int ntiles = (nkeys + 15) / 16;
+  // this workgroup's key tiles [t0, t1) and logit columns [c0, c1)
+  const int t0 = (int)((int64_t)ntiles * blockIdx.z / gridDim.z);
+  const int t1 = (int)((int64_t)ntiles * (blockIdx.z + 1) / gridDim.z);
+  const int c0 = SUB ? 2 * t0 : 16 * t0, c1 = min(SUB ? 2 * t1 : 16 * t1, n_blk);
   double qv[QD];
   {
     const double2* src = (const double2*)(qbar + ((int64_t)bh * n_blk + min(qi, n_blk - 1)) * D + QD * g);
@@ -306,7 +313,7 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, 
     }
   __shared__ double exp_tab[64];
   exp_neg_table(exp_tab);
-  kstore(0, kfetch(0));
+  kstore(t0 & 1, kfetch(t0));
   __syncthreads();
   // Logits go out through a per-wave LDS tile of 16 query rows x 64 block
   // columns, written back as whole 512-byte row pieces.
@@ -315,9 +322,9 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, 
   double* yw = y + ((int64_t)bh * n_blk + q0) * n_blk;
   auto flush = [&](int kt) {
     wave_sync_lds();
-    const int j = (kt / TPF) * 64 + lane;
+    const int j = (kt / TPF) * 64 + lane;   // only this range's columns of the group
     for (int q = 0; q < 16 && q0 + q < n_blk; ++q)
-      if (j < n_blk) yw[(int64_t)q * n_blk + j] = yt[w][q][lane];
+      if (j >= c0 && j < c1) yw[(int64_t)q * n_blk + j] = yt[w][q][lane];
     wave_sync_lds();
   };
   double m_run = -INFINITY;
@@ -377,13 +384,13 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, 
       if ((g & 1) == 0) yt[w][l16][(kt % TPF) * 2 + (g >> 1)] = yo;
     }
   };
-  f64x4 acc_prev = products(0);
+  f64x4 acc_prev = products(t0);
   {
-    const KTile nxt = kfetch(1);
-    kstore(1, nxt);
+    const KTile nxt = kfetch(t0 + 1);
+    kstore((t0 + 1) & 1, nxt);
     __syncthreads();
   }
-  for (int kt = 1; kt < ntiles; ++kt) {
+  for (int kt = t0 + 1; kt < t1; ++kt) {
     const KTile nxt = kfetch(kt + 1);
     const f64x4 acc = products(kt);
     lse(kt - 1, acc_prev);
@@ -392,11 +399,11 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, 
     __syncthreads();
     acc_prev = acc;
   }
-  lse(ntiles - 1, acc_prev);
-  flush(ntiles - 1);
+  lse(t1 - 1, acc_prev);
+  flush(t1 - 1);
   // the row max over the four lane groups that share query l16
   m_run = pair_max<32>(pair_max<16>(m_run));
-  if (g == 0 && qvalid) rowstat[(int64_t)bh * n_blk + qi] = make_double2(m_run, 0.0);
+  if (g == 0 && qvalid) rowmax[(int64_t)blockIdx.z * gridDim.y * n_blk + (int64_t)bh * n_blk + qi] = m_run;
 }
 
 // ------------------------------------------------------------------ select
@@ -418,7 +425,8 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, 
 // 0.87 instead of 0.90 ms at the Wan-14B 480P shape, lists unchanged.  Wider
 // rows keep the compiler's choice: forcing four waves spills 23 and more.
 template <int NI>
-__global__ __launch_bounds__(256, NI == 10 ? 4 : 1) void k_select(const double* __restrict__ z, const double2* __restrict__ rowstat,
+__global__ __launch_bounds__(256, NI == 10 ? 4 : 1) void k_select(const double* __restrict__ z, const double* __restrict__ rowmax,
+                                                int nsplit,
                                                 const float* __restrict__ scores_in, float* __restrict__ s_out,
                                                 SelectArgs pa, int p_count, int k_min, int n_blk,
                                                 int64_t n_rows, int32_t* __restrict__ rowcnt,
@@ -456,7 +464,8 @@ __global__ __launch_bounds__(256, NI == 10 ? 4 : 1) void k_select(const double* 
       // fp64 against the row max, their sum per lane in slot order and then
       // across the wave by a butterfly (commutative pairwise adds, so every
       // lane holds the same sum), each score rounded once to fp32
-      const double m = rowstat[r].x;
+      double m = rowmax[r];
+      for (int sp = 1; sp < nsplit; ++sp) m = fmax(m, rowmax[sp * n_rows + r]);
       const double* zr = z + r * n;
       double e[NI];
       double sl = 0.0;
@@ -845,18 +854,50 @@ void launch_pool(fva_plan_t plan, const void* q, const void* k, hipStream_t s) {
                        plan->sub_pos, plan->sub_cnt, in.n_blk, in.n_pad);
 }
 
+// Key ranges of the score grid.  Every workgroup does the same work (64
+// queries x its key tiles), so the launch takes ceil(wg * n / slots) rounds
+// of the resident workgroups; each range adds a fixed cost of about two
+// tiles (the query load, the tables, the prefetch start).  n minimises
+// rounds x (tiles / n + 2): at the 720P Hilbert shape 920 workgroups on
+// 512 slots take 2 rounds unsplit and 9 (of 8.98) with five ranges.
+int score_split(int wg, int ntiles, int slots) {
+  int best = 1;
+  double best_cost = 1e300;
+  for (int n = 1; n <= FVA_MAX_SCORE_SPLIT && n <= ntiles; ++n) {
+    const int64_t rounds = ((int64_t)wg * n + slots - 1) / slots;
+    const double cost = (double)rounds * ((double)ntiles / n + 2.0);
+    if (cost < best_cost * 0.99) best = n, best_cost = cost;
+  }
+  return best;
+}
+
+template <typename K>
+int resident_blocks(K kernel) {
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, 256, 0) != hipSuccess || nb < 1) nb = 1;
+  return nb;
+}
+
 template <int D>
 void launch_score(fva_plan_t plan, hipStream_t s) {
   const fva_plan_info& in = plan->info;
   const int bh = plan->desc.batch * plan->desc.heads;
-  dim3 grid((in.n_blk + 63) / 64, bh);
+  const int wg = (in.n_blk + 63) / 64 * bh;
+  const int ntiles = ((in.n_sub ? 8 : 1) * in.n_blk + 15) / 16;
   const double scale = 1.0 / sqrt((double)D);
-  if (in.n_sub)
+  if (in.n_sub) {
+    static const int per_cu = resident_blocks(k_score<true, D>);
+    plan->score_split = score_split(wg, ntiles, plan->num_cu * per_cu);
+    dim3 grid((in.n_blk + 63) / 64, bh, plan->score_split);
     hipLaunchKernelGGL((k_score<true, D>), grid, dim3(256), 0, s, plan->qbar, plan->kbar, plan->sub_cnt,
-                       plan->ybuf, plan->rowstat, in.n_blk, scale);
-  else
+                       plan->ybuf, plan->rowmax, in.n_blk, scale);
+  } else {
+    static const int per_cu = resident_blocks(k_score<false, D>);
+    plan->score_split = score_split(wg, ntiles, plan->num_cu * per_cu);
+    dim3 grid((in.n_blk + 63) / 64, bh, plan->score_split);
     hipLaunchKernelGGL((k_score<false, D>), grid, dim3(256), 0, s, plan->qbar, plan->kbar, plan->sub_cnt,
-                       plan->ybuf, plan->rowstat, in.n_blk, scale);
+                       plan->ybuf, plan->rowmax, in.n_blk, scale);
+  }
 }
 
 // fva_select's body.  pooled: the means come from fva_permute_pool calls
@@ -909,7 +950,8 @@ int select_impl(fva_plan_t plan, const void* q_perm, const void* k_perm, bool po
   const unsigned sel_grid = (unsigned)((in.n_rows + 3) / 4);
   const int ni = (in.n_blk + 63) / 64;
 #define FVA_SELECT(NI)                                                                                  \
-  hipLaunchKernelGGL((k_select<NI>), dim3(sel_grid), dim3(256), 0, stream, plan->ybuf, plan->rowstat,  \
+  hipLaunchKernelGGL((k_select<NI>), dim3(sel_grid), dim3(256), 0, stream, plan->ybuf, plan->rowmax,   \
+                     plan->score_split,                                                                 \
                      scores_in, s_out, pa, p_count, k_min, in.n_blk, in.n_rows, plan->rowcnt,           \
                      plan->rowmask, plan->nw)
   if (ni <= 4) FVA_SELECT(4);
