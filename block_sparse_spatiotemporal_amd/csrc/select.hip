@@ -232,6 +232,45 @@ __device__ __forceinline__ void exp_neg_table(double* tab) {
   if (threadIdx.x < 64) tab[threadIdx.x] = exp2((double)threadIdx.x / 64.0);
 }
 
+// log(x) for finite x >= 1 in fp64 with a 128-entry table: x = 2^k m with m
+// in [1, 2) taken from the bits; c = m cut to 7 fractional bits, so m - c is
+// exact and r = (m - c) / c lies in [0, 2^-7); log x = k ln 2 + log c +
+// log1p(r), with 1/c and log c from the table (tab[2j], tab[2j+1] for
+// c = 1 + j/128), log1p(r) by its degree-7 Taylor polynomial (remainder below
+// 2e-18) and ln 2 split in a head exact in k * head and a tail.  About 13
+// fp64 instructions against about 75 for the library log; within 3.8e-16 of
+// log x on [1, 8] in a host emulation (the library log's result at x = 1 and
+// at powers of two is reproduced exactly).
+__device__ __forceinline__ double log_ge1(double x, const double* tab) {
+  const uint64_t xb = (uint64_t)__double_as_longlong(x);
+  const uint32_t hx = (uint32_t)(xb >> 32);
+  const int k = (int)(hx >> 20) - 1023;
+  const uint32_t hm = (hx & 0x000FFFFFu) | 0x3FF00000u;
+  const double m = __longlong_as_double((long long)(((uint64_t)hm << 32) | (uint32_t)xb));
+  const double c = __longlong_as_double((long long)((uint64_t)(hm & 0xFFFFE000u) << 32));
+  const int j = (int)(hx >> 13) & 127;
+  const double2 t = *(const double2*)(tab + 2 * j);
+  const double r = (m - c) * t.x;
+  double q = fma(1.0 / 7.0, r, -1.0 / 6.0);
+  q = fma(q, r, 1.0 / 5.0);
+  q = fma(q, r, -0.25);
+  q = fma(q, r, 1.0 / 3.0);
+  q = fma(q, r, -0.5);
+  q = fma(q, r, 1.0);
+  const double kd = (double)k;
+  return fma(kd, 0.6931471803691238, fma(kd, 1.9082149292705877e-10, t.y + q * r));
+}
+
+// tab for log_ge1: tab[2j] = 1 / (1 + j/128), tab[2j+1] = log(1 + j/128);
+// filled by the first 128 threads (callers synchronise before use).
+__device__ __forceinline__ void log_ge1_table(double* tab) {
+  if (threadIdx.x < 128) {
+    const double c = 1.0 + (double)threadIdx.x / 128.0;
+    tab[2 * threadIdx.x] = 1.0 / c;
+    tab[2 * threadIdx.x + 1] = log1p((double)threadIdx.x / 128.0);
+  }
+}
+
 // ------------------------------------------------------------------ score
 // Block logits Y[bh, i, j] = q_bar_i . k_bar_j / sqrt(D) in fp64 (with
 // sub-blocks: the log-sum-exp over the non-empty sub-blocks of j, which makes
@@ -313,6 +352,8 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, 
     }
   __shared__ double exp_tab[64];
   exp_neg_table(exp_tab);
+  __shared__ __attribute__((aligned(16))) double log_tab[SUB ? 256 : 2];
+  if (SUB) log_ge1_table(log_tab);
   kstore(t0 & 1, kfetch(t0));
   __syncthreads();
   // Logits go out through a per-wave LDS tile of 16 query rows x 64 block
@@ -378,7 +419,8 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, 
                         (exp_neg(v[2] - c, exp_tab) + exp_neg(v[3] - c, exp_tab));
       double e = c > -INFINITY ? e4 : 0.0;
       e = pair_sum<16>(e);
-      const double lg = c + log(e);
+      // e >= 1 (the max term is 1) whenever the block has a sub-block
+      const double lg = c + log_ge1(c > -INFINITY ? e : 1.0, log_tab);
       const double yo = (g & 1) == 0 && c > -INFINITY ? lg : -INFINITY;
       m_run = fmax(m_run, yo);
       if ((g & 1) == 0) yt[w][l16][(kt % TPF) * 2 + (g >> 1)] = yo;
