@@ -356,16 +356,21 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, 
   if (SUB) log_ge1_table(log_tab);
   kstore(t0 & 1, kfetch(t0));
   __syncthreads();
-  // Logits go out through a per-wave LDS tile of 16 query rows x 64 block
-  // columns, written back as whole 512-byte row pieces.
-  constexpr int TPF = SUB ? 32 : 4;   // key tiles per flush (64 block columns)
-  __shared__ double yt[4][16][65];
+  // Logits go out through a per-wave LDS tile of 16 query rows x 32 block
+  // columns, written back as 256-byte row pieces, two rows per store.  The
+  // tile is kept that small so three workgroups fit the LDS of a compute
+  // unit without sub-blocks (the block form is LDS-bound at 64 columns).
+  constexpr int TPF = SUB ? 16 : 2;   // key tiles per flush (32 block columns)
+  __shared__ double yt[4][16][33];
   double* yw = y + ((int64_t)bh * n_blk + q0) * n_blk;
   auto flush = [&](int kt) {
     wave_sync_lds();
-    const int j = (kt / TPF) * 64 + lane;   // only this range's columns of the group
-    for (int q = 0; q < 16 && q0 + q < n_blk; ++q)
-      if (j >= c0 && j < c1) yw[(int64_t)q * n_blk + j] = yt[w][q][lane];
+    const int j = (kt / TPF) * 32 + (lane & 31);   // only this range's columns of the group
+#pragma unroll
+    for (int q2 = 0; q2 < 16; q2 += 2) {
+      const int q = q2 + (lane >> 5);
+      if (q0 + q < n_blk && j >= c0 && j < c1) yw[(int64_t)q * n_blk + j] = yt[w][q][lane & 31];
+    }
     wave_sync_lds();
   };
   double m_run = -INFINITY;
