@@ -284,7 +284,7 @@ __device__ __forceinline__ void log_ge1_table(double* tab) {
 // fp64 keeps the logits exact to ~1e-15, so the fp32 scores the selection
 // reads carry only their final rounding.
 template <bool SUB, int D>
-__global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, const double* __restrict__ kbar,
+__global__ __launch_bounds__(256, 3) void k_score(const double* __restrict__ qbar, const double* __restrict__ kbar,
                                                const int32_t* __restrict__ sub_cnt, double* __restrict__ y,
                                                double* __restrict__ rowmax, int n_blk, double scale) {
   constexpr int QD = D / 4;   // d values per lane group (k-steps of 4)
@@ -356,20 +356,21 @@ __global__ __launch_bounds__(256) void k_score(const double* __restrict__ qbar, 
   if (SUB) log_ge1_table(log_tab);
   kstore(t0 & 1, kfetch(t0));
   __syncthreads();
-  // Logits go out through a per-wave LDS tile of 16 query rows x 32 block
-  // columns, written back as 256-byte row pieces, two rows per store.  The
-  // tile is kept that small so three workgroups fit the LDS of a compute
-  // unit without sub-blocks (the block form is LDS-bound at 64 columns).
-  constexpr int TPF = SUB ? 16 : 2;   // key tiles per flush (32 block columns)
-  __shared__ double yt[4][16][33];
+  // Logits go out through a per-wave LDS tile of 16 query rows x YC block
+  // columns, written back as YC * 8-byte row pieces, 64 / YC rows per store.
+  // The tile is kept that small so three workgroups fit the LDS of a
+  // compute unit.
+  constexpr int YC = SUB ? 16 : 32;
+  constexpr int TPF = SUB ? YC / 2 : YC / 16;   // key tiles per flush
+  __shared__ double yt[4][16][YC + 1];
   double* yw = y + ((int64_t)bh * n_blk + q0) * n_blk;
   auto flush = [&](int kt) {
     wave_sync_lds();
-    const int j = (kt / TPF) * 32 + (lane & 31);   // only this range's columns of the group
+    const int j = (kt / TPF) * YC + lane % YC;   // only this range's columns of the group
 #pragma unroll
-    for (int q2 = 0; q2 < 16; q2 += 2) {
-      const int q = q2 + (lane >> 5);
-      if (q0 + q < n_blk && j >= c0 && j < c1) yw[(int64_t)q * n_blk + j] = yt[w][q][lane & 31];
+    for (int q2 = 0; q2 < 16; q2 += 64 / YC) {
+      const int q = q2 + lane / YC;
+      if (q0 + q < n_blk && j >= c0 && j < c1) yw[(int64_t)q * n_blk + j] = yt[w][q][lane % YC];
     }
     wave_sync_lds();
   };
