@@ -469,7 +469,7 @@ __global__ __launch_bounds__(256, 3) void k_score(const double* __restrict__ qba
 // exact cut is read off a prefix sum.  Output: a bitmask of kept ids per row
 // and the kept count.
 // Ten mask words (up to 640 blocks, the 480P shapes) fit four waves per SIMD
-// in 128 VGPRs (4 of them spilled); the selection then took
+// in 128 VGPRs (2 of them spilled); the selection then took
 // 0.87 instead of 0.90 ms at the Wan-14B 480P shape, lists unchanged.  Wider
 // rows keep the compiler's choice: forcing four waves spills 23 and more.
 template <int NI>
@@ -479,8 +479,11 @@ __global__ __launch_bounds__(256, NI == 10 ? 4 : 1) void k_select(const double* 
                                                 SelectArgs pa, int p_count, int k_min, int n_blk,
                                                 int64_t n_rows, int32_t* __restrict__ rowcnt,
                                                 uint64_t* __restrict__ rowmask, int nw) {
-  __shared__ unsigned long long hmass[4][256];
-  __shared__ unsigned int hcnt[4][256];
+  // two copies of each wave's histograms (even and odd lanes), which halves
+  // the same-bin atomics of one instruction: at the first level the digit
+  // is the score's exponent, shared by many lanes
+  __shared__ unsigned long long hmass[4][2][256];
+  __shared__ unsigned int hcnt[4][2][256];
   __shared__ unsigned long long lkey[4][64];
   __shared__ double exp_tab[64];
   exp_neg_table(exp_tab);
@@ -563,16 +566,18 @@ __global__ __launch_bounds__(256, NI == 10 ? 4 : 1) void k_select(const double* 
       const int shift = level < 5 ? 39 - 8 * level : 0;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        hmass[wv][lane * 4 + t] = 0;
-        hcnt[wv][lane * 4 + t] = 0;
+        hmass[wv][0][lane * 4 + t] = 0;
+        hmass[wv][1][lane * 4 + t] = 0;
+        hcnt[wv][0][lane * 4 + t] = 0;
+        hcnt[wv][1][lane * 4 + t] = 0;
       }
       wave_sync_lds();
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         if (active >> i & 1) {
           const int dg = 255 - (int)((key_of(i) >> shift) & 0xFF);
-          atomicAdd(&hmass[wv][dg], (unsigned long long)fix_mass(bits[i]));
-          atomicAdd(&hcnt[wv][dg], 1u);
+          atomicAdd(&hmass[wv][lane & 1][dg], (unsigned long long)fix_mass(bits[i]));
+          atomicAdd(&hcnt[wv][lane & 1][dg], 1u);
         }
       }
       wave_sync_lds();
@@ -582,8 +587,8 @@ __global__ __launch_bounds__(256, NI == 10 ? 4 : 1) void k_select(const double* 
       uint32_t lc = 0;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        bm[t] = hmass[wv][lane * 4 + t];
-        bc[t] = hcnt[wv][lane * 4 + t];
+        bm[t] = hmass[wv][0][lane * 4 + t] + hmass[wv][1][lane * 4 + t];
+        bc[t] = hcnt[wv][0][lane * 4 + t] + hcnt[wv][1][lane * 4 + t];
         lm += bm[t];
         lc += bc[t];
       }
@@ -641,7 +646,7 @@ __global__ __launch_bounds__(256, NI == 10 ? 4 : 1) void k_select(const double* 
       if (useP) needP -= ma;
       if (useF) needF -= (int)ca;
       kAbove += (int)ca;
-      const uint32_t cstar = hcnt[wv][bs];
+      const uint32_t cstar = hcnt[wv][0][bs] + hcnt[wv][1][bs];
 #pragma unroll
       for (int i = 0; i < NI; ++i)
         if ((active >> i & 1) && 255 - (int)((key_of(i) >> shift) & 0xFF) != bs) active &= ~(1ull << i);
