@@ -167,7 +167,8 @@ static void layout_workspace(const fva_plan_desc* d, const fva_plan_info& in, si
   offs[3] = c.take(in.n_sub ? 64 * (size_t)in.n_blk : 0);                 // sub_pos
   offs[4] = c.take(in.n_sub ? sizeof(int32_t) * 8 * in.n_blk : 0);        // sub_cnt
   offs[5] = c.take(sizeof(double) * bh * in.n_blk * d->head_dim);        // qbar
-  offs[6] = c.take(sizeof(double) * bh * in.n_blk * (in.n_sub ? 8 : 1) * d->head_dim);  // kbar
+  // kbar, plus 16 slack rows the score kernel's last key tile may read
+  offs[6] = c.take(sizeof(double) * (bh * in.n_blk * (in.n_sub ? 8 : 1) + 16) * d->head_dim);
   offs[7] = c.take(sizeof(double) * bh * in.n_blk * in.n_blk);           // ybuf
   offs[8] = c.take(sizeof(double) * FVA_MAX_SCORE_SPLIT * in.n_rows);     // rowmax
   offs[9] = c.take(sizeof(int32_t) * in.n_rows);                         // rowcnt

@@ -204,16 +204,19 @@ __global__ __launch_bounds__(64) void k_pool_sub(const T* __restrict__ k, double
   }
 }
 
-// exp(x) for x <= 0 (-inf and anything below -746 give 0), in fp64 with a
-// 64-entry table: x = k ln2/64 + r, |r| <= ln2/128, with ln2/64 split in a
-// 32-bit head (k * head exact for |k| < 2^20) and a tail; exp(r) by its
-// degree-5 Taylor polynomial (remainder below 4e-17); exp(x) =
-// 2^(k >> 6) * tab[k & 63] * exp(r) with tab[j] = 2^(j/64).  About 13 fp64
-// instructions against about 20 for the library exp, within a few units in
-// the last place of it (4.4e-16 relative in a host emulation with exact table
-// entries).
+// exp(x) for x <= 0, in fp64 with a 64-entry table: x = k ln2/64 + r,
+// |r| <= ln2/128, with ln2/64 split in a 32-bit head (k * head exact for
+// |k| < 2^20) and a tail; exp(r) by its degree-5 Taylor polynomial
+// (remainder below 4e-17); exp(x) = 2^(k >> 6) * tab[k & 63] * exp(r) with
+// tab[j] = 2^(j/64), the power of two added to the exponent field as an
+// integer.  Arguments below -700 (and -inf) are taken as -700, so the result
+// stays a normal number: exp(-700) ~ 1e-304 in place of a smaller value or
+// 0, which changes no sum of at least 1 and no score rounded to fp32.  About
+// 12 fp64 instructions against about 20 for the library exp, within a few
+// units in the last place of it (4.4e-16 relative in a host emulation with
+// exact table entries).
 __device__ __forceinline__ double exp_neg(double x, const double* tab) {
-  const double xc = fmax(x, -746.0);
+  const double xc = fmax(x, -700.0);
   const double k = __builtin_rint(xc * 92.33248261689366);          // 64 / ln 2
   double r = fma(-k, 0.010830424695086549, xc);                     // head of ln 2 / 64
   r = fma(-k, 1.162596423439437e-12, r);                            // tail of ln 2 / 64
@@ -223,7 +226,8 @@ __device__ __forceinline__ double exp_neg(double x, const double* tab) {
   p = fma(p, r, 1.0);
   p = fma(p, r, 1.0);
   const int ki = (int)k;
-  return ldexp(tab[ki & 63] * p, ki >> 6);
+  const double v = tab[ki & 63] * p;   // in [0.99, 2.02]: normal
+  return __longlong_as_double(__double_as_longlong(v) + ((long long)(ki >> 6) << 52));
 }
 
 // tab[j] = 2^(j/64) for exp_neg; filled by the first 64 threads (callers
@@ -322,14 +326,18 @@ __global__ __launch_bounds__(256, 3) void k_score(const double* __restrict__ qba
   // an array kept across the loop with conditional writes ended up in
   // scratch memory, and every prefetch then waited for its loads at once.
   struct KTile { double2 v[KV]; };
+  // The last tile may run up to 15 rows past the head's keys: those rows are
+  // read (the workspace keeps slack rows behind the pooled keys) and their
+  // logits masked, so the loads need no per-lane clamp, only a wave-uniform
+  // tile base plus a fixed lane offset.
   auto kfetch = [&](int kt) -> KTile {
     KTile t;
-    kt = min(kt, ntiles - 1);
+    const double* tb = kh + (int64_t)min(kt, ntiles - 1) * 16 * D;
 #pragma unroll
     for (int v = 0; v < KV; ++v) {
       const int e = threadIdx.x + 256 * v;         // double2 index within the tile
       const int r = e / (D / 2), d2 = e - r * (D / 2);
-      t.v[v] = *(const double2*)(kh + (int64_t)min(kt * 16 + r, nkeys - 1) * D + 2 * d2);
+      t.v[v] = *(const double2*)(tb + r * D + 2 * d2);
     }
     return t;
   };
