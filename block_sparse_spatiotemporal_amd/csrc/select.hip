@@ -672,7 +672,12 @@ __global__ __launch_bounds__(256, NI == 10 ? 4 : 1) void k_select(const double* 
       }
       wave_sync_lds();
       uint64_t kk = lane < base ? lkey[wv][lane] : 0ull;
-      for (int kb = 2; kb <= 64; kb <<= 1) {
+      // a bitonic network over the smallest power of two holding the
+      // candidates (lanes past it never meet lanes below it): most rows
+      // end with a handful of candidates, e.g. 8 or fewer in three rows of
+      // four at the Wan-14B 480P shape, and need 6 of the 21 stages
+      const int span = base <= 2 ? 2 : 1 << (32 - __builtin_clz((unsigned)(base - 1)));
+      for (int kb = 2; kb <= span; kb <<= 1) {
         for (int jb = kb >> 1; jb > 0; jb >>= 1) {
           const uint64_t o = __shfl_xor(kk, jb);
           const bool up = (lane & kb) == 0, lower = (lane & jb) == 0;
