@@ -381,6 +381,22 @@ extern "C" int fva_plan(fva_plan_t* out, const fva_plan_desc* desc, hipStream_t 
   return fva_plan_create(out, desc, stream);
 }
 
+// Top-p for denoising step `step` of `n_steps`: linear from p_first at the
+// first step to p_last at the last ("DFSAttn" explainer, trick 3: little is
+// skipped while the latent is still noise, more as the video sharpens; the
+// page gives no curve, and a straight line between the two end values is
+// the plainest monotone one).  n_steps == 1 gives p_last.
+extern "C" int fva_p_schedule(int step, int n_steps, float p_first, float p_last, float* p_out) {
+  if (!p_out) return fva_fail(FVA_EINVAL, "p_out is NULL");
+  if (n_steps < 1) return fva_fail(FVA_EINVAL, "n_steps = %d must be >= 1", n_steps);
+  if (step < 0 || step >= n_steps) return fva_fail(FVA_EINVAL, "step %d outside [0, %d)", step, n_steps);
+  if (!(p_first > 0.0f && p_first <= 1.0f) || !(p_last > 0.0f && p_last <= 1.0f))
+    return fva_fail(FVA_EINVAL, "p_first %g and p_last %g must lie in (0, 1]", (double)p_first, (double)p_last);
+  const double t = n_steps > 1 ? (double)step / (double)(n_steps - 1) : 1.0;
+  *p_out = (float)((double)p_first + ((double)p_last - (double)p_first) * t);
+  return FVA_OK;
+}
+
 extern "C" int fva_plan_query(fva_plan_t plan, fva_plan_info* info) {
   if (!plan || !info) return fva_fail(FVA_EINVAL, "plan or info is NULL");
   *info = plan->info;

@@ -76,6 +76,7 @@ def lib() -> ctypes.CDLL:
             "fva_attention_raster": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp]),
             "fva_unpermute": (c_i32, [c_vp, c_vp, c_vp, c_vp]),
             "fva_mask_overlap": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
+            "fva_p_schedule": (c_i32, [c_i32, c_i32, ctypes.c_float, ctypes.c_float, P(ctypes.c_float)]),
             "fva_mask_accumulate": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp]),
             "fva_mask_from_counts": (c_i32, [c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp]),
             "fva_attention_lse": (c_i32, [c_vp] * 10),
@@ -210,6 +211,13 @@ def fva_permute_rope(plan: Plan, x_raster, x_perm, t_offset=0, base=10000.0, str
     _expect(x_perm, plan.perm_shape(), plan.torch_dtype, "x_perm")
     _check(lib().fva_permute_rope(plan.handle, _ptr(x_raster), _ptr(x_perm), int(t_offset), float(base),
                                   _stream(stream)))
+
+
+def fva_p_schedule(step: int, n_steps: int, p_first: float, p_last: float) -> float:
+    """Top-p for denoising step ``step`` of ``n_steps`` (the library's schedule)."""
+    out = ctypes.c_float()
+    _check(lib().fva_p_schedule(int(step), int(n_steps), float(p_first), float(p_last), ctypes.byref(out)))
+    return out.value
 
 
 def fva_mask_overlap(plan: Plan, row_ptr_a, col_idx_a, row_ptr_b, col_idx_b, counts=None, stream=None):

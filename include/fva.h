@@ -331,6 +331,17 @@ int fva_attention_backward(fva_plan_t plan, const void* q_perm, const void* k_pe
 int fva_mask_transpose(fva_plan_t plan, const int32_t* row_ptr, const int32_t* col_idx,
                        int32_t* t_row_ptr, int32_t* t_col_idx, hipStream_t stream);
 
+/* Top-p for denoising step `step` (0-based) of `n_steps` ("DFSAttn"
+ * explainer, trick 3: little is skipped while the latent is still noise and
+ * more as the video sharpens).  The page gives no curve; this is the straight
+ * line from p_first at the first step to p_last at the last, so a caller that
+ * starts near 1 (almost dense) ends at its target sparsity.  n_steps == 1
+ * gives p_last.  Host function: no device work, no plan.
+ *   p_out  host float, written on success.
+ * Errors: FVA_EINVAL for a NULL p_out, n_steps < 1, step outside
+ * [0, n_steps), or p_first / p_last outside (0, 1]. */
+int fva_p_schedule(int step, int n_steps, float p_first, float p_last, float* p_out);
+
 /* Agreement of two block selections, for reusing a cached selection across
  * denoising steps ("DFSAttn" explainer, trick 3: blocks that mattered at an
  * earlier step are remembered instead of re-evaluated; fva_attention accepts

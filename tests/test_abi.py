@@ -138,3 +138,21 @@ def test_plain_grid_fits_wg_times_over_the_chunk_range(batch, heads, grid):
         for chunk in (1, 7, 32, 1000, 4095, 4096):
             deal = 8 * chunk
             assert -(-items // deal) * deal <= info.max_wg, (G, chunk)
+
+
+def test_p_schedule_endpoints_line_and_errors():
+    # straight line from p_first (step 0) to p_last (last step), monotone,
+    # n_steps == 1 gives p_last; invalid arguments are rejected
+    assert fva.fva_p_schedule(0, 50, 0.99, 0.9) == pytest.approx(0.99, abs=1e-7)
+    assert fva.fva_p_schedule(49, 50, 0.99, 0.9) == pytest.approx(0.9, abs=1e-7)
+    assert fva.fva_p_schedule(0, 1, 0.99, 0.9) == pytest.approx(0.9, abs=1e-7)
+    assert fva.fva_p_schedule(2, 5, 1.0, 0.6) == pytest.approx(0.8, abs=1e-7)
+    ps = [fva.fva_p_schedule(s, 10, 1.0, 0.85) for s in range(10)]
+    assert all(a > b for a, b in zip(ps, ps[1:]))
+    assert all(abs(ps[s] - (1.0 - 0.15 * s / 9)) < 1e-6 for s in range(10))
+    L = fva.lib()
+    out = ctypes.c_float()
+    for args in [(0, 0, 0.9, 0.9), (5, 5, 0.9, 0.9), (-1, 5, 0.9, 0.9), (0, 5, 0.0, 0.9), (0, 5, 0.9, 1.5),
+                 (0, 5, float("nan"), 0.9)]:
+        assert L.fva_p_schedule(*args, ctypes.byref(out)) == fva.FVA_EINVAL, args
+    assert L.fva_p_schedule(0, 5, 0.9, 0.9, None) == fva.FVA_EINVAL
