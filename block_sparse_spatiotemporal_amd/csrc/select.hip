@@ -212,9 +212,8 @@ __global__ __launch_bounds__(64) void k_pool_sub(const T* __restrict__ k, double
 // integer.  Arguments below -700 (and -inf) are taken as -700, so the result
 // stays a normal number: exp(-700) ~ 1e-304 in place of a smaller value or
 // 0, which changes no sum of at least 1 and no score rounded to fp32.  About
-// 12 fp64 instructions against about 20 for the library exp, within a few
-// units in the last place of it (4.4e-16 relative in a host emulation with
-// exact table entries).
+// 12 fp64 instructions against about 20 for the library exp, within 5e-16
+// relative (tests/test_host_fp64_math.py restates it on the host).
 __device__ __forceinline__ double exp_neg(double x, const double* tab) {
   const double xc = fmax(x, -700.0);
   const double k = __builtin_rint(xc * 92.33248261689366);          // 64 / ln 2
@@ -242,9 +241,9 @@ __device__ __forceinline__ void exp_neg_table(double* tab) {
 // log1p(r), with 1/c and log c from the table (tab[2j], tab[2j+1] for
 // c = 1 + j/128), log1p(r) by its degree-7 Taylor polynomial (remainder below
 // 2e-18) and ln 2 split in a head exact in k * head and a tail.  About 13
-// fp64 instructions against about 75 for the library log; within 3.8e-16 of
-// log x on [1, 8] in a host emulation (the library log's result at x = 1 and
-// at powers of two is reproduced exactly).
+// fp64 instructions against about 75 for the library log; within 4e-16 of
+// log x on [1, 8], exactly 0 at x = 1 (tests/test_host_fp64_math.py restates
+// it on the host).
 __device__ __forceinline__ double log_ge1(double x, const double* tab) {
   const uint64_t xb = (uint64_t)__double_as_longlong(x);
   const uint32_t hx = (uint32_t)(xb >> 32);
