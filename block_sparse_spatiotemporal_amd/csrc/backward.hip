@@ -184,8 +184,23 @@ __device__ __forceinline__ void store4(uint16_t* dst, const f32x16& acc, int g4,
   *(uint2*)dst = __builtin_bit_cast(uint2, __builtin_convertvector(v, bf16x4));
 }
 
+// Chunk swizzle of the row tiles of the backward kernels.  Physical 16-byte
+// chunk pc of row r holds logical chunk pc ^ kswz_t(r).  For D = 128 the
+// swizzle puts r % 4 in the high two bits and (r / 4) % 4 in the low two:
+// a plain row read (16 consecutive rows, one chunk each) still touches 16
+// different chunks, and a transposed read, whose 16-lane group takes two
+// neighbouring chunks of four consecutive rows (and whose other 16-lane group
+// in the same pass the next two chunks of those rows), touches 16 different
+// chunks over the 32 lanes: every bank once.  With r % 16 (the forward
+// kernel's swizzle) the four rows of a group share their chunks, and half the
+// LDS cycles of the dQ and dK kernels went to bank conflicts.
+template <int D>
+__device__ __forceinline__ int kswz_t(int row) {
+  return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : kswz<D>(row);
+}
+
 // Source offsets (bytes within one 32-row half) of a wave's direct loads of
-// a row tile (K-like: XOR swizzle kswz by row) and of a VT tile (vswz by d).
+// a row tile (XOR swizzle kswz_t by row) and of a VT tile (vswz by d).
 // Load j of wave w (of NW) fills LDS bytes [1024 (NW j + w), +1024) of the half.
 template <int D, int LPW, int NW>
 __device__ __forceinline__ void tile_offsets(int w, int lane, uint32_t* roff, uint32_t* toff) {
@@ -194,7 +209,7 @@ __device__ __forceinline__ void tile_offsets(int w, int lane, uint32_t* roff, ui
   for (int j = 0; j < LPW; ++j) {
     const int off = (NW * j + w) * 1024 + lane * 16;
     const int row = off / (KCH * 16), pc = (off / 16) % KCH;
-    roff[j] = row * (D * 2) + ((pc ^ kswz<D>(row)) * 16);
+    roff[j] = row * (D * 2) + ((pc ^ kswz_t<D>(row)) * 16);
     const int d = off / 64, pv = (off / 16) & 3;
     toff[j] = d * 64 + ((pv ^ vswz(d)) * 16);
   }
@@ -208,27 +223,36 @@ __device__ __forceinline__ void tile_offsets(int w, int lane, uint32_t* roff, ui
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
 
-// Lane parts of the transposed-read addresses.  For D = 128 the chunk swizzle
-// kswz is row & 15, and every address tr_operand<128> forms is one of two
-// lane constants (for an even or an odd column-tile term) plus an immediate.
+// Lane parts of the transposed-read addresses.  For D = 128 every address
+// tr_operand<128> forms is one of eight lane constants (column tile dt and
+// the first or second 8-row run of a 16-row step) plus an immediate: with
+// r = 16 ks + 8 u + rl the swizzle is 4 (rl % 4) + 2 u + rl / 4, so the
+// physical chunk of logical chunk 4 dt + c (c < 4) is
+// 4 (dt ^ (rl % 4)) + (c ^ (2 u + rl / 4)).
 struct TrBase {
-  uint32_t e, o;
+  uint32_t b[4][2];
 };
 template <int D>
 __device__ __forceinline__ TrBase tr_base(uint32_t ring_lds, int lane) {
+  TrBase t{};
   if constexpr (D == 128) {
     const int g = lane >> 4, s = lane & 15, gb = g >> 1;
-    const int rl = 4 * gb + (s >> 2);                              // row within 8
-    const int clow = (2 * (g & 1) + ((s & 3) >> 1)) ^ (s >> 2);   // low bits of the chunk
-    const uint32_t e = ring_lds + rl * 256 + 16 * (4 * gb + clow) + (s & 1) * 8;
-    return TrBase{e, e - 128 * gb};
+    const int rl = 4 * gb + (s >> 2);                    // row within 8
+    const int c = 2 * (g & 1) + ((s & 3) >> 1);          // logical chunk within the column tile
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        t.b[dt][u] = ring_lds + (8 * u + rl) * 256 + 16 * (4 * (dt ^ (rl & 3)) + (c ^ (2 * u + gb))) + (s & 1) * 8;
   } else {
-    return TrBase{ring_lds, ring_lds};
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) t.b[dt][0] = t.b[dt][1] = ring_lds;
   }
+  return t;
 }
 
 // A operand (32 x 16) of a product whose k index runs over the rows of a
-// 32-row, D-column tile in LDS (16-byte chunks swizzled by kswz, as the row
+// 32-row, D-column tile in LDS (16-byte chunks swizzled by kswz_t, as the row
 // tiles of the ring are stored), taken in the key order of the B operand fed
 // from an S-shaped accumulator: lane (i, h) element e holds row
 // 16 ks + 8 (e / 4) + 4 h + e % 4 at column 32 dt + i.  Two transposed reads,
@@ -237,17 +261,15 @@ template <int D>
 __device__ __forceinline__ bf16x8 tr_operand(uint32_t tile, const TrBase& tb, int dt, int ks, int lane) {
   uint32_t o0, o1;
   if constexpr (D == 128) {
-    // chunk of column 32 dt + 16 (g&1) + 4 (s&3) in row 16 ks + 8 half + rl:
-    // 4 (X ^ (g >> 1)) + clow with X = dt ^ 2 half
-    const int X0 = dt, X1 = dt ^ 2;
-    o0 = ((X0 & 1) ? tb.o : tb.e) + tile + (16 * ks) * 256 + 64 * X0;
-    o1 = ((X1 & 1) ? tb.o : tb.e) + tile + (16 * ks + 8) * 256 + 64 * X1;
+    // column 32 dt + 16 (g&1) + 4 (s&3) of rows 16 ks + rl and 16 ks + 8 + rl
+    o0 = tb.b[dt][0] + tile + (16 * ks) * 256;
+    o1 = tb.b[dt][1] + tile + (16 * ks) * 256;
   } else {
     const int g = lane >> 4, s = lane & 15;
     const int d = 32 * dt + 16 * (g & 1) + 4 * (s & 3);
     const int r0 = 16 * ks + 4 * (g >> 1) + (s >> 2), r1 = r0 + 8;
-    o0 = tb.e + tile + r0 * (D * 2) + (((d >> 3) ^ kswz<D>(r0)) << 4) + ((d & 7) << 1);
-    o1 = tb.e + tile + r1 * (D * 2) + (((d >> 3) ^ kswz<D>(r1)) << 4) + ((d & 7) << 1);
+    o0 = tb.b[0][0] + tile + r0 * (D * 2) + (((d >> 3) ^ kswz_t<D>(r0)) << 4) + ((d & 7) << 1);
+    o1 = tb.b[0][0] + tile + r1 * (D * 2) + (((d >> 3) ^ kswz_t<D>(r1)) << 4) + ((d & 7) << 1);
   }
   // whole-vector casts: element-wise extraction from the builtin's bf16x4
   // result is avoided
@@ -417,7 +439,7 @@ __global__ __launch_bounds__(128 * G, 2) void k_bwd_dq(BwdArgs a) {
     f32x16 s = {}, dp = {};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int c = l32 * KCH + ((2 * ks + h) ^ kswz<D>(l32));
+      const int c = l32 * KCH + ((2 * ks + h) ^ kswz_t<D>(l32));
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kst[c]), qreg[ks], s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vst[c]), doreg[ks], dp, 0, 0, 0);
     }
@@ -569,7 +591,7 @@ __global__ __launch_bounds__(128 * G, G) void k_bwd_dkdv(BwdArgs a) {
     f32x16 s = {};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qst[l32 * KCH + ((2 * ks + h) ^ kswz<D>(l32))]),
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qst[l32 * KCH + ((2 * ks + h) ^ kswz_t<D>(l32))]),
                                                   kreg[ks], s, 0, 0, 0);
     f32x16 p;
 #pragma unroll
@@ -596,7 +618,7 @@ __global__ __launch_bounds__(128 * G, G) void k_bwd_dkdv(BwdArgs a) {
     f32x16 dp = {};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(dst_[l32 * KCH + ((2 * ks + h) ^ kswz<D>(l32))]),
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(dst_[l32 * KCH + ((2 * ks + h) ^ kswz_t<D>(l32))]),
                                                    vreg[ks], dp, 0, 0, 0);
     f32x16 ds;
 #pragma unroll
@@ -773,7 +795,7 @@ __global__ __launch_bounds__(128 * G, OCC) void k_bwd_dkv(BwdArgs a) {
     f32x16 s = {}, dp = {};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int c = l32 * KCH + ((2 * ks + h) ^ kswz<D>(l32));
+      const int c = l32 * KCH + ((2 * ks + h) ^ kswz_t<D>(l32));
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qst[c]), kreg[ks], s, 0, 0, 0);
       if (DK) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(t1[c]), vreg[DK ? ks : 0], dp, 0, 0, 0);
     }
