@@ -598,11 +598,7 @@ __global__ __launch_bounds__(128 * G, G) void k_bwd_dkdv(BwdArgs a) {
     for (int c = 0; c < 4; ++c) {
       const f32x4 L = *(const f32x4*)(lds_l + 8 * c + 4 * h);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = 4 * c + j, qi = 8 * c + 4 * h + j;
-        const float e = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -L[j]));
-        p[r] = (qm >> qi & 1) && kvalid ? e : 0.0f;
-      }
+      for (int j = 0; j < 4; ++j) p[4 * c + j] = __builtin_amdgcn_exp2f(fmaf(s[4 * c + j], sl2, -L[j]));
     }
     {
       const bf16x8 pb0 = __builtin_convertvector(p.lo, bf16x8), pb1 = __builtin_convertvector(p.hi, bf16x8);
@@ -790,7 +786,11 @@ __global__ __launch_bounds__(128 * G, OCC) void k_bwd_dkv(BwdArgs a) {
     const uint4* qst = ring + (DK ? kk : st % NST) * (STAGE / 16);
     const uint4* t1 = qst + HALF / 16;       // dO rows (dK) or dO^T (dV)
     const float* lds_l = (const float*)(qst + NT * HALF / 16);
-    // element r: query 8*(r/4) + 4*h + r%4 of this half, key l32
+    // element r: query 8*(r/4) + 4*h + r%4 of this half, key l32.  No
+    // per-element mask: a pad query has zero Q, dO and delta rows and lse 0,
+    // so its P is exactly 1 and every product it enters (dO^T P for dV,
+    // Q^T dS with dS = P (0 - 0) for dK) adds exact zeros; a pad key's column
+    // only reaches its own output row, which the store writes as zero.
     typedef float f32x4 __attribute__((ext_vector_type(4)));
     f32x16 s = {}, dp = {};
 #pragma unroll
@@ -807,9 +807,8 @@ __global__ __launch_bounds__(128 * G, OCC) void k_bwd_dkv(BwdArgs a) {
       if (DK) Dl = *(const f32x4*)(lds_l + 32 + 8 * c + 4 * h);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int r = 4 * c + j, qi = 8 * c + 4 * h + j;
-        float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -L[j]));
-        if (!(qm >> qi & 1) || !kvalid) p = 0.0f;
+        const int r = 4 * c + j;
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -L[j]));
         x[r] = DK ? p * (dp[r] - Dl[j]) : p;
       }
     }

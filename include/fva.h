@@ -308,6 +308,8 @@ int fva_attention_lse(fva_plan_t plan, const void* q_perm, const void* k_perm, c
  *   q_perm, k_perm, v_perm, do_perm   FVA_LAYOUT_ROWS (fva_permute);
  *   do_vt                             dO in FVA_LAYOUT_VT (K^T and Q^T are
  *                                     read from the row layouts);
+ *                                     the pad rows of all of these must be
+ *                                     zero, as fva_permute writes them;
  *   o32, lse                          outputs of fva_attention_lse on the
  *                                     same Q, K, V and lists;
  *   row_ptr, col_idx                  the forward pass's CSR (set semantics);
