@@ -443,13 +443,21 @@ __global__ __launch_bounds__(128 * G, 2) void k_bwd_dq(BwdArgs a) {
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kst[c]), qreg[ks], s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vst[c]), doreg[ks], dp, 0, 0, 0);
     }
-    // element i: key 8*(i/4) + 4*h + i%4 of this half, query l32
+    // element i: key 8*(i/4) + 4*h + i%4 of this half, query l32.  Pad keys
+    // get s = -inf (P = 0) only in blocks that have any (a uniform branch):
+    // a pad key's zero K row would otherwise meet P = 2^-lse, which need not
+    // be finite
+    if (mh != 0xFFFFFFFFu) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = 8 * (i >> 2) + 4 * h + (i & 3);
+        if (!(mh >> key & 1)) s[i] = -INFINITY;
+      }
+    }
     f32x8 d0, d1;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int key = 8 * (i >> 2) + 4 * h + (i & 3);
-      float p = __builtin_amdgcn_exp2f(fmaf(s[i], sl2, -lse2));
-      if (mh != 0xFFFFFFFFu && !(mh >> key & 1)) p = 0.0f;
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[i], sl2, -lse2));
       const float ds = p * (dp[i] - delta);
       if (i < 8) d0[i] = ds;
       else d1[i - 8] = ds;
@@ -710,36 +718,23 @@ __global__ __launch_bounds__(128 * G, OCC) void k_bwd_dkv(BwdArgs a) {
   const char* dtbase = (const char*)(a.dot + head * D);
   // floats [LDW w, LDW (w+1)) of the stage's [32 lse | 32 delta]
   const float* lbase = (LDW * w < 32 ? a.lse + LDW * w : (const float*)a.delta + (LDW * w - 32)) + head;
-  int issued = 0, curI = 0;
+  int curI = 0;
   const int total = union_steps(un_lo, un_hi);   // two halves per union block
-  auto issue_next = [&]() __attribute__((always_inline)) {
-    if ((issued & 1) == 0) curI = iw.next_known(un_lo, un_hi);
-    const int u = issued & 1;
-    const int64_t roff0 = ((int64_t)curI * 64 + 32 * u) * D * 2;
-    const int64_t toff0 = (int64_t)curI * 64 * D * 2 + u * HALF;
-    const uint32_t dst = lds_addr(ring) + (issued % NST) * STAGE;
-#pragma unroll
-    for (int j = 0; j < LPW; ++j) {
-      const uint32_t o1 = (NW * j + w) * 1024;
-      dma16u(qbase + roff0, roff[j], dst + o1);
-      if (DK) dma16u(dbase + roff0, roff[j], dst + HALF + o1);
-      else dma16u(dtbase + toff0, toff[j], dst + HALF + o1);
-    }
-    if (lane < LDW / 4) dma16u(lbase + (int64_t)curI * 64 + 32 * u, lane * 16, dst + NT * HALF + 4 * LDW * w);
-    ++issued;
-  };
-  // dK only: the same loads into a ring stage and block half known at
-  // compile time (the dK loop below is unrolled by the ring depth, so the
-  // stage offsets need no readfirstlane)
+  // the loads of one step into a ring stage known at compile time (the step
+  // loop below is unrolled by the ring depth, so the stage offsets need no
+  // readfirstlane): Q rows, then dO rows (dK) or dO^T (dV), then lse (and
+  // delta)
   auto issue_at = [&](int stage, int u) __attribute__((always_inline)) {
     if (u == 0) curI = iw.next_known(un_lo, un_hi);
     const int64_t roff0 = ((int64_t)curI * 64 + 32 * u) * D * 2;
+    const int64_t toff0 = (int64_t)curI * 64 * D * 2 + u * HALF;
     const uint32_t dst = lds_addr(ring) + stage * STAGE;
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
       const uint32_t o1 = (NW * j + w) * 1024;
       dma16(qbase + roff0, roff[j], dst + o1);
-      dma16(dbase + roff0, roff[j], dst + HALF + o1);
+      if (DK) dma16(dbase + roff0, roff[j], dst + HALF + o1);
+      else dma16(dtbase + toff0, toff[j], dst + HALF + o1);
     }
     if (lane < LDW / 4) dma16(lbase + (int64_t)curI * 64 + 32 * u, lane * 16, dst + NT * HALF + 4 * LDW * w);
   };
@@ -750,19 +745,15 @@ __global__ __launch_bounds__(128 * G, OCC) void k_bwd_dkv(BwdArgs a) {
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
 #pragma unroll
   for (int st = 0; st < NST - 1; ++st)
-    if (st < total) {
-      if (DK) issue_at(st, st & 1);
-      else issue_next();
-    }
+    if (st < total) issue_at(st, st & 1);
 
   int I = 0;
   // valid-query mask of the current block for this wave (zero when the
   // column does not list it), a scalar word taken once per block
   uint64_t qm64 = 0;
-  // dK: unrolled by the ring depth, so copy kk reads stage kk (offsets fold
-  // into the LDS reads' immediates); dV keeps one copy (its unrolled form
-  // spills at three waves per SIMD)
-  constexpr int UNR = DK ? NST : 1;
+  // unrolled by the ring depth, so copy kk reads stage kk (offsets fold
+  // into the LDS reads' immediates) and loads into stage (kk + NST - 1) % NST
+  constexpr int UNR = NST;
   for (int st0 = 0; st0 < total; st0 += UNR) {
 #pragma unroll
   for (int kk = 0; kk < UNR; ++kk) {
@@ -775,15 +766,12 @@ __global__ __launch_bounds__(128 * G, OCC) void k_bwd_dkv(BwdArgs a) {
     }
     wait_steps<PW, NST>(st, total);
     barrier_no_fence();
-    if (st + NST - 1 < total) {
-      if (DK) issue_at((kk + NST - 1) % NST, (st + NST - 1) & 1);
-      else issue_next();
-    }
+    if (st + NST - 1 < total) issue_at((kk + NST - 1) % NST, (st + NST - 1) & 1);
 
     const int u = st & 1;
     const uint32_t qm = (uint32_t)(qm64 >> (32 * u));
     if (qm == 0) continue;   // not in this column, pad queries, or a wave of pad keys
-    const uint4* qst = ring + (DK ? kk : st % NST) * (STAGE / 16);
+    const uint4* qst = ring + kk * (STAGE / 16);
     const uint4* t1 = qst + HALF / 16;       // dO rows (dK) or dO^T (dV)
     const float* lds_l = (const float*)(qst + NT * HALF / 16);
     // element r: query 8*(r/4) + 4*h + r%4 of this half, key l32.  No
@@ -814,7 +802,7 @@ __global__ __launch_bounds__(128 * G, OCC) void k_bwd_dkv(BwdArgs a) {
     }
     const bf16x8 xb0 = __builtin_convertvector(x.lo, bf16x8), xb1 = __builtin_convertvector(x.hi, bf16x8);
     // dK: Q^T by transposed reads of the stage's Q rows; dV: the dO^T tile
-    const uint32_t qtile = (uint32_t)((DK ? kk : st % NST) * STAGE);
+    const uint32_t qtile = (uint32_t)(kk * STAGE);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const int d = 32 * dt + l32;
