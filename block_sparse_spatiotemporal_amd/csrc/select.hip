@@ -747,11 +747,12 @@ constexpr int kSlackChunk = 16384;   // pairs per histogram workgroup
 __global__ __launch_bounds__(256) void k_slack_hist(const float* __restrict__ S,
                                                     const uint64_t* __restrict__ rowmask, int nw, int n_blk,
                                                     const int32_t* __restrict__ deficit,
+                                                    const int32_t* __restrict__ need,
                                                     const uint64_t* __restrict__ prefix, int level,
                                                     uint32_t* __restrict__ hist) {
   __shared__ unsigned int h[256];
   const int bh = blockIdx.y;
-  if (deficit[bh] <= 0) return;
+  if (deficit[bh] <= 0 || (level > 0 && need[bh] == 0)) return;   // no deficit, or already resolved
   const int shift = 56 - 8 * level;
   const uint64_t pre = prefix[bh];
   h[threadIdx.x] = 0;
@@ -773,13 +774,17 @@ __global__ __launch_bounds__(256) void k_slack_hist(const float* __restrict__ S,
 }
 
 // Per head: keep the digit where the count of larger keys crosses the need,
-// extend the prefix, and clear the histogram for the next level.
+// extend the prefix, and clear the histogram for the next level.  When that
+// digit's whole bin is needed the head is resolved (need 0): the prefix with
+// zero lower digits already admits exactly the bin, so the later levels skip
+// the head (with distinct fp32 scores this happens once the score's four
+// digits are known, so the four index digits are only ever walked for ties).
 __global__ __launch_bounds__(256) void k_slack_pick(uint32_t* __restrict__ hist, const int32_t* __restrict__ deficit,
                                                     int32_t* __restrict__ need, uint64_t* __restrict__ prefix,
                                                     int level) {
   __shared__ unsigned int h[256];
   const int bh = blockIdx.x;
-  if (deficit[bh] <= 0) return;
+  if (deficit[bh] <= 0 || (level > 0 && need[bh] == 0)) return;
   h[threadIdx.x] = hist[bh * 256 + threadIdx.x];
   hist[bh * 256 + threadIdx.x] = 0;
   __syncthreads();
@@ -791,7 +796,7 @@ __global__ __launch_bounds__(256) void k_slack_pick(uint32_t* __restrict__ hist,
     for (int b = 255; b >= 0; --b) {
       if (acc + (int)h[b] >= nd) {
         prefix[bh] = pre | ((uint64_t)b << shift);
-        need[bh] = nd - acc;
+        need[bh] = nd - acc == (int)h[b] ? 0 : nd - acc;
         break;
       }
       acc += h[b];
@@ -1034,7 +1039,7 @@ int select_impl(fva_plan_t plan, const void* q_perm, const void* k_perm, bool po
     const unsigned chunks = (unsigned)(((int64_t)in.n_blk * in.n_blk + kSlackChunk - 1) / kSlackChunk);
     for (int level = 0; level < 8; ++level) {
       hipLaunchKernelGGL(k_slack_hist, dim3(chunks, n_bh), dim3(256), 0, stream, s_read, plan->rowmask, plan->nw,
-                         in.n_blk, plan->deficit, plan->slack_thr, level, plan->slack_hist);
+                         in.n_blk, plan->deficit, plan->slack_need, plan->slack_thr, level, plan->slack_hist);
       hipLaunchKernelGGL(k_slack_pick, dim3(n_bh), dim3(256), 0, stream, plan->slack_hist, plan->deficit,
                          plan->slack_need, plan->slack_thr, level);
     }

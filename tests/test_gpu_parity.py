@@ -120,13 +120,18 @@ def test_select_bit_exact_on_oracle_scores(n_grid, B, H, k_min, p):
     assert np.array_equal(b.head_nnz.cpu().numpy(), O.head_nnz(rp_ref, B, H, n))
 
 
-def test_slack_fill_bit_exact_on_oracle_scores():
+@pytest.mark.parametrize("flat_heads", [0, 2])
+def test_slack_fill_bit_exact_on_oracle_scores(flat_heads):
+    # flat heads: every score equal and a low p, so the head falls short of
+    # the median and its fill is decided by the pair index alone
     rng = np.random.default_rng(5)
     B, H = 1, 9
     plan = fva.Plan(B, H, 128, (9, 10, 13))
     n = plan.n_blk
     S = _random_scores(B, H, n, rng)
     p = rng.uniform(0.3, 0.99, size=H).astype(np.float32)
+    S[0, :flat_heads] = np.float32(1.0 / n)
+    p[:flat_heads] = 0.1
     b = fva.Buffers(plan)
     fva.fva_select(plan, None, None, p.tolist(), 2, b.row_ptr, b.col_idx, slack="median",
                    scores_in=torch.from_numpy(S).cuda(), head_nnz=b.head_nnz)
