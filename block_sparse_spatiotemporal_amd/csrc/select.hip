@@ -737,12 +737,17 @@ __global__ __launch_bounds__(1024) void k_slack_target(const int32_t* __restrict
 }
 
 // Per deficient head: the key (score bits << 32 | ~(I*n + J)) of the d-th best
-// unselected pair, by an 8-level MSD radix select over all n^2 pairs.  Each
-// level is two launches: k_slack_hist spreads a head's pairs over many
-// workgroups (LDS histogram of the level's 8-bit digit among the pairs that
-// match the prefix so far, merged into the head's global histogram), then
-// k_slack_pick finds the digit where the count crosses the remaining need.
-constexpr int kSlackChunk = 16384;   // pairs per histogram workgroup
+// unselected pair, by an MSD radix select over all n^2 pairs, 8 bits a level.
+// Each level is two launches: k_slack_hist spreads a head's pairs over many
+// workgroups (LDS histogram of the level's digit among the pairs that match
+// the prefix so far, merged into the head's global histogram), then
+// k_slack_pick keeps the digit where the count of larger keys crosses the
+// remaining need, extends the prefix and clears the histogram.  When the kept
+// digit's whole bin is needed the head is resolved (need 0): the prefix with
+// zero lower digits already admits exactly that bin, so later levels skip the
+// head.  With distinct fp32 scores that happens once the score's four digits
+// are known, so the four index digits are only walked for ties.
+constexpr int kSlackChunk = 2048;   // pairs per histogram workgroup
 
 __global__ __launch_bounds__(256) void k_slack_hist(const float* __restrict__ S,
                                                     const uint64_t* __restrict__ rowmask, int nw, int n_blk,
@@ -751,56 +756,52 @@ __global__ __launch_bounds__(256) void k_slack_hist(const float* __restrict__ S,
                                                     const uint64_t* __restrict__ prefix, int level,
                                                     uint32_t* __restrict__ hist) {
   __shared__ unsigned int h[256];
-  const int bh = blockIdx.y;
-  if (deficit[bh] <= 0 || (level > 0 && need[bh] == 0)) return;   // no deficit, or already resolved
+  const int bh = blockIdx.y, tid = threadIdx.x;
+  if (deficit[bh] <= 0 || (level > 0 && need[bh] == 0)) return;   // no deficit, or resolved
   const int shift = 56 - 8 * level;
-  const uint64_t pre = prefix[bh];
-  h[threadIdx.x] = 0;
+  const uint64_t pre = level == 0 ? 0 : prefix[bh];
+  h[tid] = 0;
   __syncthreads();
-  const int64_t n = n_blk, nn = n * n;
+  const uint32_t n = (uint32_t)n_blk, nn = n * n;   // n^2 < 2^31: the block lists are int32
   const float* Sh = S + (int64_t)bh * nn;
   const uint64_t* mh = rowmask + (int64_t)bh * n * nw;
-  const int64_t e0 = (int64_t)blockIdx.x * kSlackChunk, e1 = min<int64_t>(e0 + kSlackChunk, nn);
-  for (int64_t e = e0 + threadIdx.x; e < e1; e += 256) {
-    const int64_t I = e / n, J = e - I * n;
+  const uint32_t e0 = blockIdx.x * (uint32_t)kSlackChunk, e1 = min(e0 + (uint32_t)kSlackChunk, nn);
+  for (uint32_t e = e0 + tid; e < e1; e += 256) {
+    const uint32_t I = e / n, J = e - I * n;
     if (mh[I * nw + (J >> 6)] >> (J & 63) & 1) continue;
-    const uint64_t key = ((uint64_t)clamp_bits(Sh[e]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+    const uint64_t key = ((uint64_t)clamp_bits(Sh[e]) << 32) | (uint64_t)(0xFFFFFFFFu - e);
     if (level > 0 && (key >> (shift + 8)) != (pre >> (shift + 8))) continue;
     atomicAdd(&h[(key >> shift) & 0xFF], 1u);
   }
   __syncthreads();
-  const unsigned v = h[threadIdx.x];
-  if (v) atomicAdd(&hist[bh * 256 + threadIdx.x], v);
+  const unsigned v = h[tid];
+  if (v) atomicAdd(&hist[bh * 256 + tid], v);
 }
 
-// Per head: keep the digit where the count of larger keys crosses the need,
-// extend the prefix, and clear the histogram for the next level.  When that
-// digit's whole bin is needed the head is resolved (need 0): the prefix with
-// zero lower digits already admits exactly the bin, so the later levels skip
-// the head (with distinct fp32 scores this happens once the score's four
-// digits are known, so the four index digits are only ever walked for ties).
+// Thread t holds digit 255 - t: an inclusive scan gives the count of keys
+// whose digit is at least its own, and exactly one thread holds the crossing.
 __global__ __launch_bounds__(256) void k_slack_pick(uint32_t* __restrict__ hist, const int32_t* __restrict__ deficit,
                                                     int32_t* __restrict__ need, uint64_t* __restrict__ prefix,
                                                     int level) {
-  __shared__ unsigned int h[256];
-  const int bh = blockIdx.x;
-  if (deficit[bh] <= 0 || (level > 0 && need[bh] == 0)) return;
-  h[threadIdx.x] = hist[bh * 256 + threadIdx.x];
-  hist[bh * 256 + threadIdx.x] = 0;
+  __shared__ int wtot[4];
+  const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int nd = level == 0 ? deficit[bh] : need[bh];   // every thread reads it before one rewrites it
+  if (deficit[bh] <= 0 || nd <= 0) return;
+  const int shift = 56 - 8 * level;
+  const uint64_t pre = level == 0 ? 0 : prefix[bh];
+  uint32_t* hh = hist + bh * 256 + 255 - tid;
+  const int c = (int)*hh;
+  *hh = 0;
+  const int incl = wave_incl_scan<int>(c, lane);
+  if (lane == 63) wtot[wv] = incl;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const int shift = 56 - 8 * level;
-    const int nd = level == 0 ? deficit[bh] : need[bh];
-    const uint64_t pre = level == 0 ? 0 : prefix[bh];
-    int acc = 0;
-    for (int b = 255; b >= 0; --b) {
-      if (acc + (int)h[b] >= nd) {
-        prefix[bh] = pre | ((uint64_t)b << shift);
-        need[bh] = nd - acc == (int)h[b] ? 0 : nd - acc;
-        break;
-      }
-      acc += h[b];
-    }
+  int before = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) before += k < wv ? wtot[k] : 0;
+  const int hi = before + incl, lo = hi - c;
+  if (lo < nd && nd <= hi) {
+    prefix[bh] = pre | ((uint64_t)(255 - tid) << shift);
+    need[bh] = nd == hi ? 0 : nd - lo;
   }
 }
 
