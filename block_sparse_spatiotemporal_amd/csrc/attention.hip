@@ -103,7 +103,11 @@ __device__ __forceinline__ T* out_row(const AttnArgs& a, int bh, int64_t pos, in
 // swizzle is applied by choosing each lane's source address, since a direct
 // load writes lane i's 16 bytes at offset 16*i of its 1 KB destination.
 // The running max is raised lazily: P may grow to 2^kLazy before O and l are
-// rescaled, which skips most rescales once the row maximum is found.
+// rescaled, which skips most rescales once the row maximum is found.  The
+// inference form takes the scale (1/sqrt(D) in log2 units) into Q when it
+// loads Q, rounding the scaled Q to bf16, and starts each S accumulator at
+// minus the running max, so a weight is one exp2 of an accumulator with no
+// multiply or shift per score.
 
 // G query blocks per workgroup (2G waves; wave w serves block w/2, queries
 // 32*(w%2)..+31).  Steps walk the union of the G block lists half by half;
@@ -225,6 +229,14 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
       const uint4* qrow = (const uint4*)(a.q + (head + (int64_t)I * 64 + 32 * w2 + l32) * D);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qreg[ks] = as_bf16x8(qrow[2 * ks + h]);
+      if constexpr (!LSE) {   // Q . scale in log2 units, rounded to bf16
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          f32x8 qf = __builtin_convertvector(qreg[ks], f32x8);
+          qf *= sl2;
+          qreg[ks] = __builtin_convertvector(qf, bf16x8);
+        }
+      }
       // Settle the Q loads before any direct load is issued: a wait left to
       // the first use inside the step loop would also count, every step, the
       // direct loads in flight behind them.
@@ -234,6 +246,10 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
     float m_run = -INFINITY, l_run = 0.0f;
+    // inference form: the accumulators start at -base; base is 0 until the
+    // first step raises the running max, and equals it from then on
+    f32x16 negm = {};
+    float thr = -INFINITY;   // a lane raises its max once a score exceeds base + thr
 
 #pragma unroll
     for (int st = 0; st < NST - 1; ++st)
@@ -273,13 +289,16 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
       const uint4* kst = ring + kk * (STAGE / 16);
       const uint4* vst = kst + HALF / 16;
 
-      f32x16 s = {};
+      f32x16 s;
+      if constexpr (LSE) s = f32x16{};
+      else s = negm;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kst[l32 * KCH + ((2 * ks + h) ^ kswz<D>(l32))]),
                                                     qreg[ks], s, 0, 0, 0);
       // s[i]: key 8*(i/4) + 4*h + i%4 of this half, query l32.  Pad keys get
-      // -inf; the scale (1/sqrt(D) in log2 units, > 0) is applied after the max.
+      // -inf.  Training form: the scale (1/sqrt(D) in log2 units, > 0) is
+      // applied after the max; inference form: s is already scaled and shifted.
       if (mh != 0xFFFFFFFFu) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -291,21 +310,45 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
 #pragma unroll
       for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s[i]), s[i + 1]);
       mx = fmaxf(mx, s[15]);
-      mx = xhalf_max(mx) * sl2;
-      if (__ballot(mx > m_run + kLazy)) {   // raise the running max (first step always)
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
-        m_run = m_new;
-      }
-      const float nm = -m_run;
       f32x8 p0, p1;
+      if constexpr (LSE) {
+        mx = xhalf_max(mx) * sl2;
+        if (__ballot(mx > m_run + kLazy)) {   // raise the running max (first step always)
+          const float m_new = fmaxf(m_run, mx);
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+          l_run *= alpha;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        p0[i] = __builtin_amdgcn_exp2f(fmaf(s[i], sl2, nm));
-        p1[i] = __builtin_amdgcn_exp2f(fmaf(s[8 + i], sl2, nm));
+          for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+          m_run = m_new;
+        }
+        const float nm = -m_run;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          p0[i] = __builtin_amdgcn_exp2f(fmaf(s[i], sl2, nm));
+          p1[i] = __builtin_amdgcn_exp2f(fmaf(s[8 + i], sl2, nm));
+        }
+      } else {
+        mx = xhalf_max(mx);   // over scores already less base
+        if (__ballot(mx > thr)) {   // raise the running max (first step always)
+          const float base = -negm[0];
+          const float m_new = fmaxf(m_run, base + mx);
+          const float delta = m_new - base;
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+          l_run *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) s[i] -= delta;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) negm[i] = -m_new;
+          m_run = m_new;
+          thr = kLazy;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          p0[i] = __builtin_amdgcn_exp2f(s[i]);
+          p1[i] = __builtin_amdgcn_exp2f(s[8 + i]);
+        }
       }
       const bf16x8 pb0 = __builtin_convertvector(p0, bf16x8);
       const bf16x8 pb1 = __builtin_convertvector(p1, bf16x8);
