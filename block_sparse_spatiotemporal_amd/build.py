@@ -15,6 +15,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfva.so")
 SOURCES = ["plan.cpp", "permute.hip", "select.hip", "attention.hip", "backward.hip"]
+# The attention kernels take row maxima of matrix-core results, which in IEEE
+# mode cost a NaN-quieting max per operand; they compute no NaN from finite
+# inputs, so that file is built without IEEE mode and without NaN semantics.
+EXTRA = {"attention.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
 
 
 def hipcc() -> str:
@@ -33,7 +37,7 @@ def build(verbose: bool = False) -> str:
     objs, cmds = [], []
     for src in SOURCES:
         obj = os.path.join(objdir, src + ".o")
-        cmd = [hipcc()] + common + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc()] + common + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
         cmd[1:1] = ["-x", "hip", "--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang",
                     "-packed-fp32-ops", "-ffp-contract=fast"]
         if verbose:
