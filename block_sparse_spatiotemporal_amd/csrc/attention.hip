@@ -103,11 +103,15 @@ __device__ __forceinline__ T* out_row(const AttnArgs& a, int bh, int64_t pos, in
 // swizzle is applied by choosing each lane's source address, since a direct
 // load writes lane i's 16 bytes at offset 16*i of its 1 KB destination.
 // The running max is raised lazily: P may grow to 2^kLazy before O and l are
-// rescaled, which skips most rescales once the row maximum is found.  The
-// inference form takes the scale (1/sqrt(D) in log2 units) into Q when it
-// loads Q, rounding the scaled Q to bf16, and starts each S accumulator at
-// minus the running max, so a weight is one exp2 of an accumulator with no
-// multiply or shift per score.
+// rescaled, which skips most rescales once the row maximum is found.
+// FOLD (the default inference form) takes the scale (1/sqrt(D) in log2
+// units) into Q when it loads Q, rounding the scaled Q to bf16, and starts
+// each S accumulator at minus the running max, so a weight is one exp2 of
+// an accumulator with no multiply or shift per score.  The extra rounding
+// of Q moves a logit by up to 2^-9 of |q . k| * scale, which grows with the
+// logit range; without FOLD (the training form, and the inference form's
+// exact-scale variant) S stays exact in fp32 and one fma applies the scale
+// and the shift.
 
 // G query blocks per workgroup (2G waves; wave w serves block w/2, queries
 // 32*(w%2)..+31).  Steps walk the union of the G block lists half by half;
@@ -118,8 +122,9 @@ __device__ __forceinline__ T* out_row(const AttnArgs& a, int bh, int64_t pos, in
 // fp32 accuracy), and writes lse and the fp32 output.  The inference form
 // sums the bf16 weights PV uses, with dot instructions: half the adds, and
 // O normalised by exactly the weights applied to V.
-template <int D, int NST, int G, bool LSE>
+template <int D, int NST, int G, bool LSE, bool FOLD = !LSE>
 __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
+  static_assert(!(LSE && FOLD), "the training form keeps S exact");
   constexpr int NW = 2 * G;             // waves per workgroup
   constexpr int KS = D / 16;            // k-steps of S^T
   constexpr int DT = D / 32;            // d tiles of O^T
@@ -229,7 +234,7 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
       const uint4* qrow = (const uint4*)(a.q + (head + (int64_t)I * 64 + 32 * w2 + l32) * D);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qreg[ks] = as_bf16x8(qrow[2 * ks + h]);
-      if constexpr (!LSE) {   // Q . scale in log2 units, rounded to bf16
+      if constexpr (FOLD) {   // Q . scale in log2 units, rounded to bf16
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           f32x8 qf = __builtin_convertvector(qreg[ks], f32x8);
@@ -290,15 +295,15 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
       const uint4* vst = kst + HALF / 16;
 
       f32x16 s;
-      if constexpr (LSE) s = f32x16{};
+      if constexpr (!FOLD) s = f32x16{};
       else s = negm;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kst[l32 * KCH + ((2 * ks + h) ^ kswz<D>(l32))]),
                                                     qreg[ks], s, 0, 0, 0);
       // s[i]: key 8*(i/4) + 4*h + i%4 of this half, query l32.  Pad keys get
-      // -inf.  Training form: the scale (1/sqrt(D) in log2 units, > 0) is
-      // applied after the max; inference form: s is already scaled and shifted.
+      // -inf.  Without FOLD the scale (1/sqrt(D) in log2 units, > 0) is
+      // applied after the max; with FOLD s is already scaled and shifted.
       if (mh != 0xFFFFFFFFu) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -311,7 +316,7 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
       for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s[i]), s[i + 1]);
       mx = fmaxf(mx, s[15]);
       f32x8 p0, p1;
-      if constexpr (LSE) {
+      if constexpr (!FOLD) {
         mx = xhalf_max(mx) * sl2;
         if (__ballot(mx > m_run + kLazy)) {   // raise the running max (first step always)
           const float m_new = fmaxf(m_run, mx);
@@ -743,6 +748,16 @@ int attn_stages() {
   return n;
 }
 
+// FVA_ATTN_EXACT_SCALE=1: the inference form keeps S exact in fp32 and
+// applies the scale with one fma per score instead of folding it into a bf16
+// rounding of Q (for inputs whose logits span tens of log2 units, where that
+// rounding moves outputs by more than the bf16 output error).  It runs the
+// default launch shape: two query blocks per workgroup, a two-stage ring.
+bool attn_exact_scale() {
+  const char* v = getenv("FVA_ATTN_EXACT_SCALE");
+  return v && atoi(v) == 1;
+}
+
 template <typename K>
 int occupancy(K kernel, int threads) {
   int nb = 0;
@@ -771,7 +786,9 @@ static int attention_launch(fva_plan_t plan, const void* q_perm, const void* k_p
   const fva_plan_desc& d = plan->desc;
   const fva_plan_info& in = plan->info;
   const int n_bh = d.batch * d.heads;
-  int G = d.dtype == FVA_DTYPE_BF16 ? (lse ? 2 : attn_group()) : 1;   // the training form is G = 2 only
+  const bool exact = d.dtype == FVA_DTYPE_BF16 && !lse && attn_exact_scale();
+  // the training form and the exact-scale inference form are G = 2 only
+  int G = d.dtype == FVA_DTYPE_BF16 ? (lse || exact ? 2 : attn_group()) : 1;
   if (d.head_dim == 64 && G > 2) G = 2;   // a 4 KB half splits over at most 4 waves
   const bool paired = G == 2 && attn_pair() == 1;
   const int64_t n_items = (int64_t)n_bh * ((in.n_blk + G - 1) / G);
@@ -839,6 +856,9 @@ static int attention_launch(fva_plan_t plan, const void* q_perm, const void* k_p
     if (lse) {   // training forward: the default shape only
       if (d.head_dim == 128) FVA_LAUNCH((k_attn_bf16<128, 2, 2, true>), 256);
       else FVA_LAUNCH((k_attn_bf16<64, 2, 2, true>), 256);
+    } else if (exact) {
+      if (d.head_dim == 128) FVA_LAUNCH((k_attn_bf16<128, 2, 2, false, false>), 256);
+      else FVA_LAUNCH((k_attn_bf16<64, 2, 2, false, false>), 256);
     } else if (d.head_dim == 128) {
       if (ns == 2) { FVA_BF16_128(2) }
       else if (ns == 3) { FVA_BF16_128(3) }

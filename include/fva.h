@@ -264,6 +264,13 @@ int fva_select_pooled(fva_plan_t plan, const float* p, int32_t p_count, int32_t 
  *                   start and end of its busy time (100 MHz wall clock).
  * bf16: QK^T and PV run on bf16 matrix cores with fp32 accumulation, the
  * softmax in fp32, P rounded to bf16 before PV, O rounded to bf16 at the end.
+ * By default Q enters the products multiplied by the softmax scale in log2
+ * units (1/sqrt(D) * log2 e) and rounded to bf16 once more, which moves a
+ * logit by up to 2^-9 of sum_d |q_d k_d| * scale: well inside the bf16 output
+ * error for logits spanning a few log2 units, growing beyond it for rows
+ * whose logits span tens.  With the environment variable
+ * FVA_ATTN_EXACT_SCALE=1 set at the call, S stays exact in fp32 and the
+ * scale is applied per score (about 6% slower).
  * fp32: fp32 throughout. */
 int fva_attention(fva_plan_t plan, const void* q_perm, const void* k_perm, const void* vt_perm,
                   const int32_t* row_ptr, const int32_t* col_idx, void* o_perm,

@@ -181,6 +181,37 @@ def test_end_to_end_vs_oracle(w, sched):
     assert err < tol, err
 
 
+@pytest.mark.parametrize("qscale", [1.0, 8.0])
+def test_exact_scale_form_vs_oracle(monkeypatch, qscale):
+    """FVA_ATTN_EXACT_SCALE=1 keeps S exact in fp32 and applies the scale
+    per score.  With Q times 8 (exact in bf16) the logits of a row span
+    tens of log2 units; the exact-scale form stays within the bf16 output
+    tolerance of the oracle there, and the default form (scale folded into a
+    bf16 rounding of Q) stays within it at the inputs' own scale."""
+    w = synth.scaled(synth.WORKLOADS["wan1.3b_480p"], H=2, grid=(9, 10, 13))
+    plan, opl, (q, k, v), (q64, k64, v64), _ = _plan_and_inputs(w)
+    q = q * qscale
+    q64 = q64 * qscale
+    errs = {}
+    for mode in ("exact", "fold"):
+        if mode == "exact":
+            monkeypatch.setenv("FVA_ATTN_EXACT_SCALE", "1")
+        else:
+            monkeypatch.delenv("FVA_ATTN_EXACT_SCALE", raising=False)
+        b = fva.Buffers(plan)
+        out = torch.empty_like(q)
+        fva.attention_call(plan, q, k, v, out, 0.9, 16, b)
+        torch.cuda.synchronize()
+        rp = b.row_ptr.cpu().numpy().astype(np.int64)
+        ci = b.col_idx[: rp[-1]].cpu().numpy().astype(np.int64)
+        ref = O.unpermute(O.attention(O.permute(q64, opl), O.permute(k64, opl), O.permute(v64, opl), rp, ci, opl), opl)
+        errs[mode] = float(np.max(np.abs(to_f64(out) - ref)))
+    print(f"q x {qscale}: max abs error exact-scale {errs['exact']:.3g}, folded {errs['fold']:.3g}")
+    assert errs["exact"] < 2e-2
+    if qscale == 1.0:
+        assert errs["fold"] < 2e-2
+
+
 def test_persistent_and_plain_bitwise_equal():
     w = synth.scaled(synth.WORKLOADS["wan1.3b_480p"], H=3, grid=(9, 10, 13))
     plan, opl, (q, k, v), _, meta = _plan_and_inputs(w)
