@@ -311,15 +311,17 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
           if (!(mh >> key & 1)) s[i] = -INFINITY;
         }
       }
+      // The lazy test needs only this lane's 16 scores: some lane of the
+      // wave exceeds the threshold exactly when some query's row does.  The
+      // max over the other lane half (same query) is taken on a raise only.
       float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
 #pragma unroll
       for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s[i]), s[i + 1]);
       mx = fmaxf(mx, s[15]);
       f32x8 p0, p1;
       if constexpr (!FOLD) {
-        mx = xhalf_max(mx) * sl2;
-        if (__ballot(mx > m_run + kLazy)) {   // raise the running max (first step always)
-          const float m_new = fmaxf(m_run, mx);
+        if (__ballot(mx * sl2 > m_run + kLazy)) {   // raise the running max (first step always)
+          const float m_new = fmaxf(m_run, xhalf_max(mx) * sl2);
           const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
           l_run *= alpha;
 #pragma unroll
@@ -333,10 +335,10 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
           p1[i] = __builtin_amdgcn_exp2f(fmaf(s[8 + i], sl2, nm));
         }
       } else {
-        mx = xhalf_max(mx);   // over scores already less base
+        // scores are already less base
         if (__ballot(mx > thr)) {   // raise the running max (first step always)
           const float base = -negm[0];
-          const float m_new = fmaxf(m_run, base + mx);
+          const float m_new = fmaxf(m_run, base + xhalf_max(mx));
           const float delta = m_new - base;
           const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
           l_run *= alpha;
