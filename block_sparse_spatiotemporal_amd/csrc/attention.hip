@@ -304,11 +304,12 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
       // s[i]: key 8*(i/4) + 4*h + i%4 of this half, query l32.  Pad keys get
       // -inf.  Without FOLD the scale (1/sqrt(D) in log2 units, > 0) is
       // applied after the max; with FOLD s is already scaled and shifted.
-      if (mh != 0xFFFFFFFFu) {
+      if (mh != 0xFFFFFFFFu) {   // per register: a sign-extended bit, one three-input bit op
+        const uint32_t ml = mh >> (4 * h);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = 8 * (i >> 2) + 4 * h + (i & 3);
-          if (!(mh >> key & 1)) s[i] = -INFINITY;
+          const uint32_t vm = (uint32_t)__builtin_amdgcn_sbfe((int)ml, 8 * (i >> 2) + (i & 3), 1);
+          s[i] = __uint_as_float((__float_as_uint(s[i]) & vm) | (~vm & 0xFF800000u));   // else -inf
         }
       }
       // The lazy test needs only this lane's 16 scores: some lane of the
