@@ -297,10 +297,15 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
       f32x16 s;
       if constexpr (!FOLD) s = f32x16{};
       else s = negm;
+      // All of the step's K operand reads are issued ahead of the products
+      // (the scheduling fence keeps the compiler from trickling them in two
+      // at a time, which left each product waiting out an LDS latency).
+      bf16x8 kf[KS];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kst[l32 * KCH + ((2 * ks + h) ^ kswz<D>(l32))]),
-                                                    qreg[ks], s, 0, 0, 0);
+      for (int ks = 0; ks < KS; ++ks) kf[ks] = as_bf16x8(kst[l32 * KCH + ((2 * ks + h) ^ kswz<D>(l32))]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qreg[ks], s, 0, 0, 0);
       // s[i]: key 8*(i/4) + 4*h + i%4 of this half, query l32.  Pad keys get
       // -inf.  Without FOLD the scale (1/sqrt(D) in log2 units, > 0) is
       // applied after the max; with FOLD s is already scaled and shifted.
@@ -312,6 +317,17 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
           s[i] = __uint_as_float((__float_as_uint(s[i]) & vm) | (~vm & 0xFF800000u));   // else -inf
         }
       }
+      // The V^T operands of the PV products are read now, so their LDS
+      // latency passes under the softmax.
+      bf16x8 vf[2 * DT];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int d = 32 * dt + l32;
+        const int sw = vswz(d);
+        vf[2 * dt] = as_bf16x8(vst[d * 4 + ((0 + h) ^ sw)]);
+        vf[2 * dt + 1] = as_bf16x8(vst[d * 4 + ((2 + h) ^ sw)]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
       // The lazy test needs only this lane's 16 scores: some lane of the
       // wave exceeds the threshold exactly when some query's row does.  The
       // max over the other lane half (same query) is taken on a raise only.
@@ -375,10 +391,8 @@ __global__ __launch_bounds__(128 * G, 2) void k_attn_bf16(AttnArgs a) {
       }
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const int d = 32 * dt + l32;
-        const int sw = vswz(d);
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vst[d * 4 + ((0 + h) ^ sw)]), pb0, o[dt], 0, 0, 0);
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vst[d * 4 + ((2 + h) ^ sw)]), pb1, o[dt], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[2 * dt], pb0, o[dt], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[2 * dt + 1], pb1, o[dt], 0, 0, 0);
       }
     }
     }
