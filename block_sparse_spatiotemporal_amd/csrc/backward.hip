@@ -8,7 +8,8 @@
 // Each kernel owns its outputs outright (no atomics, so the gradients are
 // bitwise reproducible):
 //   k_bwd_dq    groups of query blocks, walking their rows of the selection
-//               (like the forward pass); also writes delta;
+//               (like the forward pass); also writes minus delta, where
+//               the dK products start their dP accumulators (dS = P * dP);
 //   k_bwd_dkv   groups of key blocks, walking the transposed selection (the
 //               query blocks that listed them), once for dV and once for dK;
 //   k_bwd_dkdv  dK and dV in one kernel (a selectable variant: holding both
@@ -85,7 +86,7 @@ struct BwdArgs {
   const uint64_t* bits_t;   // [n_rows][nw] key block -> query blocks
   const uint64_t* blk_mask;
   const uint64_t* blk_full;
-  float* delta;             // [B*H, n_pad]
+  float* ndelta;            // [B*H, n_pad]: minus delta, the start value of the dK kernel's dP
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
@@ -380,7 +381,7 @@ __global__ __launch_bounds__(128 * G, 2) void k_bwd_dq(BwdArgs a) {
     lse2 = qvalid ? a.lse[tok] : INFINITY;   // pad queries: P = 0
     // settle these loads before the ring's direct loads are counted
     wait_vm<0>();
-    if (h == 0 && has_row) a.delta[tok] = delta;
+    if (h == 0 && has_row) a.ndelta[tok] = -delta;
   }
 
   BitWalk iw, cw;
@@ -490,7 +491,7 @@ __global__ __launch_bounds__(128 * G, 2) void k_bwd_dq(BwdArgs a) {
 //   dV^T (D x 32 keys) += dO^T_half . P,   dK^T += Q^T_half . dS
 // The ring stage holds Q rows, dO rows and dO^T (VT layout) of the half
 // (Q^T is read from the Q rows by transposed LDS reads), and the half's 32
-// lse then 32 delta values (each wave brings 256/NW bytes of those).
+// lse then 32 minus-delta values (each wave brings 256/NW bytes of those).
 template <int D, int NST, int G>
 __global__ __launch_bounds__(128 * G, G) void k_bwd_dkdv(BwdArgs a) {
   constexpr int NW = 2 * G;
@@ -541,8 +542,8 @@ __global__ __launch_bounds__(128 * G, G) void k_bwd_dkdv(BwdArgs a) {
   const char* qbase = (const char*)(a.q + head * D);
   const char* dbase = (const char*)(a.dout + head * D);
   const char* dtbase = (const char*)(a.dot + head * D);
-  // floats [LDW w, LDW (w+1)) of the stage's [32 lse | 32 delta]
-  const float* lbase = (LDW * w < 32 ? a.lse + LDW * w : (const float*)a.delta + (LDW * w - 32)) + head;
+  // floats [LDW w, LDW (w+1)) of the stage's [32 lse | 32 -delta]
+  const float* lbase = (LDW * w < 32 ? a.lse + LDW * w : (const float*)a.ndelta + (LDW * w - 32)) + head;
   int issued = 0, curI = 0;
   const int total = union_steps(un_lo, un_hi);   // two halves per union block
   auto issue_next = [&]() __attribute__((always_inline)) {
@@ -619,18 +620,20 @@ __global__ __launch_bounds__(128 * G, G) void k_bwd_dkdv(BwdArgs a) {
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    f32x16 dp = {};
+    f32x16 dp;   // starts at minus delta (the stage holds -delta), so dS = P * dP
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const f32x4 nD = *(const f32x4*)(lds_l + 32 + 8 * c + 4 * h);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dp[4 * c + j] = nD[j];
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(dst_[l32 * KCH + ((2 * ks + h) ^ kswz_t<D>(l32))]),
                                                    vreg[ks], dp, 0, 0, 0);
     f32x16 ds;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const f32x4 Dl = *(const f32x4*)(lds_l + 32 + 8 * c + 4 * h);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) ds[4 * c + j] = p[4 * c + j] * (dp[4 * c + j] - Dl[j]);
-    }
+    for (int r = 0; r < 16; ++r) ds[r] = p[r] * dp[r];
     {
       const bf16x8 db0 = __builtin_convertvector(ds.lo, bf16x8), db1 = __builtin_convertvector(ds.hi, bf16x8);
 #pragma unroll
@@ -662,7 +665,7 @@ __global__ __launch_bounds__(128 * G, G) void k_bwd_dkdv(BwdArgs a) {
 //        stage: Q rows, dO^T (VT layout), 32 lse
 //   dK:  S = Q_half . K^T,  dP = dO_half . V^T,  P,  dS = P (dP - delta),
 //        dK^T += Q^T_half . dS
-//        stage: Q rows, dO rows, 32 lse, 32 delta (Q^T by transposed reads
+//        stage: Q rows, dO rows, 32 lse, 32 -delta (Q^T by transposed reads
 //        of the Q rows)
 template <int D, int NST, int G, bool DK, int OCC>
 __global__ __launch_bounds__(128 * G, OCC) void k_bwd_dkv(BwdArgs a) {
@@ -716,8 +719,8 @@ __global__ __launch_bounds__(128 * G, OCC) void k_bwd_dkv(BwdArgs a) {
   const char* qbase = (const char*)(a.q + head * D);
   const char* dbase = (const char*)(a.dout + head * D);
   const char* dtbase = (const char*)(a.dot + head * D);
-  // floats [LDW w, LDW (w+1)) of the stage's [32 lse | 32 delta]
-  const float* lbase = (LDW * w < 32 ? a.lse + LDW * w : (const float*)a.delta + (LDW * w - 32)) + head;
+  // floats [LDW w, LDW (w+1)) of the stage's [32 lse | 32 -delta]
+  const float* lbase = (LDW * w < 32 ? a.lse + LDW * w : (const float*)a.ndelta + (LDW * w - 32)) + head;
   int curI = 0;
   const int total = union_steps(un_lo, un_hi);   // two halves per union block
   // the loads of one step into a ring stage known at compile time (the step
@@ -781,6 +784,14 @@ __global__ __launch_bounds__(128 * G, OCC) void k_bwd_dkv(BwdArgs a) {
     // only reaches its own output row, which the store writes as zero.
     typedef float f32x4 __attribute__((ext_vector_type(4)));
     f32x16 s = {}, dp = {};
+    if (DK) {   // dP starts at minus delta (the stage holds -delta), so dS = P * dP
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const f32x4 nD = *(const f32x4*)(lds_l + 32 + 8 * c + 4 * h);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dp[4 * c + j] = nD[j];
+      }
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int c = l32 * KCH + ((2 * ks + h) ^ kswz_t<D>(l32));
@@ -791,13 +802,11 @@ __global__ __launch_bounds__(128 * G, OCC) void k_bwd_dkv(BwdArgs a) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const f32x4 L = *(const f32x4*)(lds_l + 8 * c + 4 * h);
-      f32x4 Dl = {};
-      if (DK) Dl = *(const f32x4*)(lds_l + 32 + 8 * c + 4 * h);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = 4 * c + j;
         const float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -L[j]));
-        x[r] = DK ? p * (dp[r] - Dl[j]) : p;
+        x[r] = DK ? p * dp[r] : p;
       }
     }
     const bf16x8 xb0 = __builtin_convertvector(x.lo, bf16x8), xb1 = __builtin_convertvector(x.hi, bf16x8);
@@ -951,7 +960,7 @@ extern "C" int fva_attention_backward(fva_plan_t plan, const void* q_perm, const
   a.bits_t = plan->bits_t;
   a.blk_mask = plan->blk_mask;
   a.blk_full = plan->blk_full;
-  a.delta = plan->bwd_delta;
+  a.ndelta = plan->bwd_delta;
   a.dq = (uint16_t*)dq_perm;
   a.dk = (uint16_t*)dk_perm;
   a.dv = (uint16_t*)dv_perm;
