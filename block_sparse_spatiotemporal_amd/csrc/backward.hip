@@ -444,6 +444,11 @@ __global__ __launch_bounds__(128 * G, 2) void k_bwd_dq(BwdArgs a) {
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kst[c]), qreg[ks], s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vst[c]), doreg[ks], dp, 0, 0, 0);
     }
+    // From the exponentials to the end of the step's last products the wave
+    // runs at a raised priority, as in the forward kernel: a wave finishing
+    // a step issues ahead of a co-resident wave starting one (bit-identical;
+    // backward kernels 52.3 -> 51.1 ms at the Wan-14B 480P shape).
+    __builtin_amdgcn_s_setprio(2);
     // element i: key 8*(i/4) + 4*h + i%4 of this half, query l32.  Pad keys
     // get s = -inf (P = 0) only in blocks that have any (a uniform branch):
     // a pad key's zero K row would otherwise meet P = 2^-lse, which need not
@@ -470,6 +475,7 @@ __global__ __launch_bounds__(128 * G, 2) void k_bwd_dq(BwdArgs a) {
       acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(kk * STAGE, trb, dt, 0, lane), db0, acc[dt], 0, 0, 0);
       acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(kk * STAGE, trb, dt, 1, lane), db1, acc[dt], 0, 0, 0);
     }
+    __builtin_amdgcn_s_setprio(0);
   }
   }
   if (!has_row) continue;
@@ -798,6 +804,7 @@ __global__ __launch_bounds__(128 * G, OCC) void k_bwd_dkv(BwdArgs a) {
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qst[c]), kreg[ks], s, 0, 0, 0);
       if (DK) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(t1[c]), vreg[DK ? ks : 0], dp, 0, 0, 0);
     }
+    __builtin_amdgcn_s_setprio(2);   // raised priority to the end of the step, as in k_bwd_dq
     f32x16 x;   // P (dV) or dS (dK)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -821,6 +828,7 @@ __global__ __launch_bounds__(128 * G, OCC) void k_bwd_dkv(BwdArgs a) {
       acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, xb0, acc[dt], 0, 0, 0);
       acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, xb1, acc[dt], 0, 0, 0);
     }
+    __builtin_amdgcn_s_setprio(0);
   }
   }
   if (!has_blk) continue;
