@@ -798,10 +798,21 @@ __global__ __launch_bounds__(128 * G, OCC) void k_bwd_dkv(BwdArgs a) {
         for (int j = 0; j < 4; ++j) dp[4 * c + j] = nD[j];
       }
     }
+    // dK: the eight Q operand reads of the S products are issued together
+    // ahead of them, held there by a scheduling fence, as in the forward
+    // kernel (246 VGPRs; backward kernels 51.0 -> 50.7 ms at the Wan-14B
+    // 480P shape, bit-identical).  The dV form, at three waves per SIMD, has
+    // no registers to spare for it.
+    bf16x8 qf[KS];
+    if constexpr (DK) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[ks] = as_bf16x8(qst[l32 * KCH + ((2 * ks + h) ^ kswz_t<D>(l32))]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int c = l32 * KCH + ((2 * ks + h) ^ kswz_t<D>(l32));
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qst[c]), kreg[ks], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(DK ? qf[ks] : as_bf16x8(qst[c]), kreg[ks], s, 0, 0, 0);
       if (DK) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(t1[c]), vreg[DK ? ks : 0], dp, 0, 0, 0);
     }
     __builtin_amdgcn_s_setprio(2);   // raised priority to the end of the step, as in k_bwd_dq
