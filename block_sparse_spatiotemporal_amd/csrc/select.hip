@@ -382,6 +382,7 @@ __global__ __launch_bounds__(256, 3) void k_score(const double* __restrict__ qba
     wave_sync_lds();
   };
   double m_run = -INFINITY;
+  double c_held = -INFINITY, e_held = 0.0;   // block max and sum of a held even tile (sub-blocks)
   // The products of tile kt run on the matrix cores while the same wave does
   // the fp64 log-sum-exp of tile kt-1 (independent work, so the two overlap
   // inside the wave): the loop carries the previous tile's accumulator.
@@ -420,7 +421,12 @@ __global__ __launch_bounds__(256, 3) void k_score(const double* __restrict__ qba
       // acc[i] is sub-key 4g + i of the tile: sub-block 4 (g % 2) + i of
       // block kt*2 + g/2.  Log-sum-exp over the block's 8 sub-blocks (4 per
       // lane, lane groups g and g ^ 1): the max first, then one exponential
-      // per sub-block; lane groups 0 and 2 write the two blocks' logits.
+      // per sub-block.  Lane groups g and g ^ 1 then hold the same block
+      // max c and sum e, so a tile's log would be taken twice: an even tile
+      // keeps (c, e) instead, and the next (odd) tile takes one log for
+      // both, the even lane groups for the held tile's blocks and the odd
+      // ones for its own.  A tile with no partner in the range (first and
+      // odd, or last and even) takes its own log.
       const int blk = kt * 2 + (g >> 1);
       const uint32_t ok = blk < n_blk ? (uint32_t)sub_ok[blk] >> (4 * (g & 1)) : 0u;
       double v[4];
@@ -432,11 +438,24 @@ __global__ __launch_bounds__(256, 3) void k_score(const double* __restrict__ qba
                         (exp_neg(v[2] - c, exp_tab) + exp_neg(v[3] - c, exp_tab));
       double e = c > -INFINITY ? e4 : 0.0;
       e = pair_sum<16>(e);
+      const bool even = (kt & 1) == 0;
+      if (even && kt + 1 < t1) {   // hold for the next tile's log
+        c_held = c;
+        e_held = e;
+        return;
+      }
+      const bool pair = !even && kt > t0;   // an even tile is held
+      const bool mine = !pair || (g & 1);    // this lane's log is for its own tile
+      const double cc = mine ? c : c_held, ee = mine ? e : e_held;
       // e >= 1 (the max term is 1) whenever the block has a sub-block
-      const double lg = c + log_ge1(c > -INFINITY ? e : 1.0, log_tab);
-      const double yo = (g & 1) == 0 && c > -INFINITY ? lg : -INFINITY;
+      const double lg = cc + log_ge1(cc > -INFINITY ? ee : 1.0, log_tab);
+      const double yo = (pair || (g & 1) == 0) && cc > -INFINITY ? lg : -INFINITY;
       m_run = fmax(m_run, yo);
-      if ((g & 1) == 0) yt[w][l16][(kt % TPF) * 2 + (g >> 1)] = yo;
+      if (!pair) {
+        if ((g & 1) == 0) yt[w][l16][(kt % TPF) * 2 + (g >> 1)] = yo;
+      } else {   // even lane groups: the held tile kt - 1; odd ones: tile kt
+        yt[w][l16][(((g & 1) ? kt : kt - 1) % TPF) * 2 + (g >> 1)] = yo;
+      }
     }
   };
   f64x4 acc_prev = products(t0);
